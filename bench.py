@@ -1,0 +1,250 @@
+"""Benchmark: single-token decode attention over a q4_0 KV cache at 32K context,
+sparse V on (threshold 1e-6) and off (threshold 0), on one MI355X.
+
+Workload ("long-ctx q4_0"): batch 1, 32 query heads over 4 kv heads, head dim
+128, ctx 32768, K/V ~ N(0,1) packed q4_0, 32 planted positions per kv head that
+raise every head's scaled logit by +20 (synthetic, seeded).
+
+One step = one kvq_decode_attn call (the whole hot path: K stream + scores,
+split statistics, log-sum-exp merge, sparse V pass, output merge) for one
+decode token of the batch. Packing the cache is a one-off host step per cache
+and is reported separately. Inputs are resident in HBM before timing; calls
+rotate over copies of the cache totalling more than twice the 256 MB Infinity
+Cache so every call streams from HBM.
+
+Prints one JSON line (rank 0). ``--gpus N`` with N > 1 exits: this build runs
+on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn tokens/s + KV GB/s (% HBM roofline) at 32K ctx, sparse-V on/off"
+HBM_PEAK_GBS = 8000.0
+ROTATION_BYTES = 640 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gqa_fused_long.json")
+KERNEL_SRC = os.path.join(ROOT, "decode_attention_quantized_amd", "csrc", "kvq_gqa.hip")
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(mode: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha256_16") != kernel_hash():
+        return None
+    m = t.get(mode)
+    return None if m is None else m.get("bytes_per_launch")
+
+
+def time_mode(att, q, caches, ctx, tau, steps, warmup, out):
+    import torch
+    R = len(caches)
+    for i in range(warmup):
+        k, v = caches[i % R]
+        att(q, ctx, tau, out=out, k=k, v=v)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        k, v = caches[(warmup + i) % R]
+        ev[i][0].record()
+        att(q, ctx, tau, out=out, k=k, v=v)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    per = sorted(a.elapsed_time(b) * 1e-3 for a, b in ev)       # seconds per launch
+    st = att.stats()
+    return dict(wall=(t1 - t0) / steps, kernel_mean=sum(per) / len(per), kernel_median=per[len(per) // 2],
+                kernel_p10=per[len(per) // 10], kernel_p90=per[(9 * len(per)) // 10], stats=st)
+
+
+def cpu_baseline(inp, budget_s=12.0):
+    """The fp64 oracle, as it stands, on a bounded sample: whole decode calls of
+    the same workload (excluding packing), repeated until ~budget_s."""
+    import numpy as np
+    from oracle import attend as A
+    from oracle import formats as F
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    w = inp.w
+    kc, ks = F.pack(w.fmt, inp.k)
+    vc, vs = F.pack(w.fmt, inp.v)
+    calls, t0 = 0, time.perf_counter()
+    ref = None
+    while True:
+        ref = A.attend(inp.q, kc, ks, vc, vs, fmt=w.fmt, dim=w.dim, v_dim=w.v_dim, ctx_len=w.ctx,
+                       sigma=w.sigma, threshold=w.threshold)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or calls >= 50:
+            break
+    return dict(value=calls * w.batch / el, unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=f"{calls} whole calls of the timed workload (B={w.batch}, ctx={w.ctx}, "
+                       f"{w.q_heads}/{w.kv_heads} heads), fp64 numpy, packing excluded, {el:.1f} s"), ref, (kc, ks)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-mode", choices=["sparse", "dense", "both"], default="both",
+                    help="which threshold(s) to time (a profiler run can restrict to one)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 512 MiB device copy 5 times (reference for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU; multi-GPU sharding is not implemented "
+              "(see DESIGN.md for how the path would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.copy_calibration:
+        n = 512 << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each_way": n, "launches": 5}), flush=True)
+        return
+
+    import decode_attention_quantized_amd as kvq
+    import synth
+    from decode_attention_quantized_amd.runtime import DecodeAttention, PackedCache
+
+    w = synth.workload("long")
+    inp = synth.generate(w)
+    t0 = time.perf_counter()
+    kc, ks = kvq.kvq_pack(w.fmt, inp.k)
+    vc, vs = kvq.kvq_pack(w.fmt, inp.v)
+    pack_s = time.perf_counter() - t0
+    cb, sb = kvq.kvq_row_bytes(w.fmt, w.dim)
+    row = cb + sb
+    set_bytes = 2 * w.batch * w.kv_heads * w.ctx * row
+    R = max(2, math.ceil(ROTATION_BYTES / set_bytes))
+    K0 = PackedCache.from_host(kc, ks, w.fmt, w.dim)
+    V0 = PackedCache.from_host(vc, vs, w.fmt, w.dim)
+    caches = [(K0, V0)] + [(K0.clone(), V0.clone()) for _ in range(R - 1)]
+    q = torch.from_numpy(inp.q).cuda()
+    out = torch.empty((w.batch, w.q_heads, w.v_dim), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    att = DecodeAttention(K0, V0, w.q_heads, ctx_len=w.ctx, softmax_scale=w.sigma, splits=args.splits,
+                          stream=stream)
+
+    modes = {"sparse": w.threshold, "dense": 0.0}
+    if args.profile_mode != "both":
+        modes = {args.profile_mode: modes[args.profile_mode]}
+    res = {}
+    outs = {}
+    for name, tau in modes.items():
+        res[name] = time_mode(att, q, caches, w.ctx, tau, args.steps, args.warmup, out)
+        outs[name] = out.cpu().numpy().copy()
+
+    qo_bytes = w.batch * w.q_heads * w.dim * 4 + w.batch * w.q_heads * w.v_dim * 4
+    k_bytes = w.batch * w.kv_heads * w.ctx * row
+
+    def alg_bytes(name):
+        st = res[name]["stats"]
+        return k_bytes + st["rows_fetched"] * row + qo_bytes
+
+    main_mode = "sparse" if "sparse" in res else next(iter(res))
+    r = res[main_mode]
+    tokens_per_s = w.batch / r["wall"]
+    ab = alg_bytes(main_mode)
+    achieved = ab / r["kernel_mean"] / 1e9
+    traffic = load_traffic(main_mode)
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["wall"] * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "long-ctx q4_0: batch 1, 32 q heads / 4 kv heads, head dim 128, ctx 32768, "
+                        "32 hot positions per kv head (+20 logit), threshold 1e-6",
+            "kv_format": "q4_0",
+            "score_math": "fp16 MFMA (q split hi+lo), fp32 accumulate; softmax and V in fp32",
+            "global_batch": w.batch,
+            "seq_len": w.ctx,
+            "rotation_sets": R,
+            "rotation_bytes": R * set_bytes,
+            "splits": r["stats"]["splits"],
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "kvq::gqa_fused<q4_0, G=8>",
+            "algorithmic_bytes_per_launch": ab,
+            "kernel_us_mean": round(r["kernel_mean"] * 1e6, 3),
+            "kernel_us_median": round(r["kernel_median"] * 1e6, 3),
+        },
+        "kv_gbs_effective": round(ab / r["wall"] / 1e9, 1),
+        "skip_fraction": round(1 - r["stats"]["rows_fetched"] / max(1, r["stats"]["positions"]), 6),
+        "pack_rows_per_s": round(2 * w.batch * w.kv_heads * w.ctx / pack_s, 1),
+    }
+    if "dense" in res and main_mode == "sparse":
+        d = res["dense"]
+        abd = alg_bytes("dense")
+        line["sparse_off"] = {
+            "tokens_per_s": round(w.batch / d["wall"], 1),
+            "ms_per_step": round(d["wall"] * 1e3, 5),
+            "kernel_us_mean": round(d["kernel_mean"] * 1e6, 3),
+            "kv_gbs_effective": round(abd / d["wall"] / 1e9, 1),
+            "achieved_gbs_kernel": round(abd / d["kernel_mean"] / 1e9, 1),
+            "frac_hbm": round(abd / d["kernel_mean"] / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": load_traffic("dense"),
+        }
+        line["speedup_sparse_vs_dense"] = round(d["wall"] / r["wall"], 3)
+    if not args.no_cpu_baseline:
+        cb_, ref, (okc, oks) = cpu_baseline(inp)
+        line["cpu_baseline"] = cb_
+        got = outs.get("sparse")
+        if got is not None:
+            err = float(np.abs(got - ref.out64).max())
+            rel = float(np.linalg.norm(got - ref.out64) / np.linalg.norm(ref.out64))
+            line["parity"] = {"max_abs": err, "rel_l2": rel, "packed_bytes_equal":
+                              bool(np.array_equal(okc, kc) and np.array_equal(oks, ks)),
+                              "kept_pairs": int(r["stats"]["kept_pairs"]), "oracle_kept_pairs": ref.kept_pairs}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

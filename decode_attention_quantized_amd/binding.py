@@ -1,0 +1,187 @@
+"""ctypes binding of ``libkvq.so`` with the C ABI's names (argument marshalling
+only: every step of the computation runs in the library's kernels).
+
+Device buffers are torch tensors on a ROCm device (``tensor.data_ptr()`` is a
+device pointer); host buffers are numpy arrays. If the library is missing the
+first call raises; there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
+
+KVQ_Q8_0, KVQ_Q4_0, KVQ_LUT3, KVQ_FP8_B128 = 0, 1, 2, 3
+KVQ_Q_F32, KVQ_Q_BF16 = 0, 1
+KVQ_LAUNCH_COOPERATIVE = 1
+FMT = {"q8_0": KVQ_Q8_0, "q4_0": KVQ_Q4_0, "lut3": KVQ_LUT3, "fp8_b128": KVQ_FP8_B128}
+
+ERRORS = {0: "OK", -1: "ARG", -2: "ALIGN", -3: "RANGE", -4: "NONFINITE", -5: "WORKSPACE",
+          -6: "LAUNCH", -7: "UNSUPPORTED", -8: "DEVICE"}
+
+
+class KvqError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        self.name = ERRORS.get(code, str(code))
+        super().__init__(f"{where}: {self.name} ({code}) {kvq_strerror(code) if code in ERRORS else ''}")
+
+
+class kvq_cache(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("batch", ctypes.c_int32),
+                ("heads", ctypes.c_int32), ("dim", ctypes.c_int32), ("capacity", ctypes.c_int32)]
+
+
+class kvq_launch(ctypes.Structure):
+    _fields_ = [("q_heads", ctypes.c_int32), ("q_dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("v_dim", ctypes.c_int32), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64),
+                ("stream", ctypes.c_void_p), ("mask_out", ctypes.c_void_p), ("splits", ctypes.c_int32),
+                ("flags", ctypes.c_int32), ("phase_times", ctypes.c_void_p)]
+
+
+class kvq_stats_t(ctypes.Structure):
+    _fields_ = [("positions", ctypes.c_int64), ("pairs", ctypes.c_int64), ("kept_pairs", ctypes.c_int64),
+                ("rows_fetched", ctypes.c_int64), ("k_bytes", ctypes.c_int64), ("v_bytes", ctypes.c_int64),
+                ("v_bytes_dense", ctypes.c_int64), ("status", ctypes.c_int32), ("splits", ctypes.c_int32),
+                ("batch", ctypes.c_int32), ("q_heads", ctypes.c_int32)]
+
+
+EXPORTS = ["kvq_row_bytes", "kvq_pack", "kvq_unpack", "kvq_lut3_levels", "kvq_workspace_bytes",
+           "kvq_decode_attn", "kvq_stats", "kvq_phase_count", "kvq_strerror"]
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the in-tree library once (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing; build it with "
+                              "`python -m decode_attention_quantized_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+        L.kvq_row_bytes.argtypes = [i32, i32, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+        L.kvq_pack.argtypes = [i32, vp, i64, i32, vp, vp]
+        L.kvq_unpack.argtypes = [i32, vp, vp, i64, i32, vp]
+        L.kvq_lut3_levels.argtypes = [vp]
+        L.kvq_workspace_bytes.argtypes = [i32, ctypes.POINTER(kvq_cache), ctypes.POINTER(kvq_launch), i32,
+                                          ctypes.POINTER(i64)]
+        L.kvq_decode_attn.argtypes = [vp, ctypes.POINTER(kvq_cache), ctypes.POINTER(kvq_cache), i32, i32,
+                                      ctypes.c_float, vp, ctypes.POINTER(kvq_launch)]
+        L.kvq_stats.argtypes = [ctypes.POINTER(kvq_launch), ctypes.POINTER(kvq_stats_t), vp]
+        L.kvq_phase_count.argtypes = [ctypes.POINTER(kvq_launch), ctypes.POINTER(i32), ctypes.POINTER(i32)]
+        L.kvq_strerror.argtypes = [i32]
+        L.kvq_strerror.restype = ctypes.c_char_p
+        for name in EXPORTS:
+            if name != "kvq_strerror":
+                getattr(L, name).restype = i32
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, where: str):
+    if rc != 0:
+        raise KvqError(rc, where)
+
+
+def _fmt(fmt) -> int:
+    return FMT[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+def kvq_strerror(code: int) -> str:
+    return lib().kvq_strerror(int(code)).decode()
+
+
+def kvq_row_bytes(fmt, dim: int):
+    cb, sb = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().kvq_row_bytes(_fmt(fmt), int(dim), ctypes.byref(cb), ctypes.byref(sb)), "kvq_row_bytes")
+    return cb.value, sb.value
+
+
+def kvq_pack(fmt, src: np.ndarray):
+    """float32 [..., dim] host rows -> (codes uint8 [..., cb], scales uint8 [..., sb])."""
+    src = np.ascontiguousarray(src, dtype=np.float32)
+    dim = src.shape[-1]
+    cb, sb = kvq_row_bytes(fmt, dim)
+    n = src.size // dim
+    codes = np.empty(src.shape[:-1] + (cb,), np.uint8)
+    scales = np.empty(src.shape[:-1] + (sb,), np.uint8)
+    _check(lib().kvq_pack(_fmt(fmt), src.ctypes.data, n, dim, codes.ctypes.data, scales.ctypes.data), "kvq_pack")
+    return codes, scales
+
+
+def kvq_unpack(fmt, codes: np.ndarray, scales: np.ndarray, dim: int):
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    n = codes.size // codes.shape[-1]
+    dst = np.empty(codes.shape[:-1] + (dim,), np.float32)
+    _check(lib().kvq_unpack(_fmt(fmt), codes.ctypes.data, scales.ctypes.data, n, dim, dst.ctypes.data),
+           "kvq_unpack")
+    return dst
+
+
+def kvq_lut3_levels():
+    out = np.zeros(4, np.uint16)
+    _check(lib().kvq_lut3_levels(out.ctypes.data), "kvq_lut3_levels")
+    return out
+
+
+def make_cache(codes, scales, dim: int) -> kvq_cache:
+    """kvq_cache for device tensors shaped [batch][heads][capacity][bytes]."""
+    B, H, cap = codes.shape[:3]
+    return kvq_cache(codes.data_ptr(), scales.data_ptr(), B, H, dim, cap)
+
+
+def make_launch(q_heads: int, *, q_dtype=KVQ_Q_F32, softmax_scale=0.0, v_dim=0, workspace=None,
+                stream=None, mask_out=None, splits=0, phase_times=None, flags=0) -> kvq_launch:
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = stream.cuda_stream if stream is not None else None
+    mo = mask_out.data_ptr() if mask_out is not None else None
+    pt = phase_times.data_ptr() if phase_times is not None else None
+    return kvq_launch(q_heads, q_dtype, float(softmax_scale), v_dim, ws_ptr, ws_bytes, st, mo, splits, flags, pt)
+
+
+def kvq_workspace_bytes(fmt, kcache: kvq_cache, launch: kvq_launch, ctx_len: int) -> int:
+    b = ctypes.c_int64()
+    _check(lib().kvq_workspace_bytes(_fmt(fmt), ctypes.byref(kcache), ctypes.byref(launch), int(ctx_len),
+                                     ctypes.byref(b)), "kvq_workspace_bytes")
+    return b.value
+
+
+def kvq_decode_attn(q, kcache: kvq_cache, vcache, fmt, ctx_len: int, threshold: float, out,
+                    launch: kvq_launch):
+    """Enqueue one decode-attention call (q, out: device tensors)."""
+    vptr = ctypes.byref(vcache) if vcache is not None else None
+    _check(lib().kvq_decode_attn(q.data_ptr(), ctypes.byref(kcache), vptr, _fmt(fmt), int(ctx_len),
+                                 float(threshold), out.data_ptr(), ctypes.byref(launch)), "kvq_decode_attn")
+
+
+def kvq_stats(launch: kvq_launch, kept_mass: bool = True):
+    """Synchronize and return the last call's statistics as a dict."""
+    s = kvq_stats_t()
+    km = None
+    ptr = None
+    rc0 = 0
+    if kept_mass:
+        # size from a first header read
+        rc0 = lib().kvq_stats(ctypes.byref(launch), ctypes.byref(s), None)
+        km = np.zeros(max(1, s.batch * s.q_heads), np.float32)
+        ptr = km.ctypes.data
+    rc = lib().kvq_stats(ctypes.byref(launch), ctypes.byref(s), ptr)
+    d = {f: getattr(s, f) for f, _ in kvq_stats_t._fields_}
+    if kept_mass:
+        d["kept_mass"] = km[: s.batch * s.q_heads].reshape(s.batch, s.q_heads)
+    d["rc"] = rc if rc else rc0
+    return d
+
+
+def kvq_phase_count(launch: kvq_launch):
+    """(workgroups, stamps per workgroup) of the last call on this workspace."""
+    nwg, ns = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().kvq_phase_count(ctypes.byref(launch), ctypes.byref(nwg), ctypes.byref(ns)), "kvq_phase_count")
+    return nwg.value, ns.value

@@ -1,0 +1,663 @@
+// Fused sparse-V decode attention for grouped-query caches (q8_0, q4_0, LUT3)
+// on gfx950. One cooperative launch per call; phases are separated by grid
+// barriers so the scores of a whole context never leave the chip:
+//
+//  1. K pass. Each workgroup owns P consecutive positions of one (sequence,
+//     kv head). Waves stream 16-position tiles of packed K rows, dequantize
+//     the codes straight into MFMA operands and form the scores of all G
+//     query heads of the group with v_mfma_f32_16x16x32_f16 (q split into
+//     fp16 hi + lo halves, so the products keep ~22 bits of q). Scores stay in
+//     LDS; the split's running (max, sum of exp) per head goes to HBM.
+//  2. Grid barrier, then every workgroup merges the split statistics of its
+//     heads into the log-sum-exp (same order everywhere, so all workgroups of
+//     a group hold bit-identical values).
+//  3. V pass. p = exp(s - LSE) is the normalized weight; a head keeps a
+//     position iff p >= threshold. Each wave ballots the union over the G
+//     heads for its 64 positions and fetches only those value rows; every
+//     other row is never read (the sparse-V rule of "Пропуск 90% работы по
+//     деквантизации…", tproger.ru, section "Решение — не ускорять, а
+//     пропускать": skip V dequantization and accumulation when the attention
+//     weight is below the threshold; weights are known from K before any V
+//     work).
+//  4. Grid barrier, then a deterministic merge of the per-split partial
+//     outputs (fixed split order) into out.
+//
+// All waits are bounded: a barrier that does not complete within ~0.5 s sets
+// a status bit and lets the kernel finish.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr uint32_t kSpinLimit = 1u << 23;
+
+__device__ inline void stamp(const GqaArgs& a, int k) {
+  if (a.times && threadIdx.x == 0) a.times[int64_t(blockIdx.x) * 16 + k] = wall_clock64();
+}
+
+// Merge two (max, sum-of-exp2) pairs of the log2 domain; commutative bit for bit.
+__device__ inline float2 lse_merge(float2 x, float2 y) {
+  const float M = fmaxf(x.x, y.x);
+  if (M == -INFINITY) return make_float2(M, 0.f);
+  const float L = x.y * exp2f(x.x - M) + y.y * exp2f(y.x - M);
+  return make_float2(M, L);
+}
+
+__device__ inline float bf16_to_f32(uint16_t u) { return __uint_as_float(uint32_t(u) << 16); }
+
+__device__ inline float half_lo(uint32_t w) {
+  return float(__builtin_bit_cast(half2v, w)[0]);
+}
+__device__ inline float half_hi(uint32_t w) {
+  return float(__builtin_bit_cast(half2v, w)[1]);
+}
+
+// ---------------------------------------------------------------- tagged words
+// A hand-off value is one 64-bit word: the call's epoch in the high half and
+// the payload in the low half, stored and loaded as a single relaxed
+// agent-scope atomic (coherent across the XCDs' L2 caches). A reader spins
+// (bounded) until the tag matches; no fence or counter orders the hand-off.
+typedef unsigned long long u64;
+
+__device__ inline void put_tagged(u64* p, uint32_t epoch, uint32_t payload) {
+  __hip_atomic_store(p, (u64(epoch) << 32) | payload, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void put_tagged_f(u64* p, uint32_t epoch, float v) { put_tagged(p, epoch, __float_as_uint(v)); }
+
+// Payload of *p once its tag equals epoch; a timeout sets a status bit.
+__device__ inline uint32_t get_tagged(const u64* p, uint32_t epoch, WsHeader* h) {
+  u64 w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint32_t spins = 0;
+  while (uint32_t(w >> 32) != epoch) {
+    __builtin_amdgcn_s_sleep(1);
+    if (++spins > kSpinLimit) {
+      __hip_atomic_fetch_or(&h->status, kStatusWaitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return uint32_t(w);
+}
+__device__ inline float get_tagged_f(const u64* p, uint32_t epoch, WsHeader* h) {
+  return __uint_as_float(get_tagged(p, epoch, h));
+}
+
+// One relaxed load; pair with settle() so a batch of loads is in flight at once.
+__device__ inline u64 peek(const u64* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Payload of a peeked word, spinning on *p only if the peek was stale.
+__device__ inline float settle_f(u64 w, const u64* p, uint32_t epoch, WsHeader* h) {
+  if (uint32_t(w >> 32) == epoch) return __uint_as_float(uint32_t(w));
+  return get_tagged_f(p, epoch, h);
+}
+
+// Online (max, sum of exp2) update with one more score; -inf scores are skipped.
+__device__ inline void online_add(float& m, float& l, float s) {
+  if (s == -INFINITY) return;
+  if (s > m) { l = l * exp2f(m - s) + 1.f; m = s; }
+  else l += exp2f(s - m);
+}
+
+// ---------------------------------------------------------------- format traits
+// Each lane of a 16x16x32 MFMA supplies 8 consecutive K-slots of one column.
+// For the K pass the column is a position and the 32 K-slots of one MFMA are
+// the 32 elements of one quantization block (so a per-position, per-block
+// scale can be applied to the fp32 result). Lane group kk = lane/16 takes
+// elements 8kk..8kk+7 of the block; dim_of() gives the element order the
+// dequantizer produces, which the q operand must follow.
+template <int FMT> struct Traits;
+
+template <> struct Traits<KVQ_Q4_0> {
+  static constexpr int CB = 64, SB = 8;
+  // codes c in 0..15 enter the MFMA as fp16 (16 + c); value = c - 8, so the
+  // bias removed per block is 24 * sum(q)
+  static constexpr float kBias = 24.0f;
+  struct Raw { uint32_t c[4]; uint2 s; };
+  __device__ static int dim_of(int bb, int kk, int e) { return 32 * bb + 8 * kk + (e >> 1) + 4 * (e & 1); }
+  __device__ static Raw load(const uint8_t* crow, const uint8_t* srow, int kk) {
+    Raw r;
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) r.c[bb] = *reinterpret_cast<const uint32_t*>(crow + 16 * bb + 4 * kk);
+    r.s = *reinterpret_cast<const uint2*>(srow);
+    return r;
+  }
+  // one dword = 8 nibbles -> fp16 (16 + c), vector order elements 0,4,1,5,2,6,3,7
+  __device__ static half8 deq(const Raw& r, int bb) {
+    const uint32_t x = r.c[bb];
+    uint4 u;
+    u.x = ((x << 6) & 0x03C003C0u) | 0x4C004C00u;
+    u.y = ((x << 2) & 0x03C003C0u) | 0x4C004C00u;
+    u.z = ((x >> 2) & 0x03C003C0u) | 0x4C004C00u;
+    u.w = ((x >> 6) & 0x03C003C0u) | 0x4C004C00u;
+    return __builtin_bit_cast(half8, u);
+  }
+  __device__ static float scale(const Raw& r, int bb) {
+    const uint32_t w = (bb < 2) ? r.s.x : r.s.y;
+    return (bb & 1) ? half_hi(w) : half_lo(w);
+  }
+  // value pass: lane owns dims 2*lane, 2*lane+1
+  __device__ static void vload(const uint8_t* crow, const uint8_t* srow, int lane, uint32_t& code, uint32_t& sc) {
+    code = crow[lane];
+    sc = *reinterpret_cast<const uint16_t*>(srow + 2 * (lane >> 4));
+  }
+  __device__ static void vdeq(uint32_t code, uint32_t sc, float& v0, float& v1) {
+    const float d = float(__builtin_bit_cast(_Float16, uint16_t(sc)));
+    v0 = float(int(code & 15u) - 8) * d;
+    v1 = float(int(code >> 4) - 8) * d;
+  }
+};
+
+template <> struct Traits<KVQ_Q8_0> {
+  static constexpr int CB = 128, SB = 8;
+  // signed codes enter as fp16 (1024 + (c + 128)); bias 1152
+  static constexpr float kBias = 1152.0f;
+  struct Raw { uint2 c[4]; uint2 s; };
+  __device__ static int dim_of(int bb, int kk, int e) { return 32 * bb + 8 * kk + e; }
+  __device__ static Raw load(const uint8_t* crow, const uint8_t* srow, int kk) {
+    Raw r;
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) r.c[bb] = *reinterpret_cast<const uint2*>(crow + 32 * bb + 8 * kk);
+    r.s = *reinterpret_cast<const uint2*>(srow);
+    return r;
+  }
+  __device__ static half8 deq(const Raw& r, int bb) {
+    const uint32_t x0 = r.c[bb].x ^ 0x80808080u, x1 = r.c[bb].y ^ 0x80808080u;
+    uint4 u;
+    u.x = __builtin_amdgcn_perm(0x64646464u, x0, 0x04010400u);
+    u.y = __builtin_amdgcn_perm(0x64646464u, x0, 0x04030402u);
+    u.z = __builtin_amdgcn_perm(0x64646464u, x1, 0x04010400u);
+    u.w = __builtin_amdgcn_perm(0x64646464u, x1, 0x04030402u);
+    return __builtin_bit_cast(half8, u);
+  }
+  __device__ static float scale(const Raw& r, int bb) {
+    const uint32_t w = (bb < 2) ? r.s.x : r.s.y;
+    return (bb & 1) ? half_hi(w) : half_lo(w);
+  }
+  __device__ static void vload(const uint8_t* crow, const uint8_t* srow, int lane, uint32_t& code, uint32_t& sc) {
+    code = *reinterpret_cast<const uint16_t*>(crow + 2 * lane);
+    sc = *reinterpret_cast<const uint16_t*>(srow + 2 * (lane >> 4));
+  }
+  __device__ static void vdeq(uint32_t code, uint32_t sc, float& v0, float& v1) {
+    const float d = float(__builtin_bit_cast(_Float16, uint16_t(sc)));
+    v0 = float(int(int8_t(code & 0xFFu))) * d;
+    v1 = float(int(int8_t(code >> 8))) * d;
+  }
+};
+
+// ---------------------------------------------------------------- the kernel
+// Workgroup roles: every workgroup scores its split and runs its own V pass;
+// split 0 of each group (the "master") also merges the group's split
+// statistics into the LSE and, at the end, the partial outputs into out.
+template <int FMT, int G>
+__global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
+  using T = Traits<FMT>;
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
+  extern __shared__ __align__(16) unsigned char smem[];
+  // LDS: scores [G][P] (then kept weights in place; then the cross-wave
+  // reduction; then the merge list), q operands, small per-head values.
+  const int P = a.P;
+  const int sc_floats = (G * P > kWaves * G * 128) ? G * P : kWaves * G * 128;
+  float* sc = reinterpret_cast<float*>(smem);
+  _Float16* qop = reinterpret_cast<_Float16*>(sc + sc_floats);     // [16 rows][4 blk][4 kk][8]
+  float* cst = reinterpret_cast<float*>(qop + 16 * 128);          // [4 blk][16 rows]
+  float* hs = cst + 64;                                           // [8] per-head score scale
+  float* lse = hs + 8;                                            // [8] log2-domain LSE
+  float* qmax = lse + 8;                                          // [8]
+  int* wcount = reinterpret_cast<int*>(qmax + 8);                 // [kWaves] kept pairs
+  int* wrows = wcount + kWaves;                                   // [kWaves] rows fetched
+  float* wmass = reinterpret_cast<float*>(wrows + kWaves);        // [kWaves][G]
+  float2* wml = reinterpret_cast<float2*>(wmass + kWaves * G);    // [kWaves][8] per-wave (max, sum)
+  int* misc = reinterpret_cast<int*>(wml + kWaves * 8);           // [kWaves + 4]
+  unsigned long long* umask = reinterpret_cast<unsigned long long*>(misc + kWaves + 4);  // [P/64]
+  int* coff = reinterpret_cast<int*>(umask + (P / kChunk));       // [P/64]
+  int* rowlist = coff + (P / kChunk);                             // [P] kept rows of the split
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wg = blockIdx.x;
+  const int bg = wg / a.S;                  // b * Hkv + g
+  const int split = wg - bg * a.S;
+  const bool master = split == 0;
+  const int b = bg / a.Hkv;
+  const int g = bg - b * a.Hkv;
+  const int pos0 = split * P;
+  const int ctx = a.ctx;
+  const float tau = a.tau;
+  const int64_t row0 = int64_t(bg) * a.cap;
+  const uint32_t epoch = __hip_atomic_load(&a.hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  stamp(a, 0);
+
+  const int n16 = lane & 15;     // MFMA column (position within a tile)
+  const int kg = lane >> 4;      // lane group
+  // issue the first K tiles before the q set-up so their latency overlaps it
+  const int ntiles = P / 16;
+  constexpr int U = 4;
+  typename T::Raw raw[U];
+  auto load_tiles = [&](int t0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = t0 + u * kWaves;
+      const int r = pos0 + t * 16 + n16;
+      if (t < ntiles && r < ctx) {
+        const int64_t row = row0 + r;
+        raw[u] = T::load(a.kc + row * T::CB, a.ks + row * T::SB, kg);
+      } else {
+        raw[u] = typename T::Raw{};
+      }
+    }
+  };
+  load_tiles(wave);
+
+  // ---------------------------------------------------------------- setup
+  if (wg == 0 && tid == 0) {
+    a.hdr->batch = a.B; a.hdr->q_heads = a.Hq; a.hdr->kv_heads = a.Hkv; a.hdr->ctx = ctx;
+    a.hdr->splits = a.S; a.hdr->positions_per_split = P; a.hdr->fmt = FMT; a.hdr->v_dim = 128;
+    a.hdr->nwg = int(gridDim.x);
+  }
+  // q of this group: per-head max |q| -> power-of-two prescale, then fp16 hi/lo rows
+  float qv[4];
+  {
+    const int j = tid >> 5, ln = tid & 31;      // 32 threads per head, 4 dims each
+    float m = 0.f;
+    if (j < G) {
+      const int h = g * G + j;
+      const int64_t qoff = (int64_t(b) * a.Hq + h) * 128 + ln * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qv[e] = a.q_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.q)[qoff + e])
+                         : reinterpret_cast<const float*>(a.q)[qoff + e];
+        m = fmaxf(m, fabsf(qv[e]));
+      }
+    }
+    if (j < 8) {
+#pragma unroll
+      for (int o = 16; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 32));
+      if (j < G && ln == 0) qmax[j] = m;
+    }
+  }
+  __syncthreads();
+  {
+    const int j = tid >> 5, ln = tid & 31;
+    if (j < G) {
+      const float m = qmax[j];
+      const int ex = (m > 0.f) ? ilogbf(m) + 1 : 0;           // m * 2^-ex in [0.5, 1)
+      if (ln == 0) hs[j] = ldexpf(a.sigma_log2e, ex);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = ln * 4 + e;
+        const float qs = ldexpf(qv[e], -ex);
+        const _Float16 hi = _Float16(qs);
+        const _Float16 lo = _Float16(qs - float(hi));
+        const int bb = d >> 5, kk = (d >> 3) & 3;
+        int slot = 0;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) if (T::dim_of(bb, kk, s) == d) slot = s;
+        qop[((2 * j) * 16 + bb * 4 + kk) * 8 + slot] = hi;
+        qop[((2 * j + 1) * 16 + bb * 4 + kk) * 8 + slot] = lo;
+      }
+    } else if (j < 8) {
+      for (int e = 0; e < 4; ++e) {
+        const int d = ln * 4 + e;
+        const int bb = d >> 5, kk = (d >> 3) & 3;
+        const int slot = d & 7;
+        qop[((2 * j) * 16 + bb * 4 + kk) * 8 + slot] = _Float16(0.f);
+        qop[((2 * j + 1) * 16 + bb * 4 + kk) * 8 + slot] = _Float16(0.f);
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {                                // bias correction per (block, row)
+    const int bb = tid >> 4, m = tid & 15;
+    float s = 0.f;
+    for (int k = 0; k < 32; ++k) s += float(qop[(m * 16 + bb * 4 + (k >> 3)) * 8 + (k & 7)]);
+    cst[bb * 16 + m] = -T::kBias * s;
+  }
+  __syncthreads();
+
+  // MFMA operands of this lane
+  half8 A[4];
+  floatx4 C0[4];
+#pragma unroll
+  for (int bb = 0; bb < 4; ++bb) {
+    A[bb] = *reinterpret_cast<const half8*>(&qop[(n16 * 16 + bb * 4 + kg) * 8]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) C0[bb][i] = cst[bb * 16 + 4 * kg + i];
+  }
+  const int j0 = 2 * kg, j1 = 2 * kg + 1;   // the two heads whose rows this lane group holds
+  const float hs0 = (j0 < G) ? hs[j0] : 0.f;
+  const float hs1 = (j1 < G) ? hs[j1] : 0.f;
+  stamp(a, 1);
+
+  // ---------------------------------------------------------------- phase 1: scores
+  // Scores go to LDS; each lane keeps an online (max, sum exp2) of its two heads.
+  float m0 = -INFINITY, l0 = 0.f, m1 = -INFINITY, l1 = 0.f;
+  for (int t0 = wave; t0 < ntiles; t0 += kWaves * U) {
+    if (t0 != wave) load_tiles(t0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = t0 + u * kWaves;
+      if (t >= ntiles) break;                   // uniform across the wave
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const floatx4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[bb], T::deq(raw[u], bb), C0[bb], 0, 0, 0);
+        const float s = T::scale(raw[u], bb);
+        acc[0] = fmaf(s, d[0], acc[0]);
+        acc[1] = fmaf(s, d[1], acc[1]);
+        acc[2] = fmaf(s, d[2], acc[2]);
+        acc[3] = fmaf(s, d[3], acc[3]);
+      }
+      const int lp = t * 16 + n16;
+      const bool valid = (pos0 + lp) < ctx;
+      const float s0 = valid ? (acc[0] + acc[1]) * hs0 : -INFINITY;
+      const float s1 = valid ? (acc[2] + acc[3]) * hs1 : -INFINITY;
+      if (j0 < G) { sc[j0 * P + lp] = s0; online_add(m0, l0, s0); }
+      if (j1 < G) { sc[j1 * P + lp] = s1; online_add(m1, l1, s1); }
+    }
+  }
+  // split statistics: merge over the 16 lanes of a lane group, then over waves
+  {
+    float2 x0 = make_float2(m0, l0), x1 = make_float2(m1, l1);
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) {
+      float2 y0, y1;
+      y0.x = __shfl_xor(x0.x, o, 16); y0.y = __shfl_xor(x0.y, o, 16);
+      y1.x = __shfl_xor(x1.x, o, 16); y1.y = __shfl_xor(x1.y, o, 16);
+      x0 = lse_merge(x0, y0);
+      x1 = lse_merge(x1, y1);
+    }
+    if (n16 == 0) {
+      wml[wave * 8 + j0] = x0;
+      wml[wave * 8 + j1] = x1;
+    }
+  }
+  __syncthreads();
+  stamp(a, 2);
+  if (tid < G) {
+    float2 acc = make_float2(-INFINITY, 0.f);
+    for (int w = 0; w < kWaves; ++w) acc = lse_merge(acc, wml[w * 8 + tid]);
+    u64* dst = a.split_ml + ((int64_t(bg) * a.S + split) * G + tid) * 2;
+    put_tagged_f(dst, epoch, acc.x);
+    put_tagged_f(dst + 1, epoch, acc.y);
+  }
+  __syncthreads();                                   // wml is reused below
+
+  // ---------------------------------------------------------------- phase 2: LSE of the group
+  // Every workgroup gathers all split statistics of its group and merges
+  // them itself (128 threads per head, fixed pattern, so every workgroup of
+  // the group computes the same bits); no workgroup waits on another's LSE.
+  {
+    float2 acc = make_float2(-INFINITY, 0.f);
+    const int j = tid >> 7, ln = tid & 127;
+    if (j < G) {
+      for (int s0 = ln; s0 < a.S; s0 += 4 * 128) {
+        u64 w[4][2];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int sp = s0 + 128 * u;
+          const u64* src = a.split_ml + ((int64_t(bg) * a.S + sp) * G + j) * 2;
+          w[u][0] = sp < a.S ? peek(src) : 0ull;
+          w[u][1] = sp < a.S ? peek(src + 1) : 0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int sp = s0 + 128 * u;
+          if (sp < a.S) {
+            const u64* src = a.split_ml + ((int64_t(bg) * a.S + sp) * G + j) * 2;
+            float2 v;
+            v.x = settle_f(w[u][0], src, epoch, a.hdr);
+            v.y = settle_f(w[u][1], src + 1, epoch, a.hdr);
+            acc = lse_merge(acc, v);
+          }
+        }
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        float2 oth;
+        oth.x = __shfl_xor(acc.x, o);
+        oth.y = __shfl_xor(acc.y, o);
+        acc = lse_merge(acc, oth);
+      }
+      if (lane == 0) wml[wave] = acc;                 // two waves per head
+    }
+    __syncthreads();
+    if (tid < G) {
+      const float2 v = lse_merge(wml[2 * tid], wml[2 * tid + 1]);
+      lse[tid] = v.x + log2f(v.y);
+    }
+    __syncthreads();
+  }
+  stamp(a, 3);
+
+  // ---------------------------------------------------------------- phase 3: sparse V pass
+  // (a) per 64-position chunk: normalized weights, per-head keep bits, the
+  //     union over the group's heads (a value row is fetched iff some head
+  //     keeps it); (b) the kept rows of all chunks are pooled in LDS and
+  //     spread over all waves; (c) each wave fetches only its kept rows.
+  float o0[G], o1[G], mass[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) { o0[j] = 0.f; o1[j] = 0.f; mass[j] = 0.f; }
+  int kept_cnt = 0;
+  float lsej[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) lsej[j] = lse[j];
+  const int nchunks = P / kChunk;
+  for (int c = wave; c < nchunks; c += kWaves) {
+    const int lp = c * kChunk + lane;
+    const int r = pos0 + lp;
+    const bool valid = r < ctx;
+    bool any = false;
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const float p = valid ? exp2f(sc[j * P + lp] - lsej[j]) : 0.f;
+      const bool keep = valid && (p >= tau);
+      const float pk = keep ? p : 0.f;
+      sc[j * P + lp] = pk;                     // kept weight replaces the score in place
+      mass[j] += pk;
+      any |= keep;
+      const unsigned long long bal = __ballot(keep);
+      kept_cnt += __popcll(bal);
+      if (a.mask_out && lane < 2) {
+        const int word = (pos0 + c * kChunk) / 32 + lane;
+        if (word < a.mask_words) {
+          const int h = g * G + j;
+          a.mask_out[(int64_t(b) * a.Hq + h) * a.mask_words + word] = uint32_t(bal >> (32 * lane));
+        }
+      }
+    }
+    const unsigned long long um = __ballot(any);
+    if (lane == 0) umask[c] = um;
+  }
+  __syncthreads();
+  if (tid < 64) {                                    // exclusive scan of kept rows per chunk
+    const int c0 = 2 * tid, c1 = 2 * tid + 1;
+    const int n0 = c0 < nchunks ? __popcll(umask[c0]) : 0;
+    const int n1 = c1 < nchunks ? __popcll(umask[c1]) : 0;
+    int incl = n0 + n1;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    const int excl = incl - n0 - n1;
+    if (c0 < nchunks) coff[c0] = excl;
+    if (c1 < nchunks) coff[c1] = excl + n0;
+    if (tid == 63) misc[kWaves + 3] = incl;
+  }
+  __syncthreads();
+  const int nrows = misc[kWaves + 3];
+  for (int c = wave; c < nchunks; c += kWaves) {
+    const unsigned long long um = umask[c];
+    if ((um >> lane) & 1ull) rowlist[coff[c] + __popcll(um & ((1ull << lane) - 1ull))] = c * kChunk + lane;
+  }
+  __syncthreads();
+  {
+    // rows [k0, k1) of the pooled list go to this wave; 16 rows of loads are
+    // in flight at once
+    const int per = (nrows + kWaves - 1) / kWaves;
+    const int k0 = wave * per;
+    const int k1 = (k0 + per < nrows) ? k0 + per : nrows;
+    constexpr int VB = 16;
+    for (int k = k0; k < k1; k += VB) {
+      uint32_t code[VB], scl[VB];
+#pragma unroll
+      for (int u = 0; u < VB; ++u) {
+        if (k + u < k1) {
+          const int64_t row = row0 + pos0 + rowlist[k + u];
+          T::vload(a.vc + row * T::CB, a.vs + row * T::SB, lane, code[u], scl[u]);
+        } else {
+          code[u] = 0; scl[u] = 0;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < VB; ++u) {
+        if (k + u >= k1) break;
+        float v0, v1;
+        T::vdeq(code[u], scl[u], v0, v1);
+        const int pr = rowlist[k + u];
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          const float pj = sc[j * P + pr];
+          o0[j] = fmaf(pj, v0, o0[j]);
+          o1[j] = fmaf(pj, v1, o1[j]);
+        }
+      }
+    }
+  }
+  const int rows_cnt = (tid == 0) ? nrows : 0;
+
+  // per-wave counters and kept mass
+  if (lane == 0) { wcount[wave] = kept_cnt; wrows[wave] = rows_cnt; }
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    float m = mass[j];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m += __shfl_xor(m, o);
+    if (lane == 0) wmass[wave * G + j] = m;
+  }
+  __syncthreads();                                   // all waves done with sc
+  int wg_rows = 0, wg_kept = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) { wg_rows += wrows[w]; wg_kept += wcount[w]; }
+  const int64_t pbase = int64_t(bg) * a.S + split;
+  if (wg_rows > 0) {                                  // uniform across the workgroup
+    float* red = sc;                                 // [kWaves][G][128]
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      red[(wave * G + j) * 128 + 2 * lane] = o0[j];
+      red[(wave * G + j) * 128 + 2 * lane + 1] = o1[j];
+    }
+    __syncthreads();
+    for (int i = tid; i < G * 128; i += kThreads) {
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) s += red[w * G * 128 + i];
+      put_tagged_f(a.partial + pbase * G * 128 + i, epoch, s);
+    }
+    if (tid < G) {
+      float s = 0.f;
+      for (int w = 0; w < kWaves; ++w) s += wmass[w * G + tid];
+      put_tagged_f(a.pmass + pbase * G + tid, epoch, s);
+    }
+  }
+  if (tid == 0) put_tagged(a.flags + pbase, epoch, (uint32_t(wg_rows) << 18) | uint32_t(wg_kept));
+  stamp(a, 4);
+
+  // ---------------------------------------------------------------- phase 4: merge (master)
+  // Sum the flagged partial outputs in ascending split order (deterministic)
+  // and write the group's statistics. The last group to finish advances the
+  // workspace epoch for the next call.
+  if (master) {
+    __syncthreads();
+    int* list = reinterpret_cast<int*>(sc);          // flagged splits, ascending
+    int* wcnt = misc;                                // [kWaves]
+    int* sk = reinterpret_cast<int*>(wml);           // per-wave kept/rows sums [kWaves][2]
+    int total = 0;
+    int kept_sum = 0, rows_sum = 0;
+    for (int s0 = 0; s0 < a.S; s0 += kThreads) {
+      const int s = s0 + tid;
+      uint32_t fv = 0;
+      if (s < a.S) fv = get_tagged(a.flags + int64_t(bg) * a.S + s, epoch, a.hdr);
+      const int rows = int(fv >> 18), kept = int(fv & 0x3FFFFu);
+      const bool f = rows > 0;
+      const unsigned long long bal = __ballot(f);
+      int kr = kept, rr = rows;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) { kr += __shfl_xor(kr, o); rr += __shfl_xor(rr, o); }
+      if (lane == 0) { wcnt[wave] = __popcll(bal); sk[2 * wave] = kr; sk[2 * wave + 1] = rr; }
+      __syncthreads();
+      int off = total;
+      for (int w = 0; w < wave; ++w) off += wcnt[w];
+      if (f) list[off + __popcll(bal & ((1ull << lane) - 1ull))] = s;
+      for (int w = 0; w < kWaves; ++w) { total += wcnt[w]; kept_sum += sk[2 * w]; rows_sum += sk[2 * w + 1]; }
+      __syncthreads();
+    }
+    stamp(a, 5);
+    const int nflag = total;
+    for (int i = tid; i < G * 128; i += kThreads) {
+      if (i < G) {                                  // kept mass of head i
+        const u64* pm = a.pmass + int64_t(bg) * a.S * G + i;
+        float m = 0.f;
+        for (int k0 = 0; k0 < nflag; k0 += 16) {
+          u64 w[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) w[u] = (k0 + u < nflag) ? peek(pm + int64_t(list[k0 + u]) * G) : 0ull;
+#pragma unroll
+          for (int u = 0; u < 16; ++u)
+            if (k0 + u < nflag) m += settle_f(w[u], pm + int64_t(list[k0 + u]) * G, epoch, a.hdr);
+        }
+        a.kept_mass[int64_t(bg) * G + i] = m;
+      }
+      const u64* pp = a.partial + int64_t(bg) * a.S * (G * 128) + i;
+      float s = 0.f;
+      for (int k0 = 0; k0 < nflag; k0 += 16) {
+        u64 w[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) w[u] = (k0 + u < nflag) ? peek(pp + int64_t(list[k0 + u]) * (G * 128)) : 0ull;
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          if (k0 + u < nflag) s += settle_f(w[u], pp + int64_t(list[k0 + u]) * (G * 128), epoch, a.hdr);
+      }
+      a.out[int64_t(bg) * (G * 128) + i] = s;
+    }
+    if (tid == 0) {
+      a.bgstat[2 * bg] = (unsigned long long)kept_sum;
+      a.bgstat[2 * bg + 1] = (unsigned long long)rows_sum;
+      const uint32_t ngroups = uint32_t(a.B * a.Hkv);
+      const uint32_t prev = __hip_atomic_fetch_add(&a.hdr->groups_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (prev == ngroups - 1) {
+        __hip_atomic_store(&a.hdr->groups_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&a.hdr->epoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    stamp(a, 6);
+  }
+}
+
+// LDS bytes the kernel needs for P positions per split and group size G.
+size_t gqa_lds_bytes(int G, int P) {
+  size_t sc = size_t(G) * P > size_t(kWaves) * G * 128 ? size_t(G) * P : size_t(kWaves) * G * 128;
+  if (sc < size_t(kThreads)) sc = kThreads;        // the merge list reuses this region
+  return sc * 4 + 16 * 128 * 2 + 64 * 4 + 3 * 8 * 4 + 2 * kWaves * 4 + size_t(kWaves) * G * 4 +
+         size_t(kWaves) * 8 * 8 + (kWaves + 4) * 4 + size_t(P / kChunk) * 12 + size_t(P) * 4 + 64;
+}
+
+const void* gqa_kernel(int fmt, int G) {
+#define KVQ_SEL(F, GG) if (fmt == F && G == GG) return reinterpret_cast<const void*>(&gqa_fused<F, GG>);
+  KVQ_SEL(KVQ_Q4_0, 1) KVQ_SEL(KVQ_Q4_0, 2) KVQ_SEL(KVQ_Q4_0, 4) KVQ_SEL(KVQ_Q4_0, 8)
+  KVQ_SEL(KVQ_Q8_0, 1) KVQ_SEL(KVQ_Q8_0, 2) KVQ_SEL(KVQ_Q8_0, 4) KVQ_SEL(KVQ_Q8_0, 8)
+#undef KVQ_SEL
+  return nullptr;
+}
+
+}  // namespace kvq

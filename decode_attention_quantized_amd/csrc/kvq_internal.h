@@ -1,0 +1,94 @@
+// Internal types shared by the host entry points (kvq_api.cpp) and the HIP
+// kernels. Not part of the public C ABI.
+#pragma once
+
+#include <stdint.h>
+
+namespace kvq {
+
+constexpr int kThreads = 1024;          // threads per workgroup (16 wave64s, one workgroup per CU)
+constexpr int kWaves = kThreads / 64;
+constexpr int kChunk = 64;              // positions per wave chunk (one ballot word)
+
+// Device fault bits reported through WsHeader::status.
+constexpr uint32_t kStatusWaitTimeout = 1u;   // a bounded wait gave up
+
+// Workspace header. The first 256 bytes of every workspace; the rest holds the
+// per-split statistics and partial outputs of the last call.
+struct WsHeader {
+  uint32_t epoch;                       // tag of the last completed call (0 in a fresh workspace)
+  uint32_t groups_done;                 // merges finished in the running call (returns to 0)
+  uint32_t status;                      // sticky device fault bits
+  uint32_t pad0;
+  unsigned long long reserved2;
+  unsigned long long reserved3;
+  int32_t batch, q_heads, kv_heads, ctx;
+  int32_t splits, positions_per_split, fmt, v_dim;
+  int32_t nwg, pad2;
+  uint8_t pad1[256 - 16 - 16 - 32 - 8];
+};
+static_assert(sizeof(WsHeader) == 256, "header is one 256-byte line");
+
+// Byte offsets of the workspace regions for one call's plan. Every value
+// that one workgroup hands to another is a 64-bit "tagged word": the call's
+// epoch in the high half, the 32-bit payload in the low half. A reader polls
+// until the tag matches, so no fence or counter orders the hand-off.
+struct WsLayout {
+  int64_t kept_mass;   // float [B*Hq]
+  int64_t bgstat;      // u64 [B*Hkv][2]: kept pairs, value rows fetched
+  int64_t lse;         // tagged [B*Hkv][G]: log2-domain log-sum-exp per head
+  int64_t split_ml;    // tagged [B*Hkv][S][G][2]: per-split (max, sum) in the log2 domain
+  int64_t flags;       // tagged [B*Hkv][S]: rows fetched << 18 | kept pairs of the split
+  int64_t pmass;       // tagged [B*Hkv][S][G]: per-split kept mass
+  int64_t partial;     // tagged [B*Hkv][S][G][Dv]: per-split partial outputs
+  int64_t total;
+};
+
+inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+inline WsLayout ws_layout(int B, int Hkv, int Hq, int S, int Dv) {
+  const int G = Hq / Hkv;
+  const int64_t BG = int64_t(B) * Hkv;
+  WsLayout w;
+  int64_t off = 256;
+  w.kept_mass = off; off = align256(off + int64_t(B) * Hq * 4);
+  w.bgstat = off;    off = align256(off + BG * 16);
+  w.lse = off;       off = align256(off + BG * G * 8);
+  w.split_ml = off;  off = align256(off + BG * S * G * 16);
+  w.flags = off;     off = align256(off + BG * S * 8);
+  w.pmass = off;     off = align256(off + BG * S * G * 8);
+  w.partial = off;   off = align256(off + BG * S * G * int64_t(Dv) * 8);
+  w.total = off;
+  return w;
+}
+
+// Arguments of the fused grouped-query kernel (one struct, passed by value).
+struct GqaArgs {
+  const void* q;                  // [B][Hq][D] float32 or bfloat16
+  const uint8_t* kc;              // key code plane
+  const uint8_t* ks;              // key scale plane
+  const uint8_t* vc;              // value code plane
+  const uint8_t* vs;              // value scale plane
+  float* out;                     // [B][Hq][D]
+  uint32_t* mask_out;             // optional keep bits
+  WsHeader* hdr;
+  float* kept_mass;
+  unsigned long long* bgstat;
+  unsigned long long* lse;        // tagged
+  unsigned long long* split_ml;   // tagged
+  unsigned long long* flags;      // tagged
+  unsigned long long* pmass;      // tagged
+  unsigned long long* partial;    // tagged
+  int32_t B, Hkv, Hq, ctx, cap;
+  int32_t S, P;                   // splits per (b, kv head), positions per split (multiple of 64)
+  int32_t mask_words;             // ceil(ctx / 32)
+  int32_t q_bf16;
+  int32_t fmt;
+  float sigma_log2e;              // softmax scale times log2(e)
+  float tau;                      // threshold on the normalized weight
+  unsigned long long* times;      // optional [nwg][16] phase stamps
+};
+
+constexpr int kStamps = 7;        // phase stamps per workgroup (5 and 6 only by a group's merging workgroup)
+
+}  // namespace kvq

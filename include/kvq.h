@@ -1,0 +1,216 @@
+/*
+ * kvq — single-token decode attention over a block-quantized KV cache, with
+ * the sparse-V skip, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources for what is computed (cited by page title and section):
+ *  [SV]  "Пропуск 90% работы по деквантизации ускорил декодирование LLM на
+ *        22,8%" (tproger.ru news item on sparse V dequantization):
+ *        "Решение — не ускорять, а пропускать" — the softmax weights come from
+ *        K before any V work, and a position whose attention weight is below
+ *        1e-6 has its V dequantization *and* accumulation skipped entirely;
+ *        "Почему это работает для любой квантизации" — the rule is format
+ *        independent (q8_0, q4_0, turbo3 with a LUT codebook and a norm);
+ *        FAQ — every K must still be dequantized to know the weights.
+ *  [MLA] "FP8 MLA KV compression projection" (kernelindex.com), workload
+ *        parameters: a 576-wide latent (kv_lora_rank 512 + qk_rope_head_dim
+ *        64), fp8 with BlockWise1x128 scaling, 128 heads, qk_nope_head_dim 128.
+ *
+ * Conventions for every entry point:
+ *  - Return 0 (KVQ_OK) on success or a negative KVQ_ERR_* code. All argument
+ *    checks happen before any device work; a failed check launches nothing.
+ *  - "host" pointers are ordinary CPU memory; "device" pointers are GPU memory
+ *    (e.g. from hipMalloc or a torch CUDA tensor's data_ptr()).
+ *  - The library allocates no device memory and keeps no global mutable state
+ *    apart from a per-device cache of the compute-unit count. Calls that share
+ *    a workspace must be serialized (same stream or explicit ordering).
+ *  - Multi-byte values in packed planes are little-endian.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------ formats
+ * A packed cache is two byte planes in row order [batch][head][position]:
+ * a code plane with a fixed number of bytes per row and a scale plane with a
+ * fixed number of bytes per row (kvq_row_bytes). All rounding is done in
+ * float64 with one round-to-nearest-even per narrowing.
+ *
+ * KVQ_Q8_0    ([SV] format list). Blocks of 32: d = fp16(max|x|/127);
+ *             code = x/d rounded half away from zero, clamped to +-127
+ *             (zero scale -> zero codes). Row: dim int8 codes, dim/32 fp16 d.
+ * KVQ_Q4_0    ([SV] format list). Blocks of 32: m = element of largest |x|
+ *             (first on ties, sign kept), d = fp16(m / -8); code =
+ *             clamp(floor(x/d + 1/2) + 8, 0, 15) (zero scale -> 8); value
+ *             (code-8)*d. Row: dim/2 bytes (block b at bytes 16b.., byte j of a
+ *             block = element 2j low nibble | element 2j+1 high nibble), then
+ *             dim/32 fp16 d.
+ * KVQ_LUT3    ([SV] turbo3-style LUT codebook). 128-wide rows only. 3-bit code
+ *             = sign bit (top) + 2-bit magnitude index into the four fp16
+ *             magnitudes of the 8-level Lloyd-Max quantizer of N(0,1)
+ *             (fp16 bits 0x33D8 0x3A0C 0x3D60 0x404E). With norm = |x|_2
+ *             (sequential float64 sum of squares) and t = x*sqrt(128)/norm,
+ *             the index is the nearest magnitude to |t| (ties to the smaller),
+ *             and the row scalar nu = fp16(norm*sqrt(128)/|LUT[codes]|_2)
+ *             keeps the decoded norm. Value = nu*(+-M[idx])/sqrt(128).
+ *             Row: 32 B magnitude plane (element i at bits 2(i%4) of byte
+ *             i/4) + 16 B sign plane (bit i%8 of byte i/8); scale plane: nu.
+ * KVQ_FP8_B128 ([MLA] BlockWise1x128). Groups of 128 along the row (the last
+ *             may be shorter): s = fp32(max|x|/448); code =
+ *             e4m3fn(clamp(x/s, -448, 448)) (OCP E4M3, nearest-even);
+ *             zero scale -> zero codes. Row: dim e4m3 bytes, then one fp32
+ *             per group.
+ */
+enum {
+  KVQ_Q8_0 = 0,
+  KVQ_Q4_0 = 1,
+  KVQ_LUT3 = 2,
+  KVQ_FP8_B128 = 3
+};
+
+/* query element types */
+enum { KVQ_Q_F32 = 0, KVQ_Q_BF16 = 1 };
+
+/* error codes */
+enum {
+  KVQ_OK = 0,
+  KVQ_ERR_ARG = -1,          /* null pointer, bad enum, inconsistent shapes */
+  KVQ_ERR_ALIGN = -2,        /* a device pointer is not 16-byte aligned */
+  KVQ_ERR_RANGE = -3,        /* ctx_len or threshold out of range; a scale overflows fp16 */
+  KVQ_ERR_NONFINITE = -4,    /* NaN or infinity in packer input */
+  KVQ_ERR_WORKSPACE = -5,    /* workspace missing or smaller than kvq_workspace_bytes */
+  KVQ_ERR_LAUNCH = -6,       /* the HIP runtime refused a launch or copy */
+  KVQ_ERR_UNSUPPORTED = -7,  /* valid request this build does not implement */
+  KVQ_ERR_DEVICE = -8        /* a kernel reported a fault (see kvq_stats.status) */
+};
+
+/* Bytes per packed row of `dim` elements for `fmt`.
+ * code_bytes/scale_bytes: host out-pointers. Errors: ARG (bad fmt, null),
+ * UNSUPPORTED (dim not allowed for fmt: q8_0/q4_0 need dim % 32 == 0, LUT3
+ * needs dim == 128, FP8 needs 1 <= dim). */
+int32_t kvq_row_bytes(int32_t fmt, int32_t dim, int64_t* code_bytes, int64_t* scale_bytes);
+
+/* Pack n_rows float32 rows of `dim` elements (host `src`, row-major) into the
+ * host planes `codes` (n_rows * code_bytes) and `scales` (n_rows *
+ * scale_bytes), per the format rules above. Synchronous, deterministic,
+ * bit-exact with the format definition. Caller owns all buffers.
+ * Errors: ARG, UNSUPPORTED, NONFINITE (any NaN/inf in src; nothing written
+ * is guaranteed), RANGE (a scale overflows fp16). */
+int32_t kvq_pack(int32_t fmt, const float* src, int64_t n_rows, int32_t dim,
+                 uint8_t* codes, uint8_t* scales);
+
+/* Decode packed host planes back to float32 host rows (a test and debugging
+ * aid; values are the exact decoded values rounded once to float32). */
+int32_t kvq_unpack(int32_t fmt, const uint8_t* codes, const uint8_t* scales,
+                   int64_t n_rows, int32_t dim, float* dst);
+
+/* The four LUT3 magnitudes as fp16 bit patterns (host out[4]). */
+int32_t kvq_lut3_levels(uint16_t* out4);
+
+/* ------------------------------------------------------------------ decode */
+
+/* A packed cache in device memory. Row r of (batch b, head h) is at
+ * codes + ((b*heads + h)*capacity + r) * code_bytes, likewise for scales.
+ * Both planes must be 16-byte aligned. Rows at positions >= ctx_len are never
+ * read. */
+typedef struct kvq_cache {
+  const void* codes;
+  const void* scales;
+  int32_t batch;
+  int32_t heads;
+  int32_t dim;
+  int32_t capacity;
+} kvq_cache;
+
+typedef struct kvq_launch {
+  int32_t q_heads;        /* Hq; must be a multiple of the cache's heads */
+  int32_t q_dtype;        /* KVQ_Q_F32 or KVQ_Q_BF16 */
+  float softmax_scale;    /* sigma; 0 selects 1/sqrt(kcache.dim) */
+  int32_t v_dim;          /* latent caches (vcache == NULL): value = first v_dim dims of each key row */
+  void* workspace;        /* device, >= kvq_workspace_bytes, zero-filled before its first use */
+  int64_t workspace_bytes;
+  void* stream;           /* hipStream_t; NULL = the default stream */
+  uint32_t* mask_out;     /* optional device [batch][q_heads][ceil(ctx_len/32)]: bit i%32 of
+                             word i/32 = position i kept by that head; NULL to skip */
+  int32_t splits;         /* 0 = automatic; otherwise context splits per (batch, kv head) */
+  int32_t flags;          /* 0 or KVQ_LAUNCH_COOPERATIVE */
+  uint64_t* phase_times;  /* optional device [workgroups][16] buffer (profiling aid; NULL to skip):
+                             each workgroup stores the 100 MHz device wall clock at its phase
+                             boundaries (see kvq_phase_count) */
+} kvq_launch;
+
+/* kvq_launch.flags. The workgroups of one call exchange data while they run,
+ * so all of them must be resident at once; the plan never launches more than
+ * one workgroup per compute unit. By default the kernel is launched normally
+ * (lowest latency), and every wait is bounded (about half a second) so a call
+ * that cannot get its workgroups resident, e.g. because another kernel holds
+ * the compute units, ends with KVQ_ERR_DEVICE from kvq_stats rather than a
+ * hang. KVQ_LAUNCH_COOPERATIVE asks the runtime to guarantee co-residency
+ * (hipLaunchCooperativeKernel), at roughly 20 us extra per call. */
+enum { KVQ_LAUNCH_COOPERATIVE = 1 };
+
+/* Device workspace bytes kvq_decode_attn needs for these shapes on the
+ * current device (bytes: host out-pointer). */
+int32_t kvq_workspace_bytes(int32_t fmt, const kvq_cache* kcache, const kvq_launch* l,
+                            int32_t ctx_len, int64_t* bytes);
+
+/* Single-token decode attention with the sparse-V skip ([SV], section
+ * "Решение — не ускорять, а пропускать"). For each sequence b and query head
+ * h (kv head g = floor(h*Hkv/Hq), n = ctx_len, sigma = softmax scale):
+ *   s_i = sigma * <q[b,h], dequant(K[b,g,i])>          for all i < n
+ *   p_i = exp(s_i - max s) / sum_j exp(s_j - max s)    (normalized weight)
+ *   out[b,h] = sum over i with p_i >= threshold of p_i * dequant(V[b,g,i])
+ * No renormalization over kept positions; V rows whose weight is below the
+ * threshold for every head of the group are never read. threshold = 0 gives
+ * dense attention.
+ *  q        device [batch][q_heads][kcache.dim], float32 or bfloat16
+ *  kcache   key cache (and, when vcache is NULL, the latent the values come from)
+ *  vcache   value cache with the same batch/heads/capacity, or NULL (latent)
+ *  fmt      KVQ_* format of both caches
+ *  ctx_len  1 <= ctx_len <= capacity
+ *  threshold  0 <= threshold < 1, finite
+ *  out      device float32 [batch][q_heads][value dim]
+ * Asynchronous on l->stream; returns after enqueueing. Errors: ARG, ALIGN,
+ * RANGE, WORKSPACE, UNSUPPORTED (shape outside the built kernels), LAUNCH.
+ * Device-side faults are reported by kvq_stats. */
+int32_t kvq_decode_attn(const void* q, const kvq_cache* kcache, const kvq_cache* vcache,
+                        int32_t fmt, int32_t ctx_len, float threshold, float* out,
+                        const kvq_launch* l);
+
+typedef struct kvq_stats_t {
+  int64_t positions;       /* batch * kv_heads * ctx_len key rows scored */
+  int64_t pairs;           /* batch * q_heads * ctx_len (head, position) weights */
+  int64_t kept_pairs;      /* weights >= threshold */
+  int64_t rows_fetched;    /* value rows read (kept by at least one head of the group) */
+  int64_t k_bytes;         /* key bytes read (codes + scales) */
+  int64_t v_bytes;         /* value bytes read */
+  int64_t v_bytes_dense;   /* value bytes a dense pass reads */
+  int32_t status;          /* 0 = ok; nonzero = device fault bits */
+  int32_t splits;          /* context splits per (batch, kv head) used */
+  int32_t batch;
+  int32_t q_heads;
+} kvq_stats_t;
+
+/* Statistics of the last kvq_decode_attn on this workspace. Synchronizes
+ * l->stream, then copies. kept_mass (optional host float[batch*q_heads])
+ * receives sum of kept weights per head. Returns KVQ_ERR_DEVICE when the
+ * call reported a fault; the workspace must then be zero-filled again. */
+int32_t kvq_stats(const kvq_launch* l, kvq_stats_t* out, float* kept_mass);
+
+/* Number of workgroups the last kvq_decode_attn on this workspace launched
+ * (rows of kvq_launch.phase_times) and the number of phase stamps per row
+ * (host out-pointers; synchronizes l->stream). */
+int32_t kvq_phase_count(const kvq_launch* l, int32_t* workgroups, int32_t* stamps);
+
+/* Static text for an error code. */
+const char* kvq_strerror(int32_t code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,124 @@
+"""GPU parity: the fused HIP path against the oracle for grouped-query caches
+(q8_0, q4_0). Every case prints its name before touching the GPU."""
+import numpy as np
+import pytest
+
+import synth
+from gpu_helpers import compare, oracle_for, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(name, threshold=None, **kw):
+    w = synth.resized(synth.workload(name), **kw) if kw else synth.workload(name)
+    return synth.generate(w), (w.threshold if threshold is None else threshold)
+
+
+@pytest.mark.parametrize("threshold", [1e-6, 0.0])
+def test_tiny_q8_0(threshold):
+    say("case tiny q8_0 tau", threshold)
+    inp, tau = _case("tiny", threshold)
+    g = run_gpu(inp, tau)
+    r, po = oracle_for(inp, tau)
+    compare(inp, tau, g, r, po)
+
+
+@pytest.mark.parametrize("threshold", [1e-6, 0.0])
+def test_long_q4_0_full_size(threshold):
+    say("case long q4_0 ctx 32768 tau", threshold)
+    inp, tau = _case("long", threshold)
+    g = run_gpu(inp, tau)
+    r, po = oracle_for(inp, tau)
+    compare(inp, tau, g, r, po)
+    if tau > 0:
+        # only the planted rows are fetched: 32 per kv head
+        assert g["stats"]["rows_fetched"] == 128
+
+
+def test_long_q4_0_cooperative_launch():
+    say("case long q4_0 ctx 32768, cooperative launch")
+    inp, tau = _case("long")
+    g = run_gpu(inp, tau, cooperative=True)
+    r, po = oracle_for(inp, tau)
+    compare(inp, tau, g, r, po)
+
+
+def test_stress_scattered_mask():
+    say("case stress q4_0 ctx 32768 (about 8% kept per head)")
+    inp, tau = _case("stress")
+    g = run_gpu(inp, tau)
+    r, po = oracle_for(inp, tau)
+    compare(inp, tau, g, r, po)
+
+
+@pytest.mark.parametrize("ctx", [1, 2, 63, 65, 1000, 4097])
+def test_ragged_contexts(ctx):
+    say("case ragged q4_0 ctx", ctx)
+    inp, tau = _case("long", ctx=ctx, hot=min(4, ctx))
+    g = run_gpu(inp, tau)
+    r, po = oracle_for(inp, tau)
+    compare(inp, tau, g, r, po)
+
+
+def test_ctx_below_capacity():
+    say("case q8_0 capacity 2048, ctx 1500")
+    inp, tau = _case("tiny", ctx=2048)
+    g = run_gpu(inp, tau, ctx_len=1500)
+    r, po = oracle_for(inp, tau, ctx_len=1500)
+    compare(inp, tau, g, r, po)
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_group_sizes(G):
+    say("case q8_0 group size", G)
+    inp, tau = _case("long", fmt="q8_0", q_heads=2 * G, kv_heads=2, ctx=3000, hot=5)
+    g = run_gpu(inp, tau)
+    r, po = oracle_for(inp, tau)
+    compare(inp, tau, g, r, po)
+
+
+def test_batch_and_bf16_queries():
+    say("case q4_0 batch 3, bf16 q")
+    import torch
+    inp, tau = _case("long", batch=3, ctx=5000, hot=6)
+    g = run_gpu(inp, tau, q_bf16=True)
+    qb = torch.from_numpy(inp.q).to(torch.bfloat16).float().numpy()
+    r, po = oracle_for(inp, tau, q_override=qb)
+    compare(inp, tau, g, r, po)
+
+
+@pytest.mark.parametrize("splits", [4, 7, 64])
+def test_split_count_does_not_change_result(splits):
+    say("case q4_0 ctx 8192 splits", splits)
+    inp, tau = _case("long", ctx=8192, hot=16)
+    g = run_gpu(inp, tau, splits=splits)
+    r, po = oracle_for(inp, tau)
+    compare(inp, tau, g, r, po)
+
+
+def test_split_too_large_for_lds_is_rejected():
+    say("case one split over 8192 positions (scores exceed LDS) -> UNSUPPORTED, nothing launched")
+    import decode_attention_quantized_amd as kvq
+    inp, tau = _case("long", ctx=8192, hot=16)
+    with pytest.raises(kvq.KvqError) as e:
+        run_gpu(inp, tau, splits=1)
+    assert e.value.name == "UNSUPPORTED"
+
+
+def test_deterministic_repeats():
+    say("case determinism stress ctx 16384, 3 calls")
+    inp, tau = _case("stress", ctx=16384)
+    g = run_gpu(inp, tau, repeat=3)
+    for o in g["outs"][1:]:
+        assert np.array_equal(o, g["outs"][0])
+    for m in g["masks"][1:]:
+        assert np.array_equal(m, g["masks"][0])
+
+
+def test_sweep_lengths():
+    for n in synth.SWEEP:
+        say("case sweep ctx", n)
+        inp, tau = _case(f"sweep_{n}")
+        g = run_gpu(inp, tau)
+        r, po = oracle_for(inp, tau)
+        compare(inp, tau, g, r, po)
