@@ -51,7 +51,7 @@ struct Plan {
   WsLayout ws{};
 };
 
-bool is_gqa_fmt(int fmt) { return fmt == KVQ_Q8_0 || fmt == KVQ_Q4_0; }
+bool is_gqa_fmt(int fmt) { return fmt == KVQ_Q8_0 || fmt == KVQ_Q4_0 || fmt == KVQ_LUT3; }
 
 // Validate shapes shared by every entry point and pick splits.
 int32_t make_plan(int32_t fmt, const kvq_cache* k, const kvq_launch* l, int32_t ctx_len, Plan* plan) {

@@ -118,11 +118,17 @@ template <int FMT> struct Traits;
 
 template <> struct Traits<KVQ_Q4_0> {
   static constexpr int CB = 64, SB = 8;
+  static constexpr bool kRowScale = false;        // one scale per 32-element block
+  static constexpr float kRowMul = 1.0f;
   // codes c in 0..15 enter the MFMA as fp16 (16 + c); value = c - 8, so the
   // bias removed per block is 24 * sum(q)
   static constexpr float kBias = 24.0f;
   struct Raw { uint32_t c[4]; uint2 s; };
   __device__ static int dim_of(int bb, int kk, int e) { return 32 * bb + 8 * kk + (e >> 1) + 4 * (e & 1); }
+  // inverse of dim_of: MFMA index, lane group and vector slot of dim d
+  __device__ static void locate(int d, int& bb, int& kk, int& slot) {
+    bb = d >> 5; kk = (d >> 3) & 3; slot = 2 * (d & 3) + ((d >> 2) & 1);
+  }
   __device__ static Raw load(const uint8_t* crow, const uint8_t* srow, int kk) {
     Raw r;
 #pragma unroll
@@ -131,7 +137,7 @@ template <> struct Traits<KVQ_Q4_0> {
     return r;
   }
   // one dword = 8 nibbles -> fp16 (16 + c), vector order elements 0,4,1,5,2,6,3,7
-  __device__ static half8 deq(const Raw& r, int bb) {
+  __device__ static half8 deq(const Raw& r, int bb, uint32_t) {
     const uint32_t x = r.c[bb];
     uint4 u;
     u.x = ((x << 6) & 0x03C003C0u) | 0x4C004C00u;
@@ -145,23 +151,29 @@ template <> struct Traits<KVQ_Q4_0> {
     return (bb & 1) ? half_hi(w) : half_lo(w);
   }
   // value pass: lane owns dims 2*lane, 2*lane+1
-  __device__ static void vload(const uint8_t* crow, const uint8_t* srow, int lane, uint32_t& code, uint32_t& sc) {
-    code = crow[lane];
-    sc = *reinterpret_cast<const uint16_t*>(srow + 2 * (lane >> 4));
+  struct VRaw { uint32_t code, sc; };
+  __device__ static VRaw vload(const uint8_t* crow, const uint8_t* srow, int lane) {
+    VRaw v;
+    v.code = crow[lane];
+    v.sc = *reinterpret_cast<const uint16_t*>(srow + 2 * (lane >> 4));
+    return v;
   }
-  __device__ static void vdeq(uint32_t code, uint32_t sc, float& v0, float& v1) {
-    const float d = float(__builtin_bit_cast(_Float16, uint16_t(sc)));
-    v0 = float(int(code & 15u) - 8) * d;
-    v1 = float(int(code >> 4) - 8) * d;
+  __device__ static void vdeq(const VRaw& r, uint32_t, float& v0, float& v1) {
+    const float d = float(__builtin_bit_cast(_Float16, uint16_t(r.sc)));
+    v0 = float(int(r.code & 15u) - 8) * d;
+    v1 = float(int(r.code >> 4) - 8) * d;
   }
 };
 
 template <> struct Traits<KVQ_Q8_0> {
   static constexpr int CB = 128, SB = 8;
+  static constexpr bool kRowScale = false;
+  static constexpr float kRowMul = 1.0f;
   // signed codes enter as fp16 (1024 + (c + 128)); bias 1152
   static constexpr float kBias = 1152.0f;
   struct Raw { uint2 c[4]; uint2 s; };
   __device__ static int dim_of(int bb, int kk, int e) { return 32 * bb + 8 * kk + e; }
+  __device__ static void locate(int d, int& bb, int& kk, int& slot) { bb = d >> 5; kk = (d >> 3) & 3; slot = d & 7; }
   __device__ static Raw load(const uint8_t* crow, const uint8_t* srow, int kk) {
     Raw r;
 #pragma unroll
@@ -169,7 +181,7 @@ template <> struct Traits<KVQ_Q8_0> {
     r.s = *reinterpret_cast<const uint2*>(srow);
     return r;
   }
-  __device__ static half8 deq(const Raw& r, int bb) {
+  __device__ static half8 deq(const Raw& r, int bb, uint32_t) {
     const uint32_t x0 = r.c[bb].x ^ 0x80808080u, x1 = r.c[bb].y ^ 0x80808080u;
     uint4 u;
     u.x = __builtin_amdgcn_perm(0x64646464u, x0, 0x04010400u);
@@ -182,14 +194,89 @@ template <> struct Traits<KVQ_Q8_0> {
     const uint32_t w = (bb < 2) ? r.s.x : r.s.y;
     return (bb & 1) ? half_hi(w) : half_lo(w);
   }
-  __device__ static void vload(const uint8_t* crow, const uint8_t* srow, int lane, uint32_t& code, uint32_t& sc) {
-    code = *reinterpret_cast<const uint16_t*>(crow + 2 * lane);
-    sc = *reinterpret_cast<const uint16_t*>(srow + 2 * (lane >> 4));
+  struct VRaw { uint32_t code, sc; };
+  __device__ static VRaw vload(const uint8_t* crow, const uint8_t* srow, int lane) {
+    VRaw v;
+    v.code = *reinterpret_cast<const uint16_t*>(crow + 2 * lane);
+    v.sc = *reinterpret_cast<const uint16_t*>(srow + 2 * (lane >> 4));
+    return v;
   }
-  __device__ static void vdeq(uint32_t code, uint32_t sc, float& v0, float& v1) {
-    const float d = float(__builtin_bit_cast(_Float16, uint16_t(sc)));
-    v0 = float(int(int8_t(code & 0xFFu))) * d;
-    v1 = float(int(int8_t(code >> 8))) * d;
+  __device__ static void vdeq(const VRaw& r, uint32_t, float& v0, float& v1) {
+    const float d = float(__builtin_bit_cast(_Float16, uint16_t(r.sc)));
+    v0 = float(int(int8_t(r.code & 0xFFu))) * d;
+    v1 = float(int(int8_t(r.code >> 8))) * d;
+  }
+};
+
+// LUT3: 3-bit codes (sign << 2 | magnitude index) packed contiguously, element
+// i at bits 3i..3i+2 of the 384-bit row, one fp16 nu per row; value =
+// nu * (+-M[idx]) / sqrt(128) with M the four fp16 Lloyd-Max magnitudes.
+// Two neighbouring codes form a 6-bit key; every lane holds one entry of the
+// 64-entry table of fp16 value pairs, read with ds_bpermute (the LUT read of
+// the turbo3 dequant, "14 попыток, которые провалились", done as one
+// cross-lane read per two elements). The scale is per row, so the four MFMAs
+// of a row accumulate into one result.
+constexpr uint16_t kLut3Bits[4] = {0x33D8, 0x3A0C, 0x3D60, 0x404E};
+
+__device__ inline uint32_t lut3_code_bits(uint32_t c) {
+  return ((c & 4u) << 13) | kLut3Bits[c & 3u];
+}
+// this lane's entry of the pair table: key = c0 | c1 << 3 -> (value c0, value c1)
+__device__ inline uint32_t lut3_pair_entry(int lane) {
+  return lut3_code_bits(uint32_t(lane) & 7u) | (lut3_code_bits(uint32_t(lane) >> 3) << 16);
+}
+
+template <> struct Traits<KVQ_LUT3> {
+  static constexpr int CB = 48, SB = 2;
+  static constexpr bool kRowScale = true;
+  static constexpr float kBias = 0.0f;
+  static constexpr float kRowMul = 0.08838834764831845f;   // 1/sqrt(128)
+  struct Raw { uint32_t c[3]; uint32_t s; };
+  // lane group kk holds elements 32kk..32kk+31 (bits 96kk..96kk+95 of the row);
+  // MFMA bb takes elements 32kk + 8bb + e
+  __device__ static int dim_of(int bb, int kk, int e) { return 32 * kk + 8 * bb + e; }
+  __device__ static void locate(int d, int& bb, int& kk, int& slot) { kk = d >> 5; bb = (d >> 3) & 3; slot = d & 7; }
+  __device__ static Raw load(const uint8_t* crow, const uint8_t* srow, int kk) {
+    Raw r;
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(crow + 12 * kk);
+    r.c[0] = p[0]; r.c[1] = p[1]; r.c[2] = p[2];
+    r.s = *reinterpret_cast<const uint16_t*>(srow);
+    return r;
+  }
+  // byte address (4 * key) of the 6-bit key at bit b of the lane's 96 bits
+  __device__ static uint32_t key_addr(const Raw& r, int b) {
+    const int w = b >> 5, o = b & 31;
+    const uint32_t x = (o <= 26) ? (r.c[w] >> o) : __builtin_amdgcn_alignbit(r.c[w + 1], r.c[w], o);
+    return (x << 2) & 0xFCu;
+  }
+  __device__ static half8 deq(const Raw& r, int bb, uint32_t table) {
+    uint4 u;
+    u.x = uint32_t(__builtin_amdgcn_ds_bpermute(int(key_addr(r, 24 * bb + 0)), int(table)));
+    u.y = uint32_t(__builtin_amdgcn_ds_bpermute(int(key_addr(r, 24 * bb + 6)), int(table)));
+    u.z = uint32_t(__builtin_amdgcn_ds_bpermute(int(key_addr(r, 24 * bb + 12)), int(table)));
+    u.w = uint32_t(__builtin_amdgcn_ds_bpermute(int(key_addr(r, 24 * bb + 18)), int(table)));
+    return __builtin_bit_cast(half8, u);
+  }
+  __device__ static float scale(const Raw& r, int) { return half_lo(r.s); }
+  // value pass: lane owns dims 2*lane, 2*lane+1 = bits 6*lane..6*lane+5
+  struct VRaw { uint32_t lo, hi, sc; };
+  __device__ static VRaw vload(const uint8_t* crow, const uint8_t* srow, int lane) {
+    VRaw v;
+    const int b = 6 * lane, w = b >> 5;
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(crow);
+    v.lo = p[w];
+    v.hi = ((b & 31) > 26) ? p[w + 1] : 0u;       // only when the key straddles two words
+    v.sc = *reinterpret_cast<const uint16_t*>(srow);
+    return v;
+  }
+  __device__ static void vdeq(const VRaw& r, uint32_t table, float& v0, float& v1) {
+    const int lane = __lane_id();
+    const int o = (6 * lane) & 31;
+    const uint32_t x = __builtin_amdgcn_alignbit(r.hi, r.lo, o);
+    const uint32_t pair = uint32_t(__builtin_amdgcn_ds_bpermute(int((x << 2) & 0xFCu), int(table)));
+    const float nu = float(__builtin_bit_cast(_Float16, uint16_t(r.sc))) * kRowMul;
+    v0 = half_lo(pair) * nu;
+    v1 = half_hi(pair) * nu;
   }
 };
 
@@ -219,7 +306,7 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   int* misc = reinterpret_cast<int*>(wml + kWaves * 8);           // [kWaves + 4]
   unsigned long long* umask = reinterpret_cast<unsigned long long*>(misc + kWaves + 4);  // [P/64]
   int* coff = reinterpret_cast<int*>(umask + (P / kChunk));       // [P/64]
-  int* rowlist = coff + (P / kChunk);                             // [P] kept rows of the split
+  uint16_t* rowlist = reinterpret_cast<uint16_t*>(coff + (P / kChunk));   // [P] kept rows of the split
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -239,6 +326,7 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
 
   const int n16 = lane & 15;     // MFMA column (position within a tile)
   const int kg = lane >> 4;      // lane group
+  const uint32_t table = (FMT == KVQ_LUT3) ? lut3_pair_entry(lane) : 0u;
   // issue the first K tiles before the q set-up so their latency overlaps it
   const int ntiles = P / 16;
   constexpr int U = 4;
@@ -291,17 +379,15 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     if (j < G) {
       const float m = qmax[j];
       const int ex = (m > 0.f) ? ilogbf(m) + 1 : 0;           // m * 2^-ex in [0.5, 1)
-      if (ln == 0) hs[j] = ldexpf(a.sigma_log2e, ex);
+      if (ln == 0) hs[j] = ldexpf(a.sigma_log2e, ex) * T::kRowMul;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int d = ln * 4 + e;
         const float qs = ldexpf(qv[e], -ex);
         const _Float16 hi = _Float16(qs);
         const _Float16 lo = _Float16(qs - float(hi));
-        const int bb = d >> 5, kk = (d >> 3) & 3;
-        int slot = 0;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) if (T::dim_of(bb, kk, s) == d) slot = s;
+        int bb, kk, slot;
+        T::locate(d, bb, kk, slot);
         qop[((2 * j) * 16 + bb * 4 + kk) * 8 + slot] = hi;
         qop[((2 * j + 1) * 16 + bb * 4 + kk) * 8 + slot] = lo;
       }
@@ -348,14 +434,22 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
       const int t = t0 + u * kWaves;
       if (t >= ntiles) break;                   // uniform across the wave
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (T::kRowScale) {
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        const floatx4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[bb], T::deq(raw[u], bb), C0[bb], 0, 0, 0);
-        const float s = T::scale(raw[u], bb);
-        acc[0] = fmaf(s, d[0], acc[0]);
-        acc[1] = fmaf(s, d[1], acc[1]);
-        acc[2] = fmaf(s, d[2], acc[2]);
-        acc[3] = fmaf(s, d[3], acc[3]);
+        for (int bb = 0; bb < 4; ++bb)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[bb], T::deq(raw[u], bb, table), acc, 0, 0, 0);
+        const float s = T::scale(raw[u], 0);
+        acc[0] *= s; acc[1] *= s; acc[2] *= s; acc[3] *= s;
+      } else {
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          const floatx4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[bb], T::deq(raw[u], bb, table), C0[bb], 0, 0, 0);
+          const float s = T::scale(raw[u], bb);
+          acc[0] = fmaf(s, d[0], acc[0]);
+          acc[1] = fmaf(s, d[1], acc[1]);
+          acc[2] = fmaf(s, d[2], acc[2]);
+          acc[3] = fmaf(s, d[3], acc[3]);
+        }
       }
       const int lp = t * 16 + n16;
       const bool valid = (pos0 + lp) < ctx;
@@ -498,7 +592,7 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   const int nrows = misc[kWaves + 3];
   for (int c = wave; c < nchunks; c += kWaves) {
     const unsigned long long um = umask[c];
-    if ((um >> lane) & 1ull) rowlist[coff[c] + __popcll(um & ((1ull << lane) - 1ull))] = c * kChunk + lane;
+    if ((um >> lane) & 1ull) rowlist[coff[c] + __popcll(um & ((1ull << lane) - 1ull))] = uint16_t(c * kChunk + lane);
   }
   __syncthreads();
   {
@@ -509,21 +603,21 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     const int k1 = (k0 + per < nrows) ? k0 + per : nrows;
     constexpr int VB = 16;
     for (int k = k0; k < k1; k += VB) {
-      uint32_t code[VB], scl[VB];
+      typename T::VRaw vr[VB];
 #pragma unroll
       for (int u = 0; u < VB; ++u) {
         if (k + u < k1) {
           const int64_t row = row0 + pos0 + rowlist[k + u];
-          T::vload(a.vc + row * T::CB, a.vs + row * T::SB, lane, code[u], scl[u]);
+          vr[u] = T::vload(a.vc + row * T::CB, a.vs + row * T::SB, lane);
         } else {
-          code[u] = 0; scl[u] = 0;
+          vr[u] = typename T::VRaw{};
         }
       }
 #pragma unroll
       for (int u = 0; u < VB; ++u) {
         if (k + u >= k1) break;
         float v0, v1;
-        T::vdeq(code[u], scl[u], v0, v1);
+        T::vdeq(vr[u], table, v0, v1);
         const int pr = rowlist[k + u];
 #pragma unroll
         for (int j = 0; j < G; ++j) {
@@ -649,13 +743,14 @@ size_t gqa_lds_bytes(int G, int P) {
   size_t sc = size_t(G) * P > size_t(kWaves) * G * 128 ? size_t(G) * P : size_t(kWaves) * G * 128;
   if (sc < size_t(kThreads)) sc = kThreads;        // the merge list reuses this region
   return sc * 4 + 16 * 128 * 2 + 64 * 4 + 3 * 8 * 4 + 2 * kWaves * 4 + size_t(kWaves) * G * 4 +
-         size_t(kWaves) * 8 * 8 + (kWaves + 4) * 4 + size_t(P / kChunk) * 12 + size_t(P) * 4 + 64;
+         size_t(kWaves) * 8 * 8 + (kWaves + 4) * 4 + size_t(P / kChunk) * 12 + size_t(P) * 2 + 64;
 }
 
 const void* gqa_kernel(int fmt, int G) {
 #define KVQ_SEL(F, GG) if (fmt == F && G == GG) return reinterpret_cast<const void*>(&gqa_fused<F, GG>);
   KVQ_SEL(KVQ_Q4_0, 1) KVQ_SEL(KVQ_Q4_0, 2) KVQ_SEL(KVQ_Q4_0, 4) KVQ_SEL(KVQ_Q4_0, 8)
   KVQ_SEL(KVQ_Q8_0, 1) KVQ_SEL(KVQ_Q8_0, 2) KVQ_SEL(KVQ_Q8_0, 4) KVQ_SEL(KVQ_Q8_0, 8)
+  KVQ_SEL(KVQ_LUT3, 1) KVQ_SEL(KVQ_LUT3, 2) KVQ_SEL(KVQ_LUT3, 4) KVQ_SEL(KVQ_LUT3, 8)
 #undef KVQ_SEL
   return nullptr;
 }

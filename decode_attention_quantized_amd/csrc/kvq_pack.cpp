@@ -166,8 +166,10 @@ int32_t pack_lut3(const float* x, uint8_t* codes, uint8_t* scales) {
     const double a = std::fabs(v * r);
     int idx = 0;
     for (int k = 0; k < 3; ++k) if (a > thr[k]) idx = k + 1;
-    codes[i / 4] |= static_cast<uint8_t>(idx << (2 * (i % 4)));
-    if (v < 0.0) codes[32 + i / 8] |= static_cast<uint8_t>(1u << (i % 8));
+    const unsigned code = static_cast<unsigned>(idx) | (v < 0.0 ? 4u : 0u);
+    // code i occupies bits 3i..3i+2 of the little-endian 384-bit row
+    for (int k = 0; k < 3; ++k)
+      if ((code >> k) & 1u) codes[(3 * i + k) / 8] |= static_cast<uint8_t>(1u << ((3 * i + k) % 8));
     lsq = lsq + M[idx] * M[idx];
   }
   const uint16_t nu = f64_to_f16((norm * std::sqrt(128.0)) / std::sqrt(lsq));
@@ -272,8 +274,10 @@ extern "C" int32_t kvq_unpack(int32_t fmt, const uint8_t* codes, const uint8_t* 
       case KVQ_LUT3: {
         const double nu = f16_to_f64(get_u16(s));
         for (int i = 0; i < 128; ++i) {
-          const int idx = (c[i / 4] >> (2 * (i % 4))) & 3;
-          const bool neg = (c[32 + i / 8] >> (i % 8)) & 1;
+          unsigned code = 0;
+          for (int k = 0; k < 3; ++k) code |= ((c[(3 * i + k) / 8] >> ((3 * i + k) % 8)) & 1u) << k;
+          const int idx = code & 3;
+          const bool neg = (code >> 2) & 1;
           const double m = f16_to_f64(kLut3Bits[idx]);
           y[i] = static_cast<float>((nu * (neg ? -m : m)) / std::sqrt(128.0));
         }

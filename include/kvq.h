@@ -57,8 +57,9 @@ extern "C" {
  *             the index is the nearest magnitude to |t| (ties to the smaller),
  *             and the row scalar nu = fp16(norm*sqrt(128)/|LUT[codes]|_2)
  *             keeps the decoded norm. Value = nu*(+-M[idx])/sqrt(128).
- *             Row: 32 B magnitude plane (element i at bits 2(i%4) of byte
- *             i/4) + 16 B sign plane (bit i%8 of byte i/8); scale plane: nu.
+ *             Row: 48 B = the 128 codes as one little-endian 384-bit string,
+ *             element i at bits 3i..3i+2 (code = sign << 2 | index); scale
+ *             plane: nu (fp16).
  * KVQ_FP8_B128 ([MLA] BlockWise1x128). Groups of 128 along the row (the last
  *             may be shorter): s = fp32(max|x|/448); code =
  *             e4m3fn(clamp(x/s, -448, 448)) (OCP E4M3, nearest-even);

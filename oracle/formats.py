@@ -179,8 +179,8 @@ def pack_lut3(x: np.ndarray):
     the decoded row's norm equal to the input's up to the fp16 rounding of nu.
     A zero row gives zero codes and nu = 0. Value = nu * (-1)^sign * M[m] / sqrt(128).
 
-    Row = 32 B magnitude plane (element i in bits 2(i%4)..2(i%4)+1 of byte i/4),
-    then 16 B sign plane (element i in bit i%8 of byte i/8); scale plane = nu.
+    Row = 48 B: the 128 codes as one little-endian 384-bit string, element i at
+    bits 3i..3i+2 (code = sign << 2 | magnitude index); scale plane = nu.
     """
     x64 = np.asarray(x, dtype=np.float32).astype(np.float64)
     _check_finite(x64)
@@ -208,13 +208,10 @@ def pack_lut3(x: np.ndarray):
     nu16 = _f16(nu64)
     if np.isinf(nu16).any():
         raise OverflowError("lut3 norm overflows fp16")
-    mp = mag.reshape(R, 32, 4)
-    mag_plane = (mp[..., 0] | (mp[..., 1] << 2) | (mp[..., 2] << 4) | (mp[..., 3] << 6)).astype(np.uint8)
-    sp = sign.reshape(R, 16, 8)
-    sign_plane = np.zeros((R, 16), dtype=np.uint8)
-    for j in range(8):
-        sign_plane |= (sp[..., j] << j).astype(np.uint8)
-    codes = np.concatenate([mag_plane, sign_plane], axis=1)
+    code = (sign << 2) | mag                                     # [R][128], 3 bits each
+    # bit 3i+k of the row is bit k of code i: unpack to bits, then pack 8 per byte
+    bits = ((code[:, :, None] >> np.arange(3, dtype=np.uint8)) & 1).reshape(R, 384)
+    codes = np.packbits(bits, axis=1, bitorder="little")
     scales = nu16.astype("<f2").view(np.uint8).reshape(R, 2).copy()
     return codes, scales
 
@@ -222,15 +219,9 @@ def pack_lut3(x: np.ndarray):
 def lut3_fields(codes):
     """Split a LUT3 code plane into per-element (magnitude index, sign bit)."""
     R = codes.shape[0]
-    mp = codes[:, :32]
-    sp = codes[:, 32:48]
-    mag = np.empty((R, 128), dtype=np.uint8)
-    for j in range(4):
-        mag[:, j::4] = (mp >> (2 * j)) & 3
-    sign = np.empty((R, 128), dtype=np.uint8)
-    for j in range(8):
-        sign[:, j::8] = (sp >> j) & 1
-    return mag, sign
+    bits = np.unpackbits(codes[:, :48], axis=1, bitorder="little").reshape(R, 128, 3)
+    code = bits[..., 0] | (bits[..., 1] << 1) | (bits[..., 2] << 2)
+    return (code & 3).astype(np.uint8), (code >> 2).astype(np.uint8)
 
 
 def unpack_lut3(codes, scales, dim=128):

@@ -66,11 +66,13 @@ def decode_row(fmt: str, code_bytes, scale_bytes, dim: int):
             out.append((c - 8) * _half(sb[2 * blk] | (sb[2 * blk + 1] << 8)))
     elif fmt == "lut3":
         nu = _half(sb[0] | (sb[1] << 8))
+        row = 0
+        for k, byte in enumerate(cb[:48]):
+            row |= byte << (8 * k)                 # the row as one 384-bit integer
         for i in range(dim):
-            mag = (cb[i // 4] >> (2 * (i % 4))) & 3
-            sgn = (cb[32 + i // 8] >> (i % 8)) & 1
-            val = _half(_M_BITS[mag])
-            out.append(nu * (-val if sgn else val) / mpmath.sqrt(128))
+            code = (row >> (3 * i)) & 7
+            val = _half(_M_BITS[code & 3])
+            out.append(nu * (-val if code >> 2 else val) / mpmath.sqrt(128))
     elif fmt == "fp8_b128":
         for i in range(dim):
             gi = i // 128

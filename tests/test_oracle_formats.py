@@ -193,14 +193,15 @@ def test_lut3_nearest_level_norm_and_idempotence():
 
 
 def test_lut3_bit_layout_single_elements():
-    for i in [0, 1, 3, 4, 7, 8, 63, 64, 127]:
+    for i in [0, 1, 2, 3, 5, 10, 21, 63, 64, 85, 127]:
         x = np.full((1, 128), 1e-3, np.float32)
         x[0, i] = -10.0
         c, s = F.pack_lut3(x)
-        # the large negative element takes the top magnitude and the sign bit
-        assert (c[0, i // 4] >> (2 * (i % 4))) & 3 == 3
-        assert (c[0, 32 + i // 8] >> (i % 8)) & 1 == 1
-        assert c[0, 32:].sum() == 1 << (i % 8)
+        row = int.from_bytes(c[0].tobytes(), "little")
+        # the large negative element is code 0b111 (sign + top magnitude) at bits 3i..3i+2;
+        # every other (small positive) element is code 0
+        assert (row >> (3 * i)) & 7 == 7
+        assert row & ~(7 << (3 * i)) == 0
     z = np.zeros((1, 128), np.float32)
     c, s = F.pack_lut3(z)
     assert not c.any() and not s.any()
