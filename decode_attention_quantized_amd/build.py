@@ -30,6 +30,7 @@ SOURCES = [
     ("kvq_pack.cpp", ["-x", "c++", "-ffp-contract=off", "-fno-fast-math"]),
     ("kvq_api.cpp", HIP_FLAGS),
     ("kvq_gqa.hip", HIP_FLAGS + ["-ffp-contract=fast"]),
+    ("kvq_mla.hip", HIP_FLAGS + ["-ffp-contract=fast"]),
 ]
 
 

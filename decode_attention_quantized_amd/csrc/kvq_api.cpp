@@ -16,6 +16,9 @@
 namespace kvq {
 size_t gqa_lds_bytes(int G, int P);
 const void* gqa_kernel(int fmt, int G);
+size_t mla_lds_bytes(int H, int P, int S);
+const void* mla_scores_kernel(int H);
+const void* mla_out_kernel();
 }  // namespace kvq
 
 namespace {
@@ -45,13 +48,58 @@ DeviceInfo device_info(int dev) {
 }
 
 struct Plan {
+  bool mla = false;
   int S = 0, P = 0, G = 0, Dv = 0;
   size_t lds = 0;
   int nwg = 0;
+  int threads = 0;
   WsLayout ws{};
+  kvq::MlaLayout mws{};
+  int64_t total = 0;
 };
 
 bool is_gqa_fmt(int fmt) { return fmt == KVQ_Q8_0 || fmt == KVQ_Q4_0 || fmt == KVQ_LUT3; }
+
+// MLA shape: H query heads over one 576-wide fp8 latent per sequence, values =
+// the first 512 dims, bf16 queries. One 4-wave workgroup per CU by default.
+int32_t make_mla_plan(const kvq_cache* k, const kvq_launch* l, int32_t ctx_len, Plan* plan) {
+  if (k->heads != 1 || k->dim != 576) return KVQ_ERR_UNSUPPORTED;
+  if (l->v_dim != 512) return KVQ_ERR_UNSUPPORTED;
+  if (l->q_dtype != KVQ_Q_BF16) return KVQ_ERR_UNSUPPORTED;
+  const int H = l->q_heads;
+  if (H != 32 && H != 64 && H != 128) return KVQ_ERR_UNSUPPORTED;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return KVQ_ERR_LAUNCH;
+  const DeviceInfo di = device_info(dev);
+  if (di.cus <= 0) return KVQ_ERR_LAUNCH;
+  int S;
+  if (l->splits > 0) {
+    S = l->splits;
+  } else {
+    int64_t s = di.cus / k->batch;
+    if (s < 1) s = 1;
+    const int64_t most = (ctx_len + 63) / 64;
+    if (s > most) s = most;
+    S = int(s);
+  }
+  int P = (ctx_len + S - 1) / S;
+  P = (P + 63) / 64 * 64;
+  S = (ctx_len + P - 1) / P;
+  if (S > 1024) return KVQ_ERR_UNSUPPORTED;
+  const size_t lds = kvq::mla_lds_bytes(H, P, S);
+  if (lds > size_t(di.max_lds)) return KVQ_ERR_UNSUPPORTED;
+  plan->mla = true;
+  plan->S = S;
+  plan->P = P;
+  plan->G = H;
+  plan->Dv = 512;
+  plan->lds = lds;
+  plan->nwg = k->batch * S;
+  plan->threads = 2 * H;
+  plan->mws = kvq::mla_ws_layout(k->batch, H, S, P);
+  plan->total = plan->mws.total;
+  return KVQ_OK;
+}
 
 // Validate shapes shared by every entry point and pick splits.
 int32_t make_plan(int32_t fmt, const kvq_cache* k, const kvq_launch* l, int32_t ctx_len, Plan* plan) {
@@ -61,6 +109,7 @@ int32_t make_plan(int32_t fmt, const kvq_cache* k, const kvq_launch* l, int32_t 
   if (l->q_heads <= 0 || l->q_heads % k->heads) return KVQ_ERR_ARG;
   if (l->q_dtype != KVQ_Q_F32 && l->q_dtype != KVQ_Q_BF16) return KVQ_ERR_ARG;
   if (ctx_len < 1 || ctx_len > k->capacity) return KVQ_ERR_RANGE;
+  if (fmt == KVQ_FP8_B128) return make_mla_plan(k, l, ctx_len, plan);
   if (!is_gqa_fmt(fmt)) return KVQ_ERR_UNSUPPORTED;
   if (k->dim != 128) return KVQ_ERR_UNSUPPORTED;
   const int G = l->q_heads / k->heads;
@@ -96,11 +145,76 @@ int32_t make_plan(int32_t fmt, const kvq_cache* k, const kvq_launch* l, int32_t 
   plan->Dv = 128;
   plan->lds = lds;
   plan->nwg = int(BG * S);
+  plan->threads = kvq::kThreads;
   plan->ws = kvq::ws_layout(k->batch, k->heads, l->q_heads, S, plan->Dv);
+  plan->total = plan->ws.total;
   return KVQ_OK;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+float sigma_log2e_of(const kvq_launch* l, int dim_qk) {
+  const float sigma = l->softmax_scale > 0.0f ? l->softmax_scale
+                                             : static_cast<float>(1.0 / std::sqrt(static_cast<double>(dim_qk)));
+  return static_cast<float>(static_cast<double>(sigma) * 1.4426950408889634);
+}
+
+hipError_t launch(const void* kern, int grid, int threads, void* arg, size_t lds, const kvq_launch* l) {
+  void* args[] = {arg};
+  const hipStream_t st = static_cast<hipStream_t>(l->stream);
+  return (l->flags & KVQ_LAUNCH_COOPERATIVE)
+             ? hipLaunchCooperativeKernel(kern, dim3(grid), dim3(threads), args, unsigned(lds), st)
+             : hipLaunchKernel(kern, dim3(grid), dim3(threads), args, unsigned(lds), st);
+}
+
+int32_t launch_mla(const void* q, const kvq_cache* kcache, const kvq_cache* vcache, int32_t ctx_len,
+                   float threshold, float* out, const kvq_launch* l, const Plan& plan) {
+  if (vcache) return KVQ_ERR_ARG;                         // the values are the latent's first 512 dims
+  if (!kcache->codes || !kcache->scales) return KVQ_ERR_ARG;
+  if (!aligned16(kcache->codes) || !aligned16(kcache->scales) || !aligned16(q) || !aligned16(out) ||
+      (l->workspace && !aligned16(l->workspace)))
+    return KVQ_ERR_ALIGN;
+  if (l->mask_out || l->phase_times) return KVQ_ERR_UNSUPPORTED;
+  if (!l->workspace || l->workspace_bytes < plan.total) return KVQ_ERR_WORKSPACE;
+  unsigned char* ws = static_cast<unsigned char*>(l->workspace);
+  kvq::MlaArgs a{};
+  a.q = q;
+  a.kc = static_cast<const uint8_t*>(kcache->codes);
+  a.ks = static_cast<const uint8_t*>(kcache->scales);
+  a.out = out;
+  a.hdr = reinterpret_cast<WsHeader*>(ws);
+  a.kept_mass = reinterpret_cast<float*>(ws + plan.mws.kept_mass);
+  a.bgstat = reinterpret_cast<unsigned long long*>(ws + plan.mws.bgstat);
+  a.split_ml = reinterpret_cast<unsigned long long*>(ws + plan.mws.split_ml);
+  a.lse = reinterpret_cast<unsigned long long*>(ws + plan.mws.lse);
+  a.kcount = reinterpret_cast<int32_t*>(ws + plan.mws.kcount);
+  a.kpairs = reinterpret_cast<int32_t*>(ws + plan.mws.kpairs);
+  a.kpos = reinterpret_cast<int32_t*>(ws + plan.mws.kpos);
+  a.kp = reinterpret_cast<float*>(ws + plan.mws.kp);
+  a.B = kcache->batch;
+  a.Hq = l->q_heads;
+  a.ctx = ctx_len;
+  a.cap = kcache->capacity;
+  a.S = plan.S;
+  a.P = plan.P;
+  a.sigma_log2e = sigma_log2e_of(l, 192);                 // default scale 1/sqrt(qk_nope + rope = 192)
+  a.tau = threshold;
+  const void* ks = kvq::mla_scores_kernel(plan.G);
+  if (!ks) return KVQ_ERR_UNSUPPORTED;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ks, plan.threads, plan.lds) != hipSuccess)
+    return KVQ_ERR_LAUNCH;
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  if (int64_t(per_cu) * device_info(dev).cus < plan.nwg) return KVQ_ERR_UNSUPPORTED;
+  hipError_t e = launch(ks, plan.nwg, plan.threads, &a, plan.lds, l);
+  if (e == hipSuccess) e = launch(kvq::mla_out_kernel(), kcache->batch * (plan.G / 32) * 4, 256, &a, 0, l);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return KVQ_ERR_LAUNCH;
+  }
+  return KVQ_OK;
+}
 
 }  // namespace
 
@@ -125,7 +239,7 @@ extern "C" int32_t kvq_workspace_bytes(int32_t fmt, const kvq_cache* kcache, con
   Plan plan;
   const int32_t rc = make_plan(fmt, kcache, l, ctx_len, &plan);
   if (rc) return rc;
-  *bytes = plan.ws.total;
+  *bytes = plan.total;
   return KVQ_OK;
 }
 
@@ -138,6 +252,7 @@ extern "C" int32_t kvq_decode_attn(const void* q, const kvq_cache* kcache, const
   Plan plan;
   int32_t rc = make_plan(fmt, kcache, l, ctx_len, &plan);
   if (rc) return rc;
+  if (plan.mla) return launch_mla(q, kcache, vcache, ctx_len, threshold, out, l, plan);
   if (!vcache) return KVQ_ERR_UNSUPPORTED;                 // latent caches: not in this kernel family
   if (vcache->batch != kcache->batch || vcache->heads != kcache->heads ||
       vcache->capacity != kcache->capacity || vcache->dim != 128)
@@ -176,9 +291,7 @@ extern "C" int32_t kvq_decode_attn(const void* q, const kvq_cache* kcache, const
   a.mask_words = (ctx_len + 31) / 32;
   a.q_bf16 = l->q_dtype == KVQ_Q_BF16;
   a.fmt = fmt;
-  const float sigma = l->softmax_scale > 0.0f ? l->softmax_scale
-                                             : static_cast<float>(1.0 / std::sqrt(static_cast<double>(kcache->dim)));
-  a.sigma_log2e = static_cast<float>(static_cast<double>(sigma) * 1.4426950408889634);
+  a.sigma_log2e = sigma_log2e_of(l, kcache->dim);
   a.tau = threshold;
   a.times = reinterpret_cast<unsigned long long*>(l->phase_times);
 
@@ -190,12 +303,7 @@ extern "C" int32_t kvq_decode_attn(const void* q, const kvq_cache* kcache, const
   int dev = 0;
   (void)hipGetDevice(&dev);
   if (int64_t(per_cu) * device_info(dev).cus < plan.nwg) return KVQ_ERR_UNSUPPORTED;
-  void* args[] = {&a};
-  const hipStream_t st = static_cast<hipStream_t>(l->stream);
-  const hipError_t e =
-      (l->flags & KVQ_LAUNCH_COOPERATIVE)
-          ? hipLaunchCooperativeKernel(kern, dim3(plan.nwg), dim3(kvq::kThreads), args, unsigned(plan.lds), st)
-          : hipLaunchKernel(kern, dim3(plan.nwg), dim3(kvq::kThreads), args, unsigned(plan.lds), st);
+  const hipError_t e = launch(kern, plan.nwg, kvq::kThreads, &a, plan.lds, l);
   if (e != hipSuccess) {
     (void)hipGetLastError();
     return KVQ_ERR_LAUNCH;
@@ -221,12 +329,11 @@ extern "C" int32_t kvq_stats(const kvq_launch* l, kvq_stats_t* out, float* kept_
   if (hipMemcpy(&h, l->workspace, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess) return KVQ_ERR_LAUNCH;
   std::memset(out, 0, sizeof(*out));
   const int G = h.kv_heads > 0 ? h.q_heads / h.kv_heads : 0;
-  int64_t cb = 0, sb = 0;
-  if (h.batch > 0 && kvq_row_bytes(h.fmt, 128, &cb, &sb) == KVQ_OK) {
+  if (h.batch > 0) {
     out->positions = int64_t(h.batch) * h.kv_heads * h.ctx;
     out->pairs = int64_t(h.batch) * h.q_heads * h.ctx;
-    out->k_bytes = out->positions * (cb + sb);
-    out->v_bytes_dense = out->positions * (cb + sb);
+    out->k_bytes = out->positions * h.k_row_bytes;
+    out->v_bytes_dense = out->positions * h.v_row_bytes;
   }
   (void)G;
   if (h.batch > 0) {
@@ -240,7 +347,7 @@ extern "C" int32_t kvq_stats(const kvq_launch* l, kvq_stats_t* out, float* kept_
       out->kept_pairs += int64_t(st[2 * i]);
       out->rows_fetched += int64_t(st[2 * i + 1]);
     }
-    out->v_bytes = out->rows_fetched * (cb + sb);
+    out->v_bytes = out->rows_fetched * h.v_row_bytes;
   }
   out->status = int32_t(h.status);
   out->splits = h.splits;

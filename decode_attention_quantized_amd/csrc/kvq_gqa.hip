@@ -351,6 +351,8 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     a.hdr->batch = a.B; a.hdr->q_heads = a.Hq; a.hdr->kv_heads = a.Hkv; a.hdr->ctx = ctx;
     a.hdr->splits = a.S; a.hdr->positions_per_split = P; a.hdr->fmt = FMT; a.hdr->v_dim = 128;
     a.hdr->nwg = int(gridDim.x);
+    a.hdr->k_row_bytes = T::CB + T::SB;
+    a.hdr->v_row_bytes = T::CB + T::SB;
   }
   // q of this group: per-head max |q| -> power-of-two prescale, then fp16 hi/lo rows
   float qv[4];

@@ -24,8 +24,9 @@ struct WsHeader {
   unsigned long long reserved3;
   int32_t batch, q_heads, kv_heads, ctx;
   int32_t splits, positions_per_split, fmt, v_dim;
-  int32_t nwg, pad2;
-  uint8_t pad1[256 - 16 - 16 - 32 - 8];
+  int32_t nwg, k_row_bytes;
+  int32_t v_row_bytes, pad2;
+  uint8_t pad1[256 - 16 - 16 - 32 - 16];
 };
 static_assert(sizeof(WsHeader) == 256, "header is one 256-byte line");
 
@@ -88,6 +89,47 @@ struct GqaArgs {
   float tau;                      // threshold on the normalized weight
   unsigned long long* times;      // optional [nwg][16] phase stamps
 };
+
+// Arguments of the two MLA kernels.
+struct MlaArgs {
+  const void* q;                  // [B][H][576] bfloat16
+  const uint8_t* kc;              // latent code plane [B][cap][576] (e4m3)
+  const uint8_t* ks;              // latent scale plane [B][cap][5] (fp32)
+  float* out;                     // [B][H][512]
+  WsHeader* hdr;
+  float* kept_mass;               // [B][H]
+  unsigned long long* bgstat;     // [B][2]
+  unsigned long long* split_ml;   // tagged [B][S][H][2]
+  unsigned long long* lse;        // tagged [B][H]
+  int32_t* kcount;                // [B][S] kept rows published by each split
+  int32_t* kpairs;                // [B][S] kept (head, position) pairs per split
+  int32_t* kpos;                  // [B][S][P] positions of kept rows
+  float* kp;                      // [B][S][P][H] weights of kept rows (0 where a head skips)
+  int32_t B, Hq, ctx, cap;
+  int32_t S, P;
+  float sigma_log2e;
+  float tau;
+};
+
+struct MlaLayout {
+  int64_t kept_mass, bgstat, split_ml, lse, kcount, kpairs, kpos, kp, total;
+};
+
+// The first two regions match ws_layout() so kvq_stats reads both families alike.
+inline MlaLayout mla_ws_layout(int B, int H, int S, int P) {
+  MlaLayout w;
+  int64_t off = 256;
+  w.kept_mass = off; off = align256(off + int64_t(B) * H * 4);
+  w.bgstat = off;    off = align256(off + int64_t(B) * 16);
+  w.split_ml = off;  off = align256(off + int64_t(B) * S * H * 16);
+  w.lse = off;       off = align256(off + int64_t(B) * H * 8);
+  w.kcount = off;    off = align256(off + int64_t(B) * S * 4);
+  w.kpairs = off;    off = align256(off + int64_t(B) * S * 4);
+  w.kpos = off;      off = align256(off + int64_t(B) * S * P * 4);
+  w.kp = off;        off = align256(off + int64_t(B) * S * P * int64_t(H) * 4);
+  w.total = off;
+  return w;
+}
 
 constexpr int kStamps = 7;        // phase stamps per workgroup (5 and 6 only by a group's merging workgroup)
 
