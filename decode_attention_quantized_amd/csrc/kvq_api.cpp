@@ -174,7 +174,7 @@ int32_t launch_mla(const void* q, const kvq_cache* kcache, const kvq_cache* vcac
   if (!aligned16(kcache->codes) || !aligned16(kcache->scales) || !aligned16(q) || !aligned16(out) ||
       (l->workspace && !aligned16(l->workspace)))
     return KVQ_ERR_ALIGN;
-  if (l->mask_out || l->phase_times) return KVQ_ERR_UNSUPPORTED;
+  if (l->mask_out) return KVQ_ERR_UNSUPPORTED;
   if (!l->workspace || l->workspace_bytes < plan.total) return KVQ_ERR_WORKSPACE;
   unsigned char* ws = static_cast<unsigned char*>(l->workspace);
   kvq::MlaArgs a{};
@@ -199,6 +199,7 @@ int32_t launch_mla(const void* q, const kvq_cache* kcache, const kvq_cache* vcac
   a.P = plan.P;
   a.sigma_log2e = sigma_log2e_of(l, 192);                 // default scale 1/sqrt(qk_nope + rope = 192)
   a.tau = threshold;
+  a.times = reinterpret_cast<unsigned long long*>(l->phase_times);
   const void* ks = kvq::mla_scores_kernel(plan.G);
   if (!ks) return KVQ_ERR_UNSUPPORTED;
   int per_cu = 0;
@@ -317,7 +318,7 @@ extern "C" int32_t kvq_phase_count(const kvq_launch* l, int32_t* workgroups, int
   WsHeader h;
   if (hipMemcpy(&h, l->workspace, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess) return KVQ_ERR_LAUNCH;
   *workgroups = h.nwg;
-  *stamps = kvq::kStamps;
+  *stamps = h.fmt == KVQ_FP8_B128 ? kvq::kMlaStamps : kvq::kStamps;
   return KVQ_OK;
 }
 

@@ -109,6 +109,7 @@ struct MlaArgs {
   int32_t S, P;
   float sigma_log2e;
   float tau;
+  unsigned long long* times;      // optional [nwg][16] phase stamps of mla_scores
 };
 
 struct MlaLayout {
@@ -132,5 +133,6 @@ inline MlaLayout mla_ws_layout(int B, int H, int S, int P) {
 }
 
 constexpr int kStamps = 7;        // phase stamps per workgroup (5 and 6 only by a group's merging workgroup)
+constexpr int kMlaStamps = 5;     // latent path: start, scores start, scores end, lse known, lists published
 
 }  // namespace kvq

@@ -10,12 +10,13 @@
 //
 // Two launches on the caller's stream:
 //  mla_scores  (one workgroup per (sequence, split); wave w owns heads
-//              32w..32w+31 with q resident in registers as f16 MFMA operands)
-//    1. streams 32-row latent tiles through LDS (double-buffered), scores
-//       them with v_mfma_f32_32x32x16_f16 (fp8 -> f16 with the hardware
-//       converter, exact), applies the per-group fp32 scale to the fp32
-//       accumulator, keeps per-head (max, sum exp2) and a per-(head,
-//       64-position tile) maximum;
+//              32w..32w+31 with q resident in registers as bf16 MFMA operands)
+//    1. streams 32-row latent tiles into a 4-deep LDS ring with direct
+//       global->LDS loads (three tiles in flight), scores them with
+//       v_mfma_f32_32x32x16_bf16 (fp8 -> bf16 with the hardware converter,
+//       exact), applies the per-group fp32 scale to the fp32 accumulators,
+//       keeps per-head (max, sum exp2) and a per-(head, 64-position tile)
+//       maximum;
 //    2. the group's split statistics are merged into per-head log-sum-exps
 //       (head h by split h mod S) and exchanged as epoch-tagged words;
 //    3. re-scores only the 64-position tiles whose maximum can reach the
@@ -36,7 +37,7 @@ namespace kvq {
 
 namespace mla {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef unsigned long long u64;
@@ -45,10 +46,23 @@ constexpr int D = 576;          // latent width (scores)
 constexpr int DV = 512;         // value width
 constexpr int KSTEPS = D / 16;  // 36 MFMA k-steps of 16 dims
 constexpr int NGROUPS = 5;      // scale groups: 4 x 128 + 1 x 64
-constexpr int ROW_LDS = 584;    // LDS pitch of a staged latent row (576 + 8; keeps b64 reads conflict-free)
+constexpr int ROW_LDS = 592;    // LDS pitch of a staged latent row: 37 x 16 bytes (odd), so the 16-byte
+                                // reads of 8 consecutive rows hit distinct bank groups
 constexpr int TILE = 32;        // positions per MFMA tile
 constexpr int LTILE = 64;       // positions per liveness tile
 constexpr uint32_t kSpinLimit = 1u << 23;
+
+// LDS ring of staged tiles. A buffer holds 32 latent rows at ROW_LDS pitch
+// (37 slots of 16 bytes, the last one padding) followed by the 32 x 5 scales.
+// Direct global->LDS loads write 64 consecutive 16-byte slots per wave
+// instruction, so the padded layout is produced by the lane -> chunk mapping.
+constexpr int PITCH16 = ROW_LDS / 16;          // 37
+constexpr int NCHUNK_I = 19;                   // chunk instructions per tile (19 x 64 >= 32 x 37 slots)
+constexpr int NSCALE_I = 3;                    // scale instructions per tile (3 x 64 >= 160 dwords)
+constexpr int NDMA = NCHUNK_I + NSCALE_I;      // wave instructions per tile
+constexpr int SC_OFF = NCHUNK_I * 64 * 16;     // byte offset of the scales in a buffer
+constexpr int BUF_BYTES = SC_OFF + NSCALE_I * 64 * 4;
+constexpr int NBUF = 4;                        // ring depth: three tiles in flight while one is scored
 
 __device__ inline void put_tagged_f(u64* p, uint32_t epoch, float v) {
   __hip_atomic_store(p, (u64(epoch) << 32) | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -73,23 +87,206 @@ __device__ inline float2 lse_merge(float2 x, float2 y) {
   return make_float2(M, x.y * exp2f(x.x - M) + y.y * exp2f(y.x - M));
 }
 
-__device__ inline void online_add(float& m, float& l, float s) {
-  if (s == -INFINITY) return;
-  if (s > m) { l = l * exp2f(m - s) + 1.f; m = s; }
-  else l += exp2f(s - m);
+// 2^x with the hardware instruction (results below the normal range flush to 0)
+__device__ inline float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int CTRL>
+__device__ inline float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+// lane j <- lane j ^ 16 within each half of the wave (swizzle, bit-mask mode)
+__device__ inline float swz16(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
 }
 
-// 8 fp8 e4m3 bytes -> 8 f16 (exact: every e4m3 value is an f16 value)
-__device__ inline half8 fp8x8_to_f16(uint2 w) {
+// Reduce 16 independent values over the 32 lanes of each wave half (max or
+// sum), every lane getting the result. Steps: neighbour in quad, other pair
+// in quad, mirrored quad in the 8-lane half row, mirrored half row, other row.
+template <bool MAX>
+__device__ inline void reduce32x16(float (&v)[16]) {
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+  float t[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) t[e] = dpp<0xB1>(v[e]);     // quad_perm [1,0,3,2]
+#pragma unroll
+  for (int e = 0; e < 16; ++e) v[e] = op(v[e], t[e]);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) t[e] = dpp<0x4E>(v[e]);     // quad_perm [2,3,0,1]
+#pragma unroll
+  for (int e = 0; e < 16; ++e) v[e] = op(v[e], t[e]);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) t[e] = dpp<0x141>(v[e]);    // row_half_mirror
+#pragma unroll
+  for (int e = 0; e < 16; ++e) v[e] = op(v[e], t[e]);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) t[e] = dpp<0x140>(v[e]);    // row_mirror
+#pragma unroll
+  for (int e = 0; e < 16; ++e) v[e] = op(v[e], t[e]);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) t[e] = swz16(v[e]);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) v[e] = op(v[e], t[e]);
+}
+
+// 8 fp8 e4m3 bytes -> 8 bf16 (exact: every e4m3 value, subnormals included,
+// is a bf16 value)
+__device__ inline bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
   uint4 u;
-  u.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.0f, false));
-  u.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.0f, true));
-  u.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.0f, false));
-  u.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.0f, true));
-  return __builtin_bit_cast(half8, u);
+  u.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
+  u.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
+  u.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
+  u.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
+  return __builtin_bit_cast(bf16x8, u);
 }
 
-__device__ inline int group_of_kstep(int ks) { return ks < 32 ? ks >> 3 : 4; }
+template <int N>
+__device__ inline void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));   // vmcnt(N), other counters untouched
+}
+
+// Wait until at most k later tiles' direct loads of this wave are in flight
+// (loads complete in order, so the tile before them has landed in LDS).
+// Wave w issues the instructions j = w, w + NW, ... < NDMA of every tile.
+template <int NW>
+__device__ inline void wait_tiles(int k, int wave) {
+  constexpr int base = NDMA / NW, extra = NDMA % NW;
+  if (wave < extra) {
+    if (k >= 2) wait_vm<2 * (base + 1)>(); else if (k == 1) wait_vm<base + 1>(); else wait_vm<0>();
+  } else {
+    if (k >= 2) wait_vm<2 * base>(); else if (k == 1) wait_vm<base>(); else wait_vm<0>();
+  }
+}
+
+// Barrier between the waves of the workgroup without a memory fence (a fence
+// would wait for every load in flight, including the tiles being prefetched);
+// the empty asm keeps the compiler from moving memory accesses across it.
+__device__ inline void bar_nofence() {
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+struct TileSrc {
+  const uint8_t* kc;
+  const float* ks;
+  int64_t row0;
+  int ctx;
+};
+
+// Issue this wave's direct loads of the tile starting at position `first`
+// into buffer `dst`. Rows at or past ctx (and padding slots) repeat a real
+// chunk of row ctx-1, so every instruction runs with all lanes and the
+// per-wave instruction count is the same for every tile.
+template <int NW>
+__device__ __attribute__((always_inline)) inline void issue_tile(uint8_t* __restrict__ dst, const TileSrc& src,
+                                                                 int first, int wave, int lane) {
+  for (int j = wave; j < NDMA; j += NW) {
+    if (j < NCHUNK_I) {
+      const int sl = 64 * j + lane;
+      int r = sl / PITCH16, c = sl - r * PITCH16;
+      r = min(r, TILE - 1);
+      c = min(c, D / 16 - 1);
+      const int pos = min(first + r, src.ctx - 1);
+      __builtin_amdgcn_global_load_lds(src.kc + (src.row0 + pos) * D + c * 16, dst + j * 1024, 16, 0, 0);
+    } else {
+      const int i = 64 * (j - NCHUNK_I) + lane;
+      int64_t gi = (src.row0 + first) * NGROUPS + min(i, TILE * NGROUPS - 1);
+      gi = min(gi, (src.row0 + src.ctx) * NGROUPS - 1);
+      __builtin_amdgcn_global_load_lds(src.ks + gi, dst + SC_OFF + (j - NCHUNK_I) * 256, 4, 0, 0);
+    }
+  }
+}
+
+// Scores of one staged tile (log2 domain): 16 heads of this lane x its
+// column. MFMA k order: step ks = 2p + e takes, in k-half kh, the latent dims
+// 32p + 16kh + 8e .. +7, so one 16-byte LDS read of chunk 2p + kh of a row
+// feeds steps 2p and 2p + 1, and every step stays inside one scale group
+// (group g = steps 8g .. 8g + 7, the last group has 4). The groups accumulate
+// separately (their fp32 scales differ per row); the operands of the next
+// group are read while the current group's MFMAs run.
+__device__ __attribute__((always_inline)) inline void score_tile(const uint8_t* __restrict__ buf,
+                                                                 const bf16x8 (&A)[KSTEPS], float hs, int col, int kh,
+                                                                 bool valid, float (&s2)[16]) {
+  const uint8_t* src = buf + col * ROW_LDS + 16 * kh;
+  const float* sc = reinterpret_cast<const float*>(buf + SC_OFF) + col * NGROUPS;
+  constexpr int NP = KSTEPS / 2;                     // 18 step pairs
+  uint4 cur[4], nxt[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) cur[j] = *reinterpret_cast<const uint4*>(src + 32 * j);
+  floatx16 cg[NGROUPS];
+#pragma unroll
+  for (int g = 0; g < NGROUPS; ++g) {
+    const int np = g < 4 ? 4 : 2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (4 * (g + 1) + j < NP) nxt[j] = *reinterpret_cast<const uint4*>(src + 32 * (4 * (g + 1) + j));
+    floatx16 c = {};
+#pragma unroll
+    for (int j = 0; j < np; ++j) {
+      const int p = 4 * g + j;
+      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[2 * p], fp8x8_to_bf16(cur[j].x, cur[j].y), c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[2 * p + 1], fp8x8_to_bf16(cur[j].z, cur[j].w), c, 0, 0, 0);
+    }
+    cg[g] = c;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cur[j] = nxt[j];
+  }
+  const float g0 = sc[0] * hs, g1 = sc[1] * hs, g2 = sc[2] * hs, g3 = sc[3] * hs, g4 = sc[4] * hs;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    float v = g0 * cg[0][e];
+    v = fmaf(g1, cg[1][e], v);
+    v = fmaf(g2, cg[2][e], v);
+    v = fmaf(g3, cg[3][e], v);
+    v = fmaf(g4, cg[4][e], v);
+    s2[e] = valid ? v : -INFINITY;
+  }
+}
+
+// One tile of the scoring pass: start the direct loads of a later tile into
+// `wr` (when given), score the tile staged in `rd`, and fold it into the
+// split statistics. The restrict qualifiers state that the buffer being
+// filled, the buffer being read and the tile-maximum table are disjoint, so
+// the compiler adds no wait for the loads in flight; the waits that order a
+// tile's loads before its reads are explicit (wait_tiles + bar_nofence).
+template <int NW>
+__device__ __attribute__((always_inline)) inline void scoring_step(
+    uint8_t* __restrict__ wr, const uint8_t* __restrict__ rd, float* __restrict__ tmax, const TileSrc& src,
+    int next_first, int wave, int lane, int t, int pos, int nlt, const bf16x8 (&A)[KSTEPS], float hs,
+    float (&m)[16], float (&l)[16], float (&sprev)[16]) {
+  const int col = lane & 31, kh = lane >> 5;
+  if (wr) issue_tile<NW>(wr, src, next_first, wave, lane);
+  float s2[16];
+  score_tile(rd, A, hs, col, kh, pos < src.ctx, s2);
+  if ((t & 1) == 0) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sprev[e] = s2[e];
+    return;
+  }
+  // end of a 64-position liveness tile: its maximum per head becomes the
+  // running reference of the lane-local sums
+  float tm[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) tm[e] = fmaxf(sprev[e], s2[e]);
+  reduce32x16<true>(tm);
+  if (col == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) tmax[(32 * wave + 8 * i + 4 * kh + j) * nlt + (t >> 1)] = tm[4 * i + j];
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float mn = fmaxf(m[e], tm[e]);
+    const float ms = mn == -INFINITY ? 0.f : mn;  // nothing valid yet: every term is 0
+    l[e] = l[e] * ex2(m[e] - ms) + ex2(sprev[e] - ms) + ex2(s2[e] - ms);
+    m[e] = mn;
+  }
+}
+
+__device__ inline void stamp_mla(const MlaArgs& a, int k) {
+  if (a.times && threadIdx.x == 0) a.times[int64_t(blockIdx.x) * 16 + k] = wall_clock64();
+}
 
 }  // namespace mla
 
@@ -103,12 +300,10 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int P = a.P;
   const int NLT = P / LTILE;          // liveness tiles per split
-  uint8_t* tiles = smem;                                                 // [2][32][ROW_LDS]
-  float* tscale = reinterpret_cast<float*>(tiles + 2 * TILE * ROW_LDS);  // [2][32][5]
-  float* tmax = tscale + 2 * TILE * NGROUPS;                             // [H][NLT]
+  uint8_t* ring = smem;                                                  // [NBUF][BUF_BYTES]
+  float* tmax = reinterpret_cast<float*>(ring + NBUF * BUF_BYTES);       // [H][NLT]
   float* lse = tmax + H * NLT;                                           // [H]
-  float* hsl = lse + H;                                                  // [H] per-head score scale
-  int* live = reinterpret_cast<int*>(hsl + H);                           // [NLT (+pad)]
+  int* live = reinterpret_cast<int*>(lse + H);                           // [NLT (+pad)]
   unsigned* keepmask = reinterpret_cast<unsigned*>(live + ((NLT + 3) & ~3));  // [TILE]
   int* misc = reinterpret_cast<int*>(keepmask + TILE);                   // [8]
   float2* mlbuf = reinterpret_cast<float2*>(misc + 8);                   // [H + S] scratch (16-B aligned)
@@ -126,6 +321,7 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
   const int kh = lane >> 5;           // k half (0: dims 0..7 of a k-step, 1: 8..15)
   const int head_a = 32 * wave + col; // head of this lane's A operand row
 
+  stamp_mla(a, 0);
   if (blockIdx.x == 0 && tid == 0) {
     a.hdr->batch = a.B; a.hdr->q_heads = H; a.hdr->kv_heads = 1; a.hdr->ctx = ctx;
     a.hdr->splits = a.S; a.hdr->positions_per_split = P; a.hdr->fmt = KVQ_FP8_B128; a.hdr->v_dim = DV;
@@ -135,161 +331,76 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
   }
 
   // ---------------------------------------------------------------- tile staging
-  // a 32-row tile = 32 x 36 chunks of 16 bytes + 32 x 5 scales; loads go to
-  // registers first so they can be in flight while the previous tile computes
+  // Register staging of one tile into buffer 0 (the re-scoring pass).
   constexpr int CHUNKS = TILE * (D / 16);
   constexpr int PER = (CHUNKS + NT - 1) / NT;
   constexpr int NSC = TILE * NGROUPS;
   constexpr int PERS = (NSC + NT - 1) / NT;
-  struct Staged { uint4 v[PER]; float s[PERS]; };
-  auto stage_load = [&](int t) {
-    Staged st;
+  auto stage = [&](int t) {
+    uint4 v[PER];
+    float sv[PERS];
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int i = tid + k * NT;
       const int r = i / (D / 16), c = i - r * (D / 16);
       const int pos = pos0 + t * TILE + r;
-      st.v[k] = (i < CHUNKS && pos < ctx) ? *reinterpret_cast<const uint4*>(a.kc + (row0 + pos) * D + c * 16)
-                                          : make_uint4(0u, 0u, 0u, 0u);
+      v[k] = (i < CHUNKS && pos < ctx) ? *reinterpret_cast<const uint4*>(a.kc + (row0 + pos) * D + c * 16)
+                                       : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int k = 0; k < PERS; ++k) {
       const int i = tid + k * NT;
       const int r = i / NGROUPS, gi = i - r * NGROUPS;
       const int pos = pos0 + t * TILE + r;
-      st.s[k] = (i < NSC && pos < ctx) ? reinterpret_cast<const float*>(a.ks + (row0 + pos) * (4 * NGROUPS))[gi]
-                                       : 0.f;
+      sv[k] = (i < NSC && pos < ctx) ? reinterpret_cast<const float*>(a.ks + (row0 + pos) * (4 * NGROUPS))[gi] : 0.f;
     }
-    return st;
-  };
-  auto stage_store = [&](const Staged& st, int buf) {
-    uint8_t* dst = tiles + buf * TILE * ROW_LDS;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int i = tid + k * NT;
       if (i < CHUNKS) {
         const int r = i / (D / 16), c = i - r * (D / 16);
-        uint2* d2 = reinterpret_cast<uint2*>(dst + r * ROW_LDS + c * 16);
-        d2[0] = make_uint2(st.v[k].x, st.v[k].y);
-        d2[1] = make_uint2(st.v[k].z, st.v[k].w);
+        *reinterpret_cast<uint4*>(ring + r * ROW_LDS + c * 16) = v[k];
       }
     }
 #pragma unroll
     for (int k = 0; k < PERS; ++k)
-      if (tid + k * NT < NSC) tscale[buf * NSC + tid + k * NT] = st.s[k];
+      if (tid + k * NT < NSC) reinterpret_cast<float*>(ring + SC_OFF)[tid + k * NT] = sv[k];
   };
-  auto stage = [&](int t, int buf) { stage_store(stage_load(t), buf); };
+  const TileSrc src{a.kc, reinterpret_cast<const float*>(a.ks), row0, ctx};
+  const int T = P / TILE;
+  // the first three tiles start loading before the query is set up
+  for (int t = 0; t < 3 && t < T; ++t) issue_tile<NW>(ring + t * BUF_BYTES, src, pos0 + t * TILE, wave, lane);
 
   // ---------------------------------------------------------------- q operands
-  // per-head power-of-two prescale so the bf16 query fits f16 without loss
-  half8 A[KSTEPS];
+  // The bf16 query is the A operand as it is, in the k order of score_tile.
+  bf16x8 A[KSTEPS];
   {
-    float mx = 0.f;
-    const uint16_t* qh = reinterpret_cast<const uint16_t*>(a.q) + (int64_t(b) * H + head_a) * D + 8 * kh;
-    uint4 raw[KSTEPS];
+    const uint16_t* qh = reinterpret_cast<const uint16_t*>(a.q) + (int64_t(b) * H + head_a) * D + 16 * kh;
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) raw[ks] = *reinterpret_cast<const uint4*>(qh + 16 * ks);
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const uint32_t w[4] = {raw[ks].x, raw[ks].y, raw[ks].z, raw[ks].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        mx = fmaxf(mx, fabsf(__uint_as_float(w[e] << 16)));
-        mx = fmaxf(mx, fabsf(__uint_as_float(w[e] & 0xFFFF0000u)));
-      }
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const int ex = (mx > 0.f) ? ilogbf(mx) + 1 : 0;
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const uint32_t w[4] = {raw[ks].x, raw[ks].y, raw[ks].z, raw[ks].w};
-      half8 h;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        h[2 * e] = _Float16(ldexpf(__uint_as_float(w[e] << 16), -ex));
-        h[2 * e + 1] = _Float16(ldexpf(__uint_as_float(w[e] & 0xFFFF0000u), -ex));
-      }
-      A[ks] = h;
-    }
-    if (kh == 0) hsl[head_a] = ldexpf(a.sigma_log2e, ex);
+    for (int ks = 0; ks < KSTEPS; ++ks)
+      A[ks] = *reinterpret_cast<const bf16x8*>(qh + 32 * (ks >> 1) + 8 * (ks & 1));
   }
-  stage(0, 0);
-  __syncthreads();
-  // per-accumulator head scale: accumulator 4i+j of lane holds head 8i + 4kh + j (of this wave)
-  float hsc[16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) hsc[4 * i + j] = hsl[32 * wave + 8 * i + 4 * kh + j];
-
-  // scores of staged tile `buf` (log2 domain), 16 heads of this lane x its column
-  auto score_tile = [&](int buf, int t, floatx16& s2) {
-    const uint8_t* src = tiles + buf * TILE * ROW_LDS + col * ROW_LDS + 8 * kh;
-    const float* sc = tscale + buf * TILE * NGROUPS + col * NGROUPS;
-    floatx16 acc = {};
-#pragma unroll
-    for (int g = 0; g < NGROUPS; ++g) {
-      floatx16 cg = {};
-      const int k0 = 8 * g, k1 = (g < 4) ? 8 * g + 8 : KSTEPS;
-#pragma unroll
-      for (int ks = k0; ks < k1; ++ks) {
-        const uint2 w = *reinterpret_cast<const uint2*>(src + 16 * ks);
-        cg = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[ks], fp8x8_to_f16(w), cg, 0, 0, 0);
-      }
-      const float s = sc[g];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[e] = fmaf(s, cg[e], acc[e]);
-    }
-    const bool valid = pos0 + t * TILE + col < ctx;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) s2[e] = valid ? acc[e] * hsc[e] : -INFINITY;
-  };
+  const float hs = a.sigma_log2e;     // score scale: softmax scale * log2 e
 
   // ---------------------------------------------------------------- phase 1
-  float m[16], l[16], tm[16];
+  // Per 64-position tile: the tile maximum per head (reduced over the 32
+  // columns) becomes the running reference m, every lane adds exp2(s - m) of
+  // its own two scores to a lane-local sum l (rescaled when m grows).
+  stamp_mla(a, 1);
+  float m[16], l[16], sprev[16];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) { m[e] = -INFINITY; l[e] = 0.f; tm[e] = -INFINITY; }
-  const int T = P / TILE;
+  for (int e = 0; e < 16; ++e) { m[e] = -INFINITY; l[e] = 0.f; sprev[e] = -INFINITY; }
   for (int t = 0; t < T; ++t) {
-    Staged nxt;
-    if (t + 1 < T) nxt = stage_load(t + 1);         // next tile's loads overlap this tile's MFMAs
-    floatx16 s2;
-    score_tile(t & 1, t, s2);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) { online_add(m[e], l[e], s2[e]); tm[e] = fmaxf(tm[e], s2[e]); }
-    if (t & 1) {                                    // end of a 64-position liveness tile
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float v = tm[e];
-#pragma unroll
-        for (int o = 16; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 32));
-        tm[e] = v;
-      }
-      if (col == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) tmax[(32 * wave + 8 * i + 4 * kh + j) * NLT + (t >> 1)] = tm[4 * i + j];
-      }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) tm[e] = -INFINITY;
-    }
-    if (t + 1 < T) stage_store(nxt, (t + 1) & 1);
-    __syncthreads();                                // buffer (t & 1) free; buffer (t+1)&1 staged
+    wait_tiles<NW>(min(2, T - 1 - t), wave);       // this wave's loads of tile t have landed
+    bar_nofence();                                  // everyone's have; buffer (t+3) % NBUF is free
+    uint8_t* wr = t + 3 < T ? ring + ((t + 3) % NBUF) * BUF_BYTES : nullptr;
+    scoring_step<NW>(wr, ring + (t % NBUF) * BUF_BYTES, tmax, src, pos0 + (t + 3) * TILE, wave, lane, t,
+                     pos0 + t * TILE + col, NLT, A, hs, m, l, sprev);
   }
-  // split statistics per head: merge over the 32 columns, publish
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    float2 x = make_float2(m[e], l[e]);
-#pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) {
-      float2 y;
-      y.x = __shfl_xor(x.x, o, 32);
-      y.y = __shfl_xor(x.y, o, 32);
-      x = lse_merge(x, y);
-    }
-    m[e] = x.x; l[e] = x.y;
-  }
+  __syncthreads();
+  stamp_mla(a, 2);
+  // split statistics per head: m is already common to the 32 columns; sum l
+  reduce32x16<false>(l);
   if (col == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -329,6 +440,7 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
     }
     __syncthreads();
   }
+  stamp_mla(a, 3);
 
   // ---------------------------------------------------------------- phase 3: live tiles
   // A 64-position tile is live when some head's tile maximum can reach the
@@ -357,11 +469,11 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
     const int u = live[li];
     for (int half = 0; half < 2; ++half) {
       const int t = 2 * u + half;
-      stage(t, 0);
+      stage(t);
       if (tid < TILE) keepmask[tid] = 0u;
       __syncthreads();
-      floatx16 s2;
-      score_tile(0, t, s2);
+      float s2[16];
+      score_tile(ring, A, hs, col, kh, pos0 + t * TILE + col < ctx, s2);
       // normalized weights and keep bits
       unsigned bits = 0u;
       float p[16];
@@ -370,7 +482,7 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int e = 4 * i + j;
-          const float pe = (s2[e] == -INFINITY) ? 0.f : exp2f(s2[e] - lse[32 * wave + 8 * i + 4 * kh + j]);
+          const float pe = ex2(s2[e] - lse[32 * wave + 8 * i + 4 * kh + j]);
           const bool keep = (s2[e] != -INFINITY) && pe >= a.tau;
           p[e] = keep ? pe : 0.f;
           bits |= keep ? 1u : 0u;
@@ -407,6 +519,7 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
     a.kcount[kbase] = misc[1];
     a.kpairs[kbase] = misc[2];
   }
+  stamp_mla(a, 4);
 }
 
 // ----------------------------------------------------------------------------- out
@@ -493,7 +606,7 @@ __global__ __launch_bounds__(256) void mla_out(MlaArgs a) {
 // the sizes below guarantee (every earlier region is a multiple of 16 bytes).
 size_t mla_lds_bytes(int H, int P, int S) {
   const int NLT = P / LTILE;
-  return size_t(2) * TILE * ROW_LDS + 2 * TILE * NGROUPS * 4 + size_t(H) * NLT * 4 + 2 * size_t(H) * 4 +
+  return size_t(NBUF) * BUF_BYTES + size_t(H) * NLT * 4 + size_t(H) * 4 +
          size_t((NLT + 3) & ~3) * 4 + TILE * 4 + 8 * 4 + size_t(H + S) * 8 + 64;
 }
 
