@@ -29,9 +29,9 @@ HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", 
 SOURCES = [
     ("kvq_pack.cpp", ["-x", "c++", "-ffp-contract=off", "-fno-fast-math"]),
     ("kvq_api.cpp", HIP_FLAGS),
-    ("kvq_gqa.hip", HIP_FLAGS + ["-ffp-contract=fast"]),
-    # the latent kernel never produces or tests NaN; without NaN semantics
-    # fmaxf needs no input quieting and folds into DPP reductions
+    # the kernels never produce or test NaN; without NaN semantics fmaxf
+    # needs no input quieting and folds into DPP reductions
+    ("kvq_gqa.hip", HIP_FLAGS + ["-ffp-contract=fast", "-fno-honor-nans"]),
     ("kvq_mla.hip", HIP_FLAGS + ["-ffp-contract=fast", "-fno-honor-nans"]),
 ]
 

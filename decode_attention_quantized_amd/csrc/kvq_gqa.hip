@@ -1,29 +1,31 @@
 // Fused sparse-V decode attention for grouped-query caches (q8_0, q4_0, LUT3)
-// on gfx950. One cooperative launch per call; phases are separated by grid
-// barriers so the scores of a whole context never leave the chip:
+// on gfx950. One launch per call; all workgroups are resident at once (at
+// most one per compute unit) and the workgroups of one (sequence, kv head)
+// group exchange data through workspace words tagged with the call's epoch,
+// so the scores of a whole context never leave the chip:
 //
 //  1. K pass. Each workgroup owns P consecutive positions of one (sequence,
 //     kv head). Waves stream 16-position tiles of packed K rows, dequantize
 //     the codes straight into MFMA operands and form the scores of all G
 //     query heads of the group with v_mfma_f32_16x16x32_f16 (q split into
 //     fp16 hi + lo halves, so the products keep ~22 bits of q). Scores stay in
-//     LDS; the split's running (max, sum of exp) per head goes to HBM.
-//  2. Grid barrier, then every workgroup merges the split statistics of its
-//     heads into the log-sum-exp (same order everywhere, so all workgroups of
+//     LDS; the split's running (max, sum of exp) per head is published.
+//  2. Every workgroup gathers the split statistics of its group and merges
+//     them into the log-sum-exp (same order everywhere, so all workgroups of
 //     a group hold bit-identical values).
 //  3. V pass. p = exp(s - LSE) is the normalized weight; a head keeps a
 //     position iff p >= threshold. Each wave ballots the union over the G
-//     heads for its 64 positions and fetches only those value rows; every
-//     other row is never read (the sparse-V rule of "Пропуск 90% работы по
-//     деквантизации…", tproger.ru, section "Решение — не ускорять, а
+//     heads for its 64 positions and only those value rows are fetched;
+//     every other row is never read (the sparse-V rule of "Пропуск 90% работы
+//     по деквантизации…", tproger.ru, section "Решение — не ускорять, а
 //     пропускать": skip V dequantization and accumulation when the attention
 //     weight is below the threshold; weights are known from K before any V
-//     work).
-//  4. Grid barrier, then a deterministic merge of the per-split partial
-//     outputs (fixed split order) into out.
+//     work). Splits with kept rows publish a partial output and a flag.
+//  4. Every workgroup of the group sums one slice of the group's output over
+//     the flagged splits in fixed split order (deterministic).
 //
-// All waits are bounded: a barrier that does not complete within ~0.5 s sets
-// a status bit and lets the kernel finish.
+// All waits are bounded: a wait that does not complete within ~0.5 s sets a
+// status bit and lets the kernel finish.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -43,12 +45,33 @@ __device__ inline void stamp(const GqaArgs& a, int k) {
   if (a.times && threadIdx.x == 0) a.times[int64_t(blockIdx.x) * 16 + k] = wall_clock64();
 }
 
-// Merge two (max, sum-of-exp2) pairs of the log2 domain; commutative bit for bit.
+// 2^x with the hardware instruction (results below the normal range flush
+// to 0; used for softmax statistics, where such terms are below rounding)
+__device__ inline float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Merge two (max, sum-of-exp2) pairs of the log2 domain.
 __device__ inline float2 lse_merge(float2 x, float2 y) {
   const float M = fmaxf(x.x, y.x);
-  if (M == -INFINITY) return make_float2(M, 0.f);
-  const float L = x.y * exp2f(x.x - M) + y.y * exp2f(y.x - M);
-  return make_float2(M, L);
+  const float Ms = M == -INFINITY ? 0.f : M;         // both empty: every term is 0
+  return make_float2(M, x.y * ex2(x.x - Ms) + y.y * ex2(y.x - Ms));
+}
+
+template <int CTRL>
+__device__ inline float dppf(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ inline float2 dpp2(float2 v) { return make_float2(dppf<CTRL>(v.x), dppf<CTRL>(v.y)); }
+
+// lse_merge over the 16 lanes of each row of the wave (quad neighbours, the
+// other pair of the quad, mirrored quads, mirrored half rows); lane 0 of the
+// row holds the merge of all 16.
+__device__ inline float2 merge_row16(float2 x) {
+  x = lse_merge(x, dpp2<0xB1>(x));                    // quad_perm [1,0,3,2]
+  x = lse_merge(x, dpp2<0x4E>(x));                    // quad_perm [2,3,0,1]
+  x = lse_merge(x, dpp2<0x141>(x));                   // row_half_mirror
+  x = lse_merge(x, dpp2<0x140>(x));                   // row_mirror
+  return x;
 }
 
 __device__ inline float bf16_to_f32(uint16_t u) { return __uint_as_float(uint32_t(u) << 16); }
@@ -99,12 +122,39 @@ __device__ inline float settle_f(u64 w, const u64* p, uint32_t epoch, WsHeader* 
   if (uint32_t(w >> 32) == epoch) return __uint_as_float(uint32_t(w));
   return get_tagged_f(p, epoch, h);
 }
+__device__ inline uint32_t settle_u(u64 w, const u64* p, uint32_t epoch, WsHeader* h) {
+  if (uint32_t(w >> 32) == epoch) return uint32_t(w);
+  return get_tagged(p, epoch, h);
+}
+
+// Bring every peeked word w[k] with use[k] set up to the current epoch,
+// re-reading all stale ones together (one round trip per retry rather than
+// one per word). Bounded like get_tagged.
+template <int N>
+__device__ inline void settle_all(u64 (&w)[N], const u64* const (&p)[N], const bool (&use)[N], uint32_t epoch,
+                                  WsHeader* h) {
+  uint32_t spins = 0;
+  while (true) {
+    bool stale = false;
+#pragma unroll
+    for (int k = 0; k < N; ++k) stale |= use[k] && uint32_t(w[k] >> 32) != epoch;
+    if (!stale) return;
+    __builtin_amdgcn_s_sleep(1);
+    if (++spins > kSpinLimit) {
+      __hip_atomic_fetch_or(&h->status, kStatusWaitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+      if (use[k] && uint32_t(w[k] >> 32) != epoch) w[k] = peek(p[k]);
+  }
+}
 
 // Online (max, sum of exp2) update with one more score; -inf scores are skipped.
 __device__ inline void online_add(float& m, float& l, float s) {
   if (s == -INFINITY) return;
-  if (s > m) { l = l * exp2f(m - s) + 1.f; m = s; }
-  else l += exp2f(s - m);
+  if (s > m) { l = l * ex2(m - s) + 1.f; m = s; }
+  else l += ex2(s - m);
 }
 
 // ---------------------------------------------------------------- format traits
@@ -281,18 +331,18 @@ template <> struct Traits<KVQ_LUT3> {
 };
 
 // ---------------------------------------------------------------- the kernel
-// Workgroup roles: every workgroup scores its split and runs its own V pass;
-// split 0 of each group (the "master") also merges the group's split
-// statistics into the LSE and, at the end, the partial outputs into out.
+// Workgroup roles: every workgroup scores its split, merges its group's LSE,
+// runs its own V pass and sums one slice of the group's output; split 0 of
+// each group also counts its group towards publishing the next epoch.
 template <int FMT, int G>
 __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   using T = Traits<FMT>;
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
   extern __shared__ __align__(16) unsigned char smem[];
   // LDS: scores [G][P] (then kept weights in place; then the cross-wave
-  // reduction; then the merge list), q operands, small per-head values.
+  // reduction; then the merge inputs), q operands, small per-head values.
   const int P = a.P;
-  const int sc_floats = (G * P > kWaves * G * 128) ? G * P : kWaves * G * 128;
+  const int sc_floats = gqa_sc_floats(G, P, a.S);
   float* sc = reinterpret_cast<float*>(smem);
   _Float16* qop = reinterpret_cast<_Float16*>(sc + sc_floats);     // [16 rows][4 blk][4 kk][8]
   float* cst = reinterpret_cast<float*>(qop + 16 * 128);          // [4 blk][16 rows]
@@ -314,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   const int wg = blockIdx.x;
   const int bg = wg / a.S;                  // b * Hkv + g
   const int split = wg - bg * a.S;
-  const bool master = split == 0;
+  const bool master = split == 0;                  // advances the epoch for its group
   const int b = bg / a.Hkv;
   const int g = bg - b * a.Hkv;
   const int pos0 = split * P;
@@ -345,6 +395,9 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     }
   };
   load_tiles(wave);
+  // keep these loads ahead of the q loads below (both latencies then overlap
+  // in the set-up's first barrier instead of following one another)
+  __asm__ volatile("" ::: "memory");
 
   // ---------------------------------------------------------------- setup
   if (wg == 0 && tid == 0) {
@@ -362,12 +415,16 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     if (j < G) {
       const int h = g * G + j;
       const int64_t qoff = (int64_t(b) * a.Hq + h) * 128 + ln * 4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qv[e] = a.q_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.q)[qoff + e])
-                         : reinterpret_cast<const float*>(a.q)[qoff + e];
-        m = fmaxf(m, fabsf(qv[e]));
+      if (a.q_bf16) {                                  // one 8-byte load
+        const uint2 r = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.q) + qoff);
+        qv[0] = __uint_as_float(r.x << 16); qv[1] = __uint_as_float(r.x & 0xFFFF0000u);
+        qv[2] = __uint_as_float(r.y << 16); qv[3] = __uint_as_float(r.y & 0xFFFF0000u);
+      } else {                                         // one 16-byte load
+        const float4 r = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.q) + qoff);
+        qv[0] = r.x; qv[1] = r.y; qv[2] = r.z; qv[3] = r.w;
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(qv[e]));
     }
     if (j < 8) {
 #pragma unroll
@@ -463,15 +520,8 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   }
   // split statistics: merge over the 16 lanes of a lane group, then over waves
   {
-    float2 x0 = make_float2(m0, l0), x1 = make_float2(m1, l1);
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) {
-      float2 y0, y1;
-      y0.x = __shfl_xor(x0.x, o, 16); y0.y = __shfl_xor(x0.y, o, 16);
-      y1.x = __shfl_xor(x1.x, o, 16); y1.y = __shfl_xor(x1.y, o, 16);
-      x0 = lse_merge(x0, y0);
-      x1 = lse_merge(x1, y1);
-    }
+    const float2 x0 = merge_row16(make_float2(m0, l0));
+    const float2 x1 = merge_row16(make_float2(m1, l1));
     if (n16 == 0) {
       wml[wave * 8 + j0] = x0;
       wml[wave * 8 + j1] = x1;
@@ -497,33 +547,33 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     const int j = tid >> 7, ln = tid & 127;
     if (j < G) {
       for (int s0 = ln; s0 < a.S; s0 += 4 * 128) {
-        u64 w[4][2];
+        u64 w[8];
+        const u64* src[8];
+        bool use[8];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int sp = s0 + 128 * u;
-          const u64* src = a.split_ml + ((int64_t(bg) * a.S + sp) * G + j) * 2;
-          w[u][0] = sp < a.S ? peek(src) : 0ull;
-          w[u][1] = sp < a.S ? peek(src + 1) : 0ull;
+          src[2 * u] = a.split_ml + ((int64_t(bg) * a.S + (sp < a.S ? sp : 0)) * G + j) * 2;
+          src[2 * u + 1] = src[2 * u] + 1;
+          use[2 * u] = use[2 * u + 1] = sp < a.S;
+          w[2 * u] = use[2 * u] ? peek(src[2 * u]) : 0ull;
+          w[2 * u + 1] = use[2 * u] ? peek(src[2 * u + 1]) : 0ull;
         }
+        settle_all(w, src, use, epoch, a.hdr);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int sp = s0 + 128 * u;
-          if (sp < a.S) {
-            const u64* src = a.split_ml + ((int64_t(bg) * a.S + sp) * G + j) * 2;
-            float2 v;
-            v.x = settle_f(w[u][0], src, epoch, a.hdr);
-            v.y = settle_f(w[u][1], src + 1, epoch, a.hdr);
-            acc = lse_merge(acc, v);
-          }
-        }
+        for (int u = 0; u < 4; ++u)
+          if (use[2 * u]) acc = lse_merge(acc, make_float2(__uint_as_float(uint32_t(w[2 * u])),
+                                                           __uint_as_float(uint32_t(w[2 * u + 1]))));
+      }
+      acc = merge_row16(acc);                        // lane 16r holds row r's merge
+      float2 row[3];                                 // rows 1..3, read before any merging
+#pragma unroll
+      for (int r = 1; r < 4; ++r) {
+        row[r - 1].x = __shfl(acc.x, 16 * r);
+        row[r - 1].y = __shfl(acc.y, 16 * r);
       }
 #pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        float2 oth;
-        oth.x = __shfl_xor(acc.x, o);
-        oth.y = __shfl_xor(acc.y, o);
-        acc = lse_merge(acc, oth);
-      }
+      for (int r = 0; r < 3; ++r) acc = lse_merge(acc, row[r]);
       if (lane == 0) wml[wave] = acc;                 // two waves per head
     }
     __syncthreads();
@@ -534,6 +584,17 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     __syncthreads();
   }
   stamp(a, 3);
+  // Every workgroup of this group has published its split statistics, so it
+  // has read the epoch; once every group is past this point the epoch of the
+  // next call can be published (no workgroup of this call reads it again).
+  if (master && tid == 0) {
+    const uint32_t ngroups = uint32_t(a.B * a.Hkv);
+    const uint32_t prev = __hip_atomic_fetch_add(&a.hdr->groups_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev == ngroups - 1) {
+      __hip_atomic_store(&a.hdr->groups_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.hdr->epoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 
   // ---------------------------------------------------------------- phase 3: sparse V pass
   // (a) per 64-position chunk: normalized weights, per-head keep bits, the
@@ -646,7 +707,10 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) { wg_rows += wrows[w]; wg_kept += wcount[w]; }
   const int64_t pbase = int64_t(bg) * a.S + split;
-  if (wg_rows > 0) {                                  // uniform across the workgroup
+  if (wg_rows == 0) {                                 // uniform: nothing kept, publish zeros
+    for (int i = tid; i < G * 128; i += kThreads) put_tagged_f(a.partial + pbase * G * 128 + i, epoch, 0.f);
+    if (tid < G) put_tagged_f(a.pmass + pbase * G + tid, epoch, 0.f);
+  } else {
     float* red = sc;                                 // [kWaves][G][128]
 #pragma unroll
     for (int j = 0; j < G; ++j) {
@@ -669,81 +733,86 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   if (tid == 0) put_tagged(a.flags + pbase, epoch, (uint32_t(wg_rows) << 18) | uint32_t(wg_kept));
   stamp(a, 4);
 
-  // ---------------------------------------------------------------- phase 4: merge (master)
-  // Sum the flagged partial outputs in ascending split order (deterministic)
-  // and write the group's statistics. The last group to finish advances the
-  // workspace epoch for the next call.
-  if (master) {
-    __syncthreads();
-    int* list = reinterpret_cast<int*>(sc);          // flagged splits, ascending
-    int* wcnt = misc;                                // [kWaves]
-    int* sk = reinterpret_cast<int*>(wml);           // per-wave kept/rows sums [kWaves][2]
-    int total = 0;
-    int kept_sum = 0, rows_sum = 0;
-    for (int s0 = 0; s0 < a.S; s0 += kThreads) {
-      const int s = s0 + tid;
-      uint32_t fv = 0;
-      if (s < a.S) fv = get_tagged(a.flags + int64_t(bg) * a.S + s, epoch, a.hdr);
-      const int rows = int(fv >> 18), kept = int(fv & 0x3FFFFu);
-      const bool f = rows > 0;
-      const unsigned long long bal = __ballot(f);
-      int kr = kept, rr = rows;
+  // ---------------------------------------------------------------- phase 4: merge
+  // Workgroup `split` of the group sums the slice [split*E, split*E + E) of
+  // the group's G*128 outputs over all splits (a split without kept rows
+  // published zeros) in ascending split order, which is deterministic, and
+  // the kept mass of heads split, split+S, ... ; split 0 also sums the
+  // group's counters. All words are read in one batch and stale ones are
+  // re-read together.
+  {
+    constexpr int NE = G * 128;
+    const int S = a.S;
+    const int E = (NE + S - 1) / S;
+    const int e0 = split * E;
+    const int ne = e0 < NE ? (NE - e0 < E ? NE - e0 : E) : 0;
+    const int nh = split < G ? (G - split + S - 1) / S : 0;
+    const int nf = master ? S : 0;
+    float* pv = sc;                                  // [ne][S]
+    float* pm = pv + ne * S;                         // [nh][S]
+    uint32_t* fl = reinterpret_cast<uint32_t*>(pm + nh * S);   // [S] (split 0)
+    const int64_t gb = int64_t(bg) * S;
+    __syncthreads();                                 // sc is free again
+    constexpr int NW = 3 + 2 + 2;                    // partial, mass and flag words per thread
+    u64 w[NW];
+    const u64* src[NW];
+    bool use[NW];
 #pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) { kr += __shfl_xor(kr, o); rr += __shfl_xor(rr, o); }
-      if (lane == 0) { wcnt[wave] = __popcll(bal); sk[2 * wave] = kr; sk[2 * wave + 1] = rr; }
-      __syncthreads();
-      int off = total;
-      for (int w = 0; w < wave; ++w) off += wcnt[w];
-      if (f) list[off + __popcll(bal & ((1ull << lane) - 1ull))] = s;
-      for (int w = 0; w < kWaves; ++w) { total += wcnt[w]; kept_sum += sk[2 * w]; rows_sum += sk[2 * w + 1]; }
-      __syncthreads();
+    for (int k = 0; k < 3; ++k) {
+      const int i = tid + k * kThreads;
+      use[k] = i < ne * S;
+      const int e = e0 + (use[k] ? i / S : 0), sp = use[k] ? i % S : 0;
+      src[k] = a.partial + (gb + sp) * NE + (use[k] ? e : 0);
     }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = tid + k * kThreads;
+      use[3 + k] = i < nh * S;
+      const int j = use[3 + k] ? split + (i / S) * S : 0, sp = use[3 + k] ? i % S : 0;
+      src[3 + k] = a.pmass + (gb + sp) * G + j;
+      use[5 + k] = i < nf;
+      src[5 + k] = a.flags + gb + (use[5 + k] ? i : 0);
+    }
+#pragma unroll
+    for (int k = 0; k < NW; ++k) w[k] = use[k] ? peek(src[k]) : 0ull;
+    settle_all(w, src, use, epoch, a.hdr);
     stamp(a, 5);
-    const int nflag = total;
-    for (int i = tid; i < G * 128; i += kThreads) {
-      if (i < G) {                                  // kept mass of head i
-        const u64* pm = a.pmass + int64_t(bg) * a.S * G + i;
-        float m = 0.f;
-        for (int k0 = 0; k0 < nflag; k0 += 16) {
-          u64 w[16];
 #pragma unroll
-          for (int u = 0; u < 16; ++u) w[u] = (k0 + u < nflag) ? peek(pm + int64_t(list[k0 + u]) * G) : 0ull;
+    for (int k = 0; k < 3; ++k)
+      if (use[k]) pv[tid + k * kThreads] = __uint_as_float(uint32_t(w[k]));
 #pragma unroll
-          for (int u = 0; u < 16; ++u)
-            if (k0 + u < nflag) m += settle_f(w[u], pm + int64_t(list[k0 + u]) * G, epoch, a.hdr);
-        }
-        a.kept_mass[int64_t(bg) * G + i] = m;
-      }
-      const u64* pp = a.partial + int64_t(bg) * a.S * (G * 128) + i;
-      float s = 0.f;
-      for (int k0 = 0; k0 < nflag; k0 += 16) {
-        u64 w[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) w[u] = (k0 + u < nflag) ? peek(pp + int64_t(list[k0 + u]) * (G * 128)) : 0ull;
-#pragma unroll
-        for (int u = 0; u < 16; ++u)
-          if (k0 + u < nflag) s += settle_f(w[u], pp + int64_t(list[k0 + u]) * (G * 128), epoch, a.hdr);
-      }
-      a.out[int64_t(bg) * (G * 128) + i] = s;
+    for (int k = 0; k < 2; ++k) {
+      if (use[3 + k]) pm[tid + k * kThreads] = __uint_as_float(uint32_t(w[3 + k]));
+      if (use[5 + k]) fl[tid + k * kThreads] = uint32_t(w[5 + k]);
     }
-    if (tid == 0) {
-      a.bgstat[2 * bg] = (unsigned long long)kept_sum;
-      a.bgstat[2 * bg + 1] = (unsigned long long)rows_sum;
-      const uint32_t ngroups = uint32_t(a.B * a.Hkv);
-      const uint32_t prev = __hip_atomic_fetch_add(&a.hdr->groups_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (prev == ngroups - 1) {
-        __hip_atomic_store(&a.hdr->groups_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&a.hdr->epoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (tid < ne) {
+      float s = 0.f;
+      for (int sp = 0; sp < S; ++sp) s += pv[tid * S + sp];
+      a.out[int64_t(bg) * NE + e0 + tid] = s;
+    }
+    if (tid >= kThreads - nh) {
+      const int hh = tid - (kThreads - nh);
+      float m = 0.f;
+      for (int sp = 0; sp < S; ++sp) m += pm[hh * S + sp];
+      a.kept_mass[int64_t(bg) * G + split + hh * S] = m;
+    }
+    if (master && tid == kThreads / 2) {
+      unsigned long long kept_sum = 0, rows_sum = 0;
+      for (int sp = 0; sp < S; ++sp) {
+        kept_sum += fl[sp] & 0x3FFFFu;
+        rows_sum += fl[sp] >> 18;
       }
+      a.bgstat[2 * bg] = kept_sum;
+      a.bgstat[2 * bg + 1] = rows_sum;
     }
     stamp(a, 6);
   }
 }
 
 // LDS bytes the kernel needs for P positions per split and group size G.
-size_t gqa_lds_bytes(int G, int P) {
-  size_t sc = size_t(G) * P > size_t(kWaves) * G * 128 ? size_t(G) * P : size_t(kWaves) * G * 128;
-  if (sc < size_t(kThreads)) sc = kThreads;        // the merge list reuses this region
+size_t gqa_lds_bytes(int G, int P, int S) {
+  const size_t sc = size_t(gqa_sc_floats(G, P, S));
   return sc * 4 + 16 * 128 * 2 + 64 * 4 + 3 * 8 * 4 + 2 * kWaves * 4 + size_t(kWaves) * G * 4 +
          size_t(kWaves) * 8 * 8 + (kWaves + 4) * 4 + size_t(P / kChunk) * 12 + size_t(P) * 2 + 64;
 }

@@ -16,8 +16,8 @@ constexpr uint32_t kStatusWaitTimeout = 1u;   // a bounded wait gave up
 // Workspace header. The first 256 bytes of every workspace; the rest holds the
 // per-split statistics and partial outputs of the last call.
 struct WsHeader {
-  uint32_t epoch;                       // tag of the last completed call (0 in a fresh workspace)
-  uint32_t groups_done;                 // merges finished in the running call (returns to 0)
+  uint32_t epoch;                       // tag of the last call (0 in a fresh workspace)
+  uint32_t groups_done;                 // groups past their LSE exchange in the running call (returns to 0)
   uint32_t status;                      // sticky device fault bits
   uint32_t pad0;
   unsigned long long reserved2;
@@ -132,7 +132,20 @@ inline MlaLayout mla_ws_layout(int B, int H, int S, int P) {
   return w;
 }
 
-constexpr int kStamps = 7;        // phase stamps per workgroup (5 and 6 only by a group's merging workgroup)
+constexpr int kStamps = 7;        // phase stamps per workgroup
+
+// Floats of the first LDS region of the grouped kernel: scores [G][P], the
+// cross-wave reduction [kWaves][G][128], and the merge's slice partials
+// [E][S] (E = ceil(G*128 / S)), kept-mass inputs [nh][S] (nh = heads a
+// workgroup sums: 1 if S >= G, else ceil(G / S)) and flags [S].
+inline __host__ __device__ int gqa_sc_floats(int G, int P, int S) {
+  int n = G * P;
+  if (kWaves * G * 128 > n) n = kWaves * G * 128;
+  const int E = (G * 128 + S - 1) / S;
+  const int nh = S >= G ? 1 : (G + S - 1) / S;
+  const int m = S * (1 + E + nh);
+  return m > n ? m : n;
+}
 constexpr int kMlaStamps = 5;     // latent path: start, scores start, scores end, lse known, lists published
 
 }  // namespace kvq

@@ -482,7 +482,7 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int e = 4 * i + j;
-          const float pe = ex2(s2[e] - lse[32 * wave + 8 * i + 4 * kh + j]);
+          const float pe = exp2f(s2[e] - lse[32 * wave + 8 * i + 4 * kh + j]);   // denormal-exact
           const bool keep = (s2[e] != -INFINITY) && pe >= a.tau;
           p[e] = keep ? pe : 0.f;
           bits |= keep ? 1u : 0u;
