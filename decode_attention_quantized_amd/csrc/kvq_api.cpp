@@ -14,7 +14,7 @@
 #include "kvq_internal.h"
 
 namespace kvq {
-size_t gqa_lds_bytes(int G, int P, int S);
+size_t gqa_lds_bytes(int fmt, int G, int P, int S);
 const void* gqa_kernel(int fmt, int G);
 size_t mla_lds_bytes(int H, int P, int S);
 const void* mla_scores_kernel(int H);
@@ -136,7 +136,7 @@ int32_t make_plan(int32_t fmt, const kvq_cache* k, const kvq_launch* l, int32_t 
   S = (ctx_len + P - 1) / P;                             // drop splits that would be empty
   if (P > 8192) return KVQ_ERR_UNSUPPORTED;              // per-split counts are packed in 14/18 bits
   if (S > 2048 || BG * S > (int64_t(1) << 30)) return KVQ_ERR_UNSUPPORTED;
-  const size_t lds = kvq::gqa_lds_bytes(G, P, S);
+  const size_t lds = kvq::gqa_lds_bytes(fmt, G, P, S);
   if (lds > size_t(di.max_lds)) return KVQ_ERR_UNSUPPORTED;
 
   plan->S = S;

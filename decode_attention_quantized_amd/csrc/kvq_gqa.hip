@@ -179,11 +179,28 @@ template <> struct Traits<KVQ_Q4_0> {
   __device__ static void locate(int d, int& bb, int& kk, int& slot) {
     bb = d >> 5; kk = (d >> 3) & 3; slot = 2 * (d & 3) + ((d >> 2) & 1);
   }
-  __device__ static Raw load(const uint8_t* crow, const uint8_t* srow, int kk) {
+  // Staged K load: lane group kg reads block kg of its row (16 contiguous
+  // bytes, so one instruction covers a whole 16-row tile); the wave then
+  // swaps the pieces through LDS so that lane group kk holds dword kk of
+  // every block (the layout of Raw).
+  static constexpr bool kStaged = true;
+  static constexpr int NV = 1;                    // 16-byte pieces per lane and row
+  static constexpr int PITCH = 80;                // staged row pitch in LDS (bytes)
+  struct Raw16 { uint4 v[NV]; uint2 s; };
+  __device__ static Raw16 load16(const uint8_t* crow, const uint8_t* srow, int kg) {
+    Raw16 r;
+    r.v[0] = *reinterpret_cast<const uint4*>(crow + 16 * kg);
+    r.s = *reinterpret_cast<const uint2*>(srow);
+    return r;
+  }
+  __device__ static void stage(uint8_t* lrow, const Raw16& r, int kg) {
+    *reinterpret_cast<uint4*>(lrow + 16 * kg) = r.v[0];
+  }
+  __device__ static Raw unstage(const uint8_t* lrow, int kk, uint2 s) {
     Raw r;
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb) r.c[bb] = *reinterpret_cast<const uint32_t*>(crow + 16 * bb + 4 * kk);
-    r.s = *reinterpret_cast<const uint2*>(srow);
+    for (int bb = 0; bb < 4; ++bb) r.c[bb] = *reinterpret_cast<const uint32_t*>(lrow + 16 * bb + 4 * kk);
+    r.s = s;
     return r;
   }
   // one dword = 8 nibbles -> fp16 (16 + c), vector order elements 0,4,1,5,2,6,3,7
@@ -224,11 +241,27 @@ template <> struct Traits<KVQ_Q8_0> {
   struct Raw { uint2 c[4]; uint2 s; };
   __device__ static int dim_of(int bb, int kk, int e) { return 32 * bb + 8 * kk + e; }
   __device__ static void locate(int d, int& bb, int& kk, int& slot) { bb = d >> 5; kk = (d >> 3) & 3; slot = d & 7; }
-  __device__ static Raw load(const uint8_t* crow, const uint8_t* srow, int kk) {
+  // staged K load (see the q4_0 traits): lane group kg reads block kg (32 bytes)
+  static constexpr bool kStaged = true;
+  static constexpr int NV = 2;
+  static constexpr int PITCH = 144;
+  struct Raw16 { uint4 v[NV]; uint2 s; };
+  __device__ static Raw16 load16(const uint8_t* crow, const uint8_t* srow, int kg) {
+    Raw16 r;
+    r.v[0] = *reinterpret_cast<const uint4*>(crow + 32 * kg);
+    r.v[1] = *reinterpret_cast<const uint4*>(crow + 32 * kg + 16);
+    r.s = *reinterpret_cast<const uint2*>(srow);
+    return r;
+  }
+  __device__ static void stage(uint8_t* lrow, const Raw16& r, int kg) {
+    *reinterpret_cast<uint4*>(lrow + 32 * kg) = r.v[0];
+    *reinterpret_cast<uint4*>(lrow + 32 * kg + 16) = r.v[1];
+  }
+  __device__ static Raw unstage(const uint8_t* lrow, int kk, uint2 s) {
     Raw r;
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb) r.c[bb] = *reinterpret_cast<const uint2*>(crow + 32 * bb + 8 * kk);
-    r.s = *reinterpret_cast<const uint2*>(srow);
+    for (int bb = 0; bb < 4; ++bb) r.c[bb] = *reinterpret_cast<const uint2*>(lrow + 32 * bb + 8 * kk);
+    r.s = s;
     return r;
   }
   __device__ static half8 deq(const Raw& r, int bb, uint32_t) {
@@ -279,6 +312,8 @@ __device__ inline uint32_t lut3_pair_entry(int lane) {
 template <> struct Traits<KVQ_LUT3> {
   static constexpr int CB = 48, SB = 2;
   static constexpr bool kRowScale = true;
+  static constexpr bool kStaged = false;          // lane group kk already reads 12 contiguous bytes
+  static constexpr int PITCH = 0;
   static constexpr float kBias = 0.0f;
   static constexpr float kRowMul = 0.08838834764831845f;   // 1/sqrt(128)
   struct Raw { uint32_t c[3]; uint32_t s; };
@@ -330,6 +365,9 @@ template <> struct Traits<KVQ_LUT3> {
   }
 };
 
+template <class T, bool kStaged> struct LoadedOf { using type = typename T::Raw; };
+template <class T> struct LoadedOf<T, true> { using type = typename T::Raw16; };
+
 // ---------------------------------------------------------------- the kernel
 // Workgroup roles: every workgroup scores its split, merges its group's LSE,
 // runs its own V pass and sums one slice of the group's output; split 0 of
@@ -354,9 +392,14 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   float* wmass = reinterpret_cast<float*>(wrows + kWaves);        // [kWaves][G]
   float2* wml = reinterpret_cast<float2*>(wmass + kWaves * G);    // [kWaves][8] per-wave (max, sum)
   int* misc = reinterpret_cast<int*>(wml + kWaves * 8);           // [kWaves + 4]
-  unsigned long long* umask = reinterpret_cast<unsigned long long*>(misc + kWaves + 4);  // [P/64]
-  int* coff = reinterpret_cast<int*>(umask + (P / kChunk));       // [P/64]
-  uint16_t* rowlist = reinterpret_cast<uint16_t*>(coff + (P / kChunk));   // [P] kept rows of the split
+  unsigned long long* umask = reinterpret_cast<unsigned long long*>(misc + kWaves + 4);  // [P/64] union keep bits
+  // per-wave lists of the kept rows a wave fetches: [kWaves][32 * ceil(P/64 / (kWaves/2))]
+  uint16_t* rowlist = reinterpret_cast<uint16_t*>(umask + (P / kChunk));
+  const int list_cap = 32 * ((P / kChunk + kWaves / 2 - 1) / (kWaves / 2));
+  // per-wave K staging strip [kWaves][16 rows][PITCH] (16-byte aligned; the
+  // offset is rounded, not the pointer, so accesses stay LDS instructions)
+  const int stg_off = (int(reinterpret_cast<unsigned char*>(rowlist + kWaves * list_cap) - smem) + 15) & ~15;
+  uint8_t* stg = smem + stg_off;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -380,7 +423,8 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   // issue the first K tiles before the q set-up so their latency overlaps it
   const int ntiles = P / 16;
   constexpr int U = 4;
-  typename T::Raw raw[U];
+  using Loaded = typename LoadedOf<T, T::kStaged>::type;
+  Loaded raw[U];
   auto load_tiles = [&](int t0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -388,10 +432,22 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
       const int r = pos0 + t * 16 + n16;
       if (t < ntiles && r < ctx) {
         const int64_t row = row0 + r;
-        raw[u] = T::load(a.kc + row * T::CB, a.ks + row * T::SB, kg);
+        if constexpr (T::kStaged) raw[u] = T::load16(a.kc + row * T::CB, a.ks + row * T::SB, kg);
+        else raw[u] = T::load(a.kc + row * T::CB, a.ks + row * T::SB, kg);
       } else {
-        raw[u] = typename T::Raw{};
+        raw[u] = Loaded{};
       }
+    }
+  };
+  // the operand layout of tile u (through this wave's LDS strip when staged;
+  // a wave's LDS accesses complete in order, so no barrier is needed)
+  uint8_t* lrow = stg + (wave * 16 + n16) * T::PITCH;
+  auto operands = [&](int u) -> typename T::Raw {
+    if constexpr (T::kStaged) {
+      T::stage(lrow, raw[u], kg);
+      return T::unstage(lrow, kg, raw[u].s);
+    } else {
+      return raw[u];
     }
   };
   load_tiles(wave);
@@ -407,6 +463,7 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     a.hdr->k_row_bytes = T::CB + T::SB;
     a.hdr->v_row_bytes = T::CB + T::SB;
   }
+  for (int c = tid; c < P / kChunk; c += kThreads) umask[c] = 0ull;
   // q of this group: per-head max |q| -> power-of-two prescale, then fp16 hi/lo rows
   float qv[4];
   {
@@ -493,17 +550,18 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
       const int t = t0 + u * kWaves;
       if (t >= ntiles) break;                   // uniform across the wave
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      const typename T::Raw ru = operands(u);
       if constexpr (T::kRowScale) {
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[bb], T::deq(raw[u], bb, table), acc, 0, 0, 0);
-        const float s = T::scale(raw[u], 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[bb], T::deq(ru, bb, table), acc, 0, 0, 0);
+        const float s = T::scale(ru, 0);
         acc[0] *= s; acc[1] *= s; acc[2] *= s; acc[3] *= s;
       } else {
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
-          const floatx4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[bb], T::deq(raw[u], bb, table), C0[bb], 0, 0, 0);
-          const float s = T::scale(raw[u], bb);
+          const floatx4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[bb], T::deq(ru, bb, table), C0[bb], 0, 0, 0);
+          const float s = T::scale(ru, bb);
           acc[0] = fmaf(s, d[0], acc[0]);
           acc[1] = fmaf(s, d[1], acc[1]);
           acc[2] = fmaf(s, d[2], acc[2]);
@@ -529,12 +587,15 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   }
   __syncthreads();
   stamp(a, 2);
-  if (tid < G) {
-    float2 acc = make_float2(-INFINITY, 0.f);
-    for (int w = 0; w < kWaves; ++w) acc = lse_merge(acc, wml[w * 8 + tid]);
-    u64* dst = a.split_ml + ((int64_t(bg) * a.S + split) * G + tid) * 2;
-    put_tagged_f(dst, epoch, acc.x);
-    put_tagged_f(dst + 1, epoch, acc.y);
+  if (tid < 128) {                                   // row j of 16 lanes merges head j over the 16 waves
+    const int j = tid >> 4, w = tid & 15;
+    float2 acc = (j < G) ? wml[w * 8 + j] : make_float2(-INFINITY, 0.f);
+    acc = merge_row16(acc);
+    if (w == 0 && j < G) {
+      u64* dst = a.split_ml + ((int64_t(bg) * a.S + split) * G + j) * 2;
+      put_tagged_f(dst, epoch, acc.x);
+      put_tagged_f(dst + 1, epoch, acc.y);
+    }
   }
   __syncthreads();                                   // wml is reused below
 
@@ -597,80 +658,73 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   }
 
   // ---------------------------------------------------------------- phase 3: sparse V pass
-  // (a) per 64-position chunk: normalized weights, per-head keep bits, the
-  //     union over the group's heads (a value row is fetched iff some head
-  //     keeps it); (b) the kept rows of all chunks are pooled in LDS and
-  //     spread over all waves; (c) each wave fetches only its kept rows.
+  // Waves 2c' and 2c'+1 share the 64-position chunks c = c' (mod kWaves/2).
+  // (a) Each computes the normalized weights and keep bits of half of the
+  //     group's heads and ORs the union (a value row is fetched iff some
+  //     head keeps it) into umask[c].
+  // (b) After one barrier each takes the kept rows of its chunks of even
+  //     (first wave of the pair) or odd (second) rank and fetches only those.
+  constexpr int HALF = G > 1 ? G / 2 : 1;
+  const int pair = wave >> 1, side = wave & 1;
+  const int jb = G > 1 ? side * HALF : 0;
+  const bool do_p = G > 1 || side == 0;
   float o0[G], o1[G], mass[G];
 #pragma unroll
   for (int j = 0; j < G; ++j) { o0[j] = 0.f; o1[j] = 0.f; mass[j] = 0.f; }
   int kept_cnt = 0;
-  float lsej[G];
+  float lsej[HALF];
 #pragma unroll
-  for (int j = 0; j < G; ++j) lsej[j] = lse[j];
+  for (int jj = 0; jj < HALF; ++jj) lsej[jj] = lse[jb + jj];
   const int nchunks = P / kChunk;
-  for (int c = wave; c < nchunks; c += kWaves) {
-    const int lp = c * kChunk + lane;
-    const int r = pos0 + lp;
-    const bool valid = r < ctx;
-    bool any = false;
+  if (do_p) {
+    for (int c = pair; c < nchunks; c += kWaves / 2) {
+      const int lp = c * kChunk + lane;
+      const bool valid = pos0 + lp < ctx;
+      bool any = false;
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const float p = valid ? exp2f(sc[j * P + lp] - lsej[j]) : 0.f;
-      const bool keep = valid && (p >= tau);
-      const float pk = keep ? p : 0.f;
-      sc[j * P + lp] = pk;                     // kept weight replaces the score in place
-      mass[j] += pk;
-      any |= keep;
-      const unsigned long long bal = __ballot(keep);
-      kept_cnt += __popcll(bal);
-      if (a.mask_out && lane < 2) {
-        const int word = (pos0 + c * kChunk) / 32 + lane;
-        if (word < a.mask_words) {
-          const int h = g * G + j;
-          a.mask_out[(int64_t(b) * a.Hq + h) * a.mask_words + word] = uint32_t(bal >> (32 * lane));
+      for (int jj = 0; jj < HALF; ++jj) {
+        const int j = jb + jj;
+        const float p = valid ? exp2f(sc[j * P + lp] - lsej[jj]) : 0.f;
+        const bool keep = valid && (p >= tau);
+        sc[j * P + lp] = keep ? p : 0.f;          // kept weight replaces the score in place
+        any |= keep;
+        const unsigned long long bal = __ballot(keep);
+        kept_cnt += __popcll(bal);
+        if (a.mask_out && lane < 2) {
+          const int word = (pos0 + c * kChunk) / 32 + lane;
+          if (word < a.mask_words) {
+            const int h = g * G + j;
+            a.mask_out[(int64_t(b) * a.Hq + h) * a.mask_words + word] = uint32_t(bal >> (32 * lane));
+          }
         }
       }
+      const unsigned long long um = __ballot(any);
+      if (lane == 0 && um) atomicOr(&umask[c], um);
     }
-    const unsigned long long um = __ballot(any);
-    if (lane == 0) umask[c] = um;
   }
+  stamp(a, 7);
   __syncthreads();
-  if (tid < 64) {                                    // exclusive scan of kept rows per chunk
-    const int c0 = 2 * tid, c1 = 2 * tid + 1;
-    const int n0 = c0 < nchunks ? __popcll(umask[c0]) : 0;
-    const int n1 = c1 < nchunks ? __popcll(umask[c1]) : 0;
-    int incl = n0 + n1;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
-    const int excl = incl - n0 - n1;
-    if (c0 < nchunks) coff[c0] = excl;
-    if (c1 < nchunks) coff[c1] = excl + n0;
-    if (tid == 63) misc[kWaves + 3] = incl;
-  }
-  __syncthreads();
-  const int nrows = misc[kWaves + 3];
-  for (int c = wave; c < nchunks; c += kWaves) {
+  uint16_t* mylist = rowlist + wave * list_cap;
+  int nmine = 0, rows_cnt = 0;
+  for (int c = pair; c < nchunks; c += kWaves / 2) {
     const unsigned long long um = umask[c];
-    if ((um >> lane) & 1ull) rowlist[coff[c] + __popcll(um & ((1ull << lane) - 1ull))] = uint16_t(c * kChunk + lane);
+    const int n = __popcll(um);
+    if (side == 0) rows_cnt += n;
+    const int rank = __popcll(um & ((1ull << lane) - 1ull));
+    if (((um >> lane) & 1ull) && (rank & 1) == side) mylist[nmine + (rank >> 1)] = uint16_t(c * kChunk + lane);
+    nmine += (n + 1 - side) >> 1;
   }
-  __syncthreads();
+  stamp(a, 8);
   {
-    // rows [k0, k1) of the pooled list go to this wave; 16 rows of loads are
-    // in flight at once
-    const int per = (nrows + kWaves - 1) / kWaves;
-    const int k0 = wave * per;
-    const int k1 = (k0 + per < nrows) ? k0 + per : nrows;
+    // this wave's rows, 16 rows of loads in flight at once (the list was
+    // written by this wave, and its LDS accesses complete in order)
     constexpr int VB = 16;
-    for (int k = k0; k < k1; k += VB) {
+    for (int k = 0; k < nmine; k += VB) {
       typename T::VRaw vr[VB];
 #pragma unroll
       for (int u = 0; u < VB; ++u) {
-        if (k + u < k1) {
-          const int64_t row = row0 + pos0 + rowlist[k + u];
+        if (k + u < nmine) {
+          const int64_t row = row0 + pos0 + mylist[k + u];
           vr[u] = T::vload(a.vc + row * T::CB, a.vs + row * T::SB, lane);
         } else {
           vr[u] = typename T::VRaw{};
@@ -678,29 +732,29 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
       }
 #pragma unroll
       for (int u = 0; u < VB; ++u) {
-        if (k + u >= k1) break;
+        if (k + u >= nmine) break;
         float v0, v1;
         T::vdeq(vr[u], table, v0, v1);
-        const int pr = rowlist[k + u];
+        const int pr = mylist[k + u];
 #pragma unroll
         for (int j = 0; j < G; ++j) {
-          const float pj = sc[j * P + pr];
+          const float pj = sc[j * P + pr];        // same for every lane of the wave
           o0[j] = fmaf(pj, v0, o0[j]);
           o1[j] = fmaf(pj, v1, o1[j]);
+          mass[j] += pj;
         }
       }
     }
   }
-  const int rows_cnt = (tid == 0) ? nrows : 0;
+  stamp(a, 9);
 
-  // per-wave counters and kept mass
-  if (lane == 0) { wcount[wave] = kept_cnt; wrows[wave] = rows_cnt; }
+  // per-wave counters and kept mass (mass is wave-uniform: summed over the
+  // wave's rows in row order)
+  if (lane == 0) {
+    wcount[wave] = kept_cnt;
+    wrows[wave] = rows_cnt;
 #pragma unroll
-  for (int j = 0; j < G; ++j) {
-    float m = mass[j];
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m += __shfl_xor(m, o);
-    if (lane == 0) wmass[wave * G + j] = m;
+    for (int j = 0; j < G; ++j) wmass[wave * G + j] = mass[j];
   }
   __syncthreads();                                   // all waves done with sc
   int wg_rows = 0, wg_kept = 0;
@@ -811,10 +865,13 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
 }
 
 // LDS bytes the kernel needs for P positions per split and group size G.
-size_t gqa_lds_bytes(int G, int P, int S) {
+size_t gqa_lds_bytes(int fmt, int G, int P, int S) {
   const size_t sc = size_t(gqa_sc_floats(G, P, S));
+  const size_t list_cap = 32 * ((P / kChunk + kWaves / 2 - 1) / (kWaves / 2));
+  const size_t pitch = fmt == KVQ_Q4_0 ? Traits<KVQ_Q4_0>::PITCH : fmt == KVQ_Q8_0 ? Traits<KVQ_Q8_0>::PITCH : 0;
   return sc * 4 + 16 * 128 * 2 + 64 * 4 + 3 * 8 * 4 + 2 * kWaves * 4 + size_t(kWaves) * G * 4 +
-         size_t(kWaves) * 8 * 8 + (kWaves + 4) * 4 + size_t(P / kChunk) * 12 + size_t(P) * 2 + 64;
+         size_t(kWaves) * 8 * 8 + (kWaves + 4) * 4 + size_t(P / kChunk) * 8 + size_t(kWaves) * list_cap * 2 + 16 +
+         size_t(kWaves) * 16 * pitch + 64;
 }
 
 const void* gqa_kernel(int fmt, int G) {

@@ -132,7 +132,7 @@ inline MlaLayout mla_ws_layout(int B, int H, int S, int P) {
   return w;
 }
 
-constexpr int kStamps = 7;        // phase stamps per workgroup
+constexpr int kStamps = 10;       // phase stamps per workgroup (7..9 split the V pass)
 
 // Floats of the first LDS region of the grouped kernel: scores [G][P], the
 // cross-wave reduction [kWaves][G][128], and the merge's slice partials
@@ -144,7 +144,8 @@ inline __host__ __device__ int gqa_sc_floats(int G, int P, int S) {
   const int E = (G * 128 + S - 1) / S;
   const int nh = S >= G ? 1 : (G + S - 1) / S;
   const int m = S * (1 + E + nh);
-  return m > n ? m : n;
+  if (m > n) n = m;
+  return (n + 3) & ~3;                  // keeps the regions after it 16-byte aligned
 }
 constexpr int kMlaStamps = 5;     // latent path: start, scores start, scores end, lse known, lists published
 
