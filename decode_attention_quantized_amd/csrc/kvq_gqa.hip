@@ -63,6 +63,17 @@ __device__ inline float dppf(float v) {
 template <int CTRL>
 __device__ inline float2 dpp2(float2 v) { return make_float2(dppf<CTRL>(v.x), dppf<CTRL>(v.y)); }
 
+// Sum over the 64 lanes of the wave in a fixed tree (rows with DPP, then the
+// four row results); lane 0 holds the total.
+__device__ inline float sum_wave(float v) {
+  v += dppf<0xB1>(v);                                 // quad_perm [1,0,3,2]
+  v += dppf<0x4E>(v);                                 // quad_perm [2,3,0,1]
+  v += dppf<0x141>(v);                                // row_half_mirror
+  v += dppf<0x140>(v);                                // row_mirror
+  const float r1 = __shfl(v, 16), r2 = __shfl(v, 32), r3 = __shfl(v, 48);
+  return (v + r1) + (r2 + r3);
+}
+
 // lse_merge over the 16 lanes of each row of the wave (quad neighbours, the
 // other pair of the quad, mirrored quads, mirrored half rows); lane 0 of the
 // row holds the merge of all 16.
@@ -371,7 +382,8 @@ template <class T> struct LoadedOf<T, true> { using type = typename T::Raw16; };
 // ---------------------------------------------------------------- the kernel
 // Workgroup roles: every workgroup scores its split, merges its group's LSE,
 // runs its own V pass and sums one slice of the group's output; split 0 of
-// each group also counts its group towards publishing the next epoch.
+// each group also counts its group towards publishing the next epoch (once
+// past the LSE exchange every workgroup of the group has read the epoch).
 template <int FMT, int G>
 __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   using T = Traits<FMT>;
@@ -391,8 +403,8 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   int* wrows = wcount + kWaves;                                   // [kWaves] rows fetched
   float* wmass = reinterpret_cast<float*>(wrows + kWaves);        // [kWaves][G]
   float2* wml = reinterpret_cast<float2*>(wmass + kWaves * G);    // [kWaves][8] per-wave (max, sum)
-  int* misc = reinterpret_cast<int*>(wml + kWaves * 8);           // [kWaves + 4]
-  unsigned long long* umask = reinterpret_cast<unsigned long long*>(misc + kWaves + 4);  // [P/64] union keep bits
+  int* wproc = reinterpret_cast<int*>(wml + kWaves * 8);          // [kWaves + 4] value rows each wave summed
+  unsigned long long* umask = reinterpret_cast<unsigned long long*>(wproc + kWaves + 4);  // [P/64] union keep bits
   // per-wave lists of the kept rows a wave fetches: [kWaves][32 * ceil(P/64 / (kWaves/2))]
   uint16_t* rowlist = reinterpret_cast<uint16_t*>(umask + (P / kChunk));
   const int list_cap = 32 * ((P / kChunk + kWaves / 2 - 1) / (kWaves / 2));
@@ -645,17 +657,6 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     __syncthreads();
   }
   stamp(a, 3);
-  // Every workgroup of this group has published its split statistics, so it
-  // has read the epoch; once every group is past this point the epoch of the
-  // next call can be published (no workgroup of this call reads it again).
-  if (master && tid == 0) {
-    const uint32_t ngroups = uint32_t(a.B * a.Hkv);
-    const uint32_t prev = __hip_atomic_fetch_add(&a.hdr->groups_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (prev == ngroups - 1) {
-      __hip_atomic_store(&a.hdr->groups_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&a.hdr->epoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
 
   // ---------------------------------------------------------------- phase 3: sparse V pass
   // Waves 2c' and 2c'+1 share the 64-position chunks c = c' (mod kWaves/2).
@@ -753,34 +754,46 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   if (lane == 0) {
     wcount[wave] = kept_cnt;
     wrows[wave] = rows_cnt;
+    wproc[wave] = nmine;
 #pragma unroll
     for (int j = 0; j < G; ++j) wmass[wave * G + j] = mass[j];
   }
   __syncthreads();                                   // all waves done with sc
-  int wg_rows = 0, wg_kept = 0;
+  int wg_rows = 0, wg_kept = 0, nact = 0;
+  uint32_t act = 0;                                  // waves that summed value rows
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) { wg_rows += wrows[w]; wg_kept += wcount[w]; }
+  for (int w = 0; w < kWaves; ++w) {
+    wg_rows += wrows[w];
+    wg_kept += wcount[w];
+    if (wproc[w] > 0) act |= 1u << w;
+  }
+  nact = __popc(act);
   const int64_t pbase = int64_t(bg) * a.S + split;
-  if (wg_rows == 0) {                                 // uniform: nothing kept, publish zeros
+  if (nact == 0) {                                    // uniform: nothing kept, publish zeros
     for (int i = tid; i < G * 128; i += kThreads) put_tagged_f(a.partial + pbase * G * 128 + i, epoch, 0.f);
     if (tid < G) put_tagged_f(a.pmass + pbase * G + tid, epoch, 0.f);
   } else {
-    float* red = sc;                                 // [kWaves][G][128]
+    // the partials of the waves that summed rows meet in LDS and are added in
+    // ascending wave order; every thread publishes one word
+    float* red = sc;                                 // [nact][G][128]
+    if ((act >> wave) & 1u) {
+      const int slot = __popc(act & ((1u << wave) - 1u));
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      red[(wave * G + j) * 128 + 2 * lane] = o0[j];
-      red[(wave * G + j) * 128 + 2 * lane + 1] = o1[j];
+      for (int j = 0; j < G; ++j) {
+        red[(slot * G + j) * 128 + 2 * lane] = o0[j];
+        red[(slot * G + j) * 128 + 2 * lane + 1] = o1[j];
+      }
     }
     __syncthreads();
     for (int i = tid; i < G * 128; i += kThreads) {
       float s = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) s += red[w * G * 128 + i];
+      for (int k = 0; k < nact; ++k) s += red[k * G * 128 + i];
       put_tagged_f(a.partial + pbase * G * 128 + i, epoch, s);
     }
     if (tid < G) {
       float s = 0.f;
-      for (int w = 0; w < kWaves; ++w) s += wmass[w * G + tid];
+      for (int w = 0; w < kWaves; ++w)
+        if ((act >> w) & 1u) s += wmass[w * G + tid];
       put_tagged_f(a.pmass + pbase * G + tid, epoch, s);
     }
   }
@@ -829,7 +842,17 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     }
 #pragma unroll
     for (int k = 0; k < NW; ++k) w[k] = use[k] ? peek(src[k]) : 0ull;
+    // Every workgroup of this group is past its LSE exchange, so each has
+    // read the epoch; the last group to get here publishes the next call's
+    // epoch. The counter's round trip overlaps the merge loads.
+    uint32_t prev = 0;
+    const bool counts = master && tid == 0;
+    if (counts) prev = __hip_atomic_fetch_add(&a.hdr->groups_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     settle_all(w, src, use, epoch, a.hdr);
+    if (counts && prev == uint32_t(a.B * a.Hkv) - 1) {
+      __hip_atomic_store(&a.hdr->groups_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.hdr->epoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     stamp(a, 5);
 #pragma unroll
     for (int k = 0; k < 3; ++k)
@@ -840,25 +863,33 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
       if (use[5 + k]) fl[tid + k * kThreads] = uint32_t(w[5 + k]);
     }
     __syncthreads();
-    if (tid < ne) {
-      float s = 0.f;
-      for (int sp = 0; sp < S; ++sp) s += pv[tid * S + sp];
-      a.out[int64_t(bg) * NE + e0 + tid] = s;
+    // one wave per sum: lane l adds splits l, l+64, ... in order, then a
+    // fixed tree over the lanes (deterministic)
+    for (int job = wave; job < ne + nh; job += kWaves) {
+      const float* src = job < ne ? pv + job * S : pm + (job - ne) * S;
+      float v = 0.f;
+      for (int sp = lane; sp < S; sp += 64) v += src[sp];
+      v = sum_wave(v);
+      if (lane == 0) {
+        if (job < ne) a.out[int64_t(bg) * NE + e0 + job] = v;
+        else a.kept_mass[int64_t(bg) * G + split + (job - ne) * S] = v;
+      }
     }
-    if (tid >= kThreads - nh) {
-      const int hh = tid - (kThreads - nh);
-      float m = 0.f;
-      for (int sp = 0; sp < S; ++sp) m += pm[hh * S + sp];
-      a.kept_mass[int64_t(bg) * G + split + hh * S] = m;
-    }
-    if (master && tid == kThreads / 2) {
+    if (master && wave == kWaves - 1) {
       unsigned long long kept_sum = 0, rows_sum = 0;
-      for (int sp = 0; sp < S; ++sp) {
+      for (int sp = lane; sp < S; sp += 64) {
         kept_sum += fl[sp] & 0x3FFFFu;
         rows_sum += fl[sp] >> 18;
       }
-      a.bgstat[2 * bg] = kept_sum;
-      a.bgstat[2 * bg + 1] = rows_sum;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        kept_sum += __shfl_xor(kept_sum, o);
+        rows_sum += __shfl_xor(rows_sum, o);
+      }
+      if (lane == 0) {
+        a.bgstat[2 * bg] = kept_sum;
+        a.bgstat[2 * bg + 1] = rows_sum;
+      }
     }
     stamp(a, 6);
   }
