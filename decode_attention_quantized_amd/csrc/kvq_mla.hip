@@ -523,75 +523,181 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
 }
 
 // ----------------------------------------------------------------------------- out
-// One workgroup per (sequence, 32 heads, 128 value dims): thread t owns head
-// 32*hb + t/8 and dims 128*db + 16*(t%8) .. +15.
+// One workgroup per (sequence, 32 heads, 128-dim value group g): the output
+// block out[h][d] = sum over the sequence's kept rows r of p[h][r] * v[r][d],
+// a contraction over rows on v_mfma_f32_32x32x16_bf16 (M = heads, N = dims,
+// K = rows; wave w owns dims 32w..32w+31 of the group). Exact operands: v is
+// the e4m3 code converted to bf16 (exact) and the row's fp32 group scale
+// goes to the weight side, p * scale (one fp32 rounding) split into three
+// bf16 terms that add up to it exactly (8 + 8 + 8 significant bits); each
+// term is a separate MFMA into the same fp32 accumulator. Rows are taken in
+// split order and, within a split, in position order, 64 at a time; both
+// operands are staged transposed in LDS (rows contiguous per head / dim).
+constexpr int OUT_CHUNK = 64;                   // rows per LDS stage (4 MFMA k-steps)
+constexpr int OUT_PITCH = OUT_CHUNK + 8;        // bf16 per staged head / dim line (bank spread)
+constexpr int OUT_MAX_S = 1024;                 // splits per sequence the prefix table holds
+
+__device__ inline uint16_t bf16_bits_rne(float x) {  // exact-to-nearest-even fp32 -> bf16
+  const uint32_t u = __float_as_uint(x);
+  return uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+__device__ inline float bf16_value(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
 __global__ __launch_bounds__(256) void mla_out(MlaArgs a) {
+  __shared__ __align__(16) uint16_t vt[128 * OUT_PITCH];            // [dim][row] bf16 values
+  __shared__ __align__(16) uint16_t pt[3 * 32 * OUT_PITCH];         // [term][head][row] bf16 weight terms
+  __shared__ int pre[OUT_MAX_S + 1];                                // exclusive prefix of kept rows per split
+  __shared__ float mpart[256][8];                                   // kept-mass partials [thread][head slot]
+  __shared__ long long cnt[4];
+
   const int H = a.Hq;
-  const int nhb = H / 32, ndb = DV / 128;
-  const int b = blockIdx.x / (nhb * ndb);
-  const int rem = blockIdx.x - b * nhb * ndb;
-  const int hb = rem / ndb, db = rem - hb * ndb;
-  const int tid = threadIdx.x;
-  const int h = 32 * hb + (tid >> 3);
-  const int d0 = 128 * db + 16 * (tid & 7);
+  const int nhb = H / 32;
+  const int b = blockIdx.x / (nhb * 4);
+  const int rem = blockIdx.x - b * nhb * 4;
+  const int hb = rem >> 2, g = rem & 3;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int S = a.S;
   const int64_t row0 = int64_t(b) * a.cap;
   const uint32_t epoch_next =
       __hip_atomic_load(&a.hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-  float o[16];
+
+  // kept rows per split: one batch of loads, then an exclusive prefix sum
+  long long pairs_part = 0;
+  {
+    int c[OUT_MAX_S / 256];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) o[e] = 0.f;
-  float mass = 0.f;
-  int rows = 0;
-  long long pairs = 0;
-  for (int sp = 0; sp < a.S; ++sp) {
-    const int64_t kbase = int64_t(b) * a.S + sp;
-    const int n = a.kcount[kbase];
-    rows += n;
-    pairs += a.kpairs[kbase];
-    for (int k0 = 0; k0 < n; k0 += 8) {
-      int pos[8];
-      float p[8];
-      uint4 v[8];
-      float s[8];
+    for (int k = 0; k < OUT_MAX_S / 256; ++k) {
+      const int sp = tid * (OUT_MAX_S / 256) + k;
+      c[k] = sp < S ? a.kcount[int64_t(b) * S + sp] : 0;
+      if (sp < S) pairs_part += a.kpairs[int64_t(b) * S + sp];
+    }
+    int local = 0;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const bool in = k0 + u < n;
-        pos[u] = in ? a.kpos[kbase * a.P + k0 + u] : 0;
-        p[u] = in ? a.kp[(kbase * a.P + k0 + u) * H + h] : 0.f;
+    for (int k = 0; k < OUT_MAX_S / 256; ++k) local += c[k];
+    // block-wide exclusive scan of the per-thread sums (wave scan, then waves)
+    int incl = local;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) pre[OUT_MAX_S - 4 + wave] = incl;   // wave totals parked at the table's end
+    __syncthreads();
+    int wbase = 0;
+    for (int w = 0; w < wave; ++w) wbase += pre[OUT_MAX_S - 4 + w];
+    const int total = pre[OUT_MAX_S - 4] + pre[OUT_MAX_S - 3] + pre[OUT_MAX_S - 2] + pre[OUT_MAX_S - 1];
+    __syncthreads();
+    int run = wbase + incl - local;
+#pragma unroll
+    for (int k = 0; k < OUT_MAX_S / 256; ++k) {
+      pre[tid * (OUT_MAX_S / 256) + k] = run;
+      run += c[k];
+    }
+    if (tid == 0) pre[OUT_MAX_S] = total;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) pairs_part += __shfl_xor(pairs_part, o);
+    if (lane == 0) cnt[wave] = pairs_part;
+    __syncthreads();
+  }
+  const int N = pre[OUT_MAX_S];
+
+  floatx16 acc = {};
+  float mass[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) mass[j] = 0.f;
+  const int col = lane & 31, kh = lane >> 5;
+  // staging roles: row r = tid / 4 of the chunk, quarter q = tid % 4
+  const int sr = tid >> 2, sq = tid & 3;
+  for (int c0 = 0; c0 < N; c0 += OUT_CHUNK) {
+    const int r = c0 + sr;
+    uint4 v0 = make_uint4(0u, 0u, 0u, 0u), v1 = v0;
+    float pw[8], sc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pw[j] = 0.f;
+    if (r < N) {
+      // split of global row r: the last split whose prefix is <= r (binary search)
+      int lo = 0, hi = S - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pre[mid] <= r) lo = mid; else hi = mid - 1;
       }
+      const int64_t kb = int64_t(b) * S + lo;
+      const int64_t idx = kb * a.P + (r - pre[lo]);
+      const int pos = a.kpos[idx];
+      const uint8_t* vrow = a.kc + (row0 + pos) * D + 128 * g + 32 * sq;
+      v0 = *reinterpret_cast<const uint4*>(vrow);
+      v1 = *reinterpret_cast<const uint4*>(vrow + 16);
+      sc = reinterpret_cast<const float*>(a.ks + (row0 + pos) * (4 * NGROUPS))[g];
+      const float4 p0 = *reinterpret_cast<const float4*>(a.kp + idx * H + 32 * hb + 8 * sq);
+      const float4 p1 = *reinterpret_cast<const float4*>(a.kp + idx * H + 32 * hb + 8 * sq + 4);
+      pw[0] = p0.x; pw[1] = p0.y; pw[2] = p0.z; pw[3] = p0.w;
+      pw[4] = p1.x; pw[5] = p1.y; pw[6] = p1.z; pw[7] = p1.w;
+    }
+    // values: 32 dims of row sr -> bf16, transposed into vt[dim][row]
+    {
+      const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const bool in = k0 + u < n;
-        v[u] = in ? *reinterpret_cast<const uint4*>(a.kc + (row0 + pos[u]) * D + d0) : make_uint4(0u, 0u, 0u, 0u);
-        s[u] = in ? reinterpret_cast<const float*>(a.ks + (row0 + pos[u]) * (4 * NGROUPS))[db] : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (k0 + u >= n) break;
-        mass += p[u];
-        const float ps = p[u] * s[u];
-        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const half2v lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[q], 1.0f, false);
-          const half2v hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[q], 1.0f, true);
-          o[4 * q + 0] = fmaf(ps, float(lo[0]), o[4 * q + 0]);
-          o[4 * q + 1] = fmaf(ps, float(lo[1]), o[4 * q + 1]);
-          o[4 * q + 2] = fmaf(ps, float(hi[0]), o[4 * q + 2]);
-          o[4 * q + 3] = fmaf(ps, float(hi[1]), o[4 * q + 3]);
-        }
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t lo2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[k], 1.0f, false));
+        const uint32_t hi2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[k], 1.0f, true));
+        const int d = 32 * sq + 4 * k;
+        vt[(d + 0) * OUT_PITCH + sr] = uint16_t(lo2);
+        vt[(d + 1) * OUT_PITCH + sr] = uint16_t(lo2 >> 16);
+        vt[(d + 2) * OUT_PITCH + sr] = uint16_t(hi2);
+        vt[(d + 3) * OUT_PITCH + sr] = uint16_t(hi2 >> 16);
       }
     }
-  }
-  float* dst = a.out + (int64_t(b) * H + h) * DV + d0;
+    // weights: p * scale as three bf16 terms, transposed into pt[term][head][row]
 #pragma unroll
-  for (int e = 0; e < 16; e += 4) *reinterpret_cast<float4*>(dst + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
-  if (db == 0 && (tid & 7) == 0) a.kept_mass[int64_t(b) * H + h] = mass;
-  if (hb == 0 && db == 0 && tid == 0) {
-    a.bgstat[2 * b] = (unsigned long long)pairs;
-    a.bgstat[2 * b + 1] = (unsigned long long)rows;
+    for (int j = 0; j < 8; ++j) {
+      mass[j] += pw[j];
+      const float x = pw[j] * sc;
+      const uint16_t t0 = bf16_bits_rne(x);
+      const float r1 = x - bf16_value(t0);
+      const uint16_t t1 = bf16_bits_rne(r1);
+      const uint16_t t2 = bf16_bits_rne(r1 - bf16_value(t1));
+      const int h = 8 * sq + j;
+      pt[(0 * 32 + h) * OUT_PITCH + sr] = t0;
+      pt[(1 * 32 + h) * OUT_PITCH + sr] = t1;
+      pt[(2 * 32 + h) * OUT_PITCH + sr] = t2;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < OUT_CHUNK / 16; ++ks) {
+      const int k0 = 16 * ks + 8 * kh;
+      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&vt[(32 * wave + col) * OUT_PITCH + k0]);
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&pt[(t * 32 + col) * OUT_PITCH + k0]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+      }
+    }
+    __syncthreads();                                 // the next chunk reuses vt / pt
   }
-  // the last sequence's output workgroup advances the epoch for the next call
+  // accumulator 4i+j of the lane: head 8i + 4kh + j, dim 32*wave + col of the group
+  float* ob = a.out + (int64_t(b) * H + 32 * hb) * DV + 128 * g + 32 * wave + col;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ob[int64_t(8 * i + 4 * kh + j) * DV] = acc[4 * i + j];
+  if (g == 0) {
+    // kept mass of the 32 heads: thread t summed the rows t/4 (mod 64) of
+    // heads 8*(t%4)..+7; the 64 threads of a head are added in thread order
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mpart[tid][j] = mass[j];
+    __syncthreads();
+    if (tid < 32) {
+      const int q = tid >> 3, j = tid & 7;
+      float m = 0.f;
+      for (int t = q; t < 256; t += 4) m += mpart[t][j];
+      a.kept_mass[int64_t(b) * H + 32 * hb + 8 * q + j] = m;
+    }
+  }
+  if (hb == 0 && g == 0 && tid == 0) {
+    a.bgstat[2 * b] = (unsigned long long)(cnt[0] + cnt[1] + cnt[2] + cnt[3]);
+    a.bgstat[2 * b + 1] = (unsigned long long)N;
+  }
+  // the last workgroup advances the epoch for the next call
   __syncthreads();
   if (tid == 0) {
     const uint32_t prev = __hip_atomic_fetch_add(&a.hdr->groups_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
