@@ -128,6 +128,63 @@ def cpu_baseline(inp, budget_s=12.0):
                        f"{w.q_heads}/{w.kv_heads} heads), fp64 numpy, packing excluded, {el:.1f} s"), ref, (kc, ks)
 
 
+def run_config(w, steps, warmup, splits=0):
+    """Graph-timed sparse (w.threshold) and dense (threshold 0) calls of one
+    workload; returns one JSON-ready dict. Caches rotate over copies larger
+    than twice the 256 MB Infinity Cache."""
+    import torch
+    import decode_attention_quantized_amd as kvq
+    import synth
+    from decode_attention_quantized_amd.runtime import DecodeAttention, PackedCache
+
+    inp = synth.generate(w)
+    latent = inp.v is None
+    kc, ks = kvq.kvq_pack(w.fmt, inp.k)
+    cb, sb = kvq.kvq_row_bytes(w.fmt, w.dim)
+    row = cb + sb
+    if latent:
+        vrow = w.v_dim + 4 * (w.v_dim // 128)                 # value part of a latent row
+        set_bytes = w.batch * w.ctx * row
+    else:
+        vc, vs = kvq.kvq_pack(w.fmt, inp.v)
+        vrow = row
+        set_bytes = 2 * w.batch * w.kv_heads * w.ctx * row
+    R = max(2, math.ceil(ROTATION_BYTES / set_bytes))
+    K0 = PackedCache.from_host(kc, ks, w.fmt, w.dim)
+    V0 = None if latent else PackedCache.from_host(vc, vs, w.fmt, w.dim)
+    caches = [(K0, V0)] + [(K0.clone(), None if latent else V0.clone()) for _ in range(R - 1)]
+    q = torch.from_numpy(inp.q).cuda()
+    if w.q_bf16:
+        q = q.to(torch.bfloat16)
+    out = torch.empty((w.batch, w.q_heads, w.v_dim), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.Stream()
+    att = DecodeAttention(K0, V0, w.q_heads, ctx_len=w.ctx, softmax_scale=w.sigma, splits=splits, stream=stream,
+                          q_dtype=kvq.KVQ_Q_BF16 if w.q_bf16 else kvq.KVQ_Q_F32,
+                          v_dim=w.v_dim if latent else 0)
+    res = {m: time_mode(att, q, caches, w.ctx, tau, steps, warmup, out, stream)
+           for m, tau in (("sparse", w.threshold), ("dense", 0.0))}
+    qo = w.batch * w.q_heads * (w.dim * q.element_size() + w.v_dim * 4)
+    k_bytes = (w.batch * w.ctx if latent else w.batch * w.kv_heads * w.ctx) * row
+    line = {"workload": w.name, "fmt": str(w.fmt), "batch": w.batch,
+            "q_heads": w.q_heads, "kv_heads": w.kv_heads, "dim": w.dim, "ctx": w.ctx,
+            "rotation_sets": R, "splits": res["sparse"]["stats"]["splits"]}
+    for m, r in res.items():
+        st = r["stats"]
+        ab = k_bytes + st["rows_fetched"] * vrow + qo
+        d = {"tokens_per_s": round(w.batch / r["wall"], 1), "kernel_us_mean": round(r["kernel_mean"] * 1e6, 3),
+             "algorithmic_bytes": ab, "achieved_gbs": round(ab / r["kernel_mean"] / 1e9, 1),
+             "frac_hbm": round(ab / r["kernel_mean"] / 1e9 / HBM_PEAK_GBS, 4),
+             "rows_fetched": st["rows_fetched"], "kept_pairs": st["kept_pairs"],
+             "skip_fraction": round(1 - st["rows_fetched"] / max(1, st["positions"]), 6)}
+        if latent:
+            flops = 2 * w.q_heads * w.dim * w.ctx * w.batch + 2 * w.q_heads * w.v_dim * st["rows_fetched"]
+            d["mfma_tflops"] = round(flops / r["kernel_mean"] / 1e12, 2)
+            d["frac_mfma_bf16"] = round(flops / r["kernel_mean"] / 1e12 / 2500.0, 4)
+        line[m] = d
+    line["speedup_sparse_vs_dense"] = round(res["dense"]["wall"] / res["sparse"]["wall"], 3)
+    return line
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -139,6 +196,9 @@ def main():
                     help="which threshold(s) to time (a profiler run can restrict to one)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy 5 times (reference for HBM byte counters)")
+    ap.add_argument("--workload", choices=["long", "tiny", "sweep", "lut3", "mla", "stress"], default="long",
+                    help="long (default) prints the metric line; the others print one line per "
+                         "configuration (sweep: one per context length)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU; multi-GPU sharding is not implemented "
@@ -161,6 +221,12 @@ def main():
     import decode_attention_quantized_amd as kvq
     import synth
     from decode_attention_quantized_amd.runtime import DecodeAttention, PackedCache
+
+    if args.workload != "long":
+        names = [f"sweep_{n}" for n in synth.SWEEP] if args.workload == "sweep" else [args.workload]
+        for nm in names:
+            print(json.dumps(run_config(synth.workload(nm), args.steps, args.warmup, args.splits)), flush=True)
+        return
 
     w = synth.workload("long")
     inp = synth.generate(w)
