@@ -324,7 +324,7 @@ template <> struct Traits<KVQ_LUT3> {
   static constexpr int CB = 48, SB = 2;
   static constexpr bool kRowScale = true;
   static constexpr bool kStaged = false;          // lane group kk already reads 12 contiguous bytes
-  static constexpr int PITCH = 0;
+  static constexpr int PITCH = 64;                // staged row pitch in LDS (value rows only)
   static constexpr float kBias = 0.0f;
   static constexpr float kRowMul = 0.08838834764831845f;   // 1/sqrt(128)
   struct Raw { uint32_t c[3]; uint32_t s; };
@@ -436,8 +436,11 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   const int ntiles = P / 16;
   constexpr int U = 4;
   using Loaded = typename LoadedOf<T, T::kStaged>::type;
-  Loaded raw[U];
-  auto load_tiles = [&](int t0) {
+  // a wave's batches of U tiles are double-buffered (the next batch is
+  // requested before the current one is scored) when two fit in registers
+  constexpr bool kDouble = sizeof(Loaded) <= 24;
+  Loaded rawA[U], rawB[kDouble ? U : 1];
+  auto load_tiles = [&](Loaded* raw, int t0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = t0 + u * kWaves;
@@ -451,18 +454,18 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
       }
     }
   };
-  // the operand layout of tile u (through this wave's LDS strip when staged;
-  // a wave's LDS accesses complete in order, so no barrier is needed)
+  // the operand layout of a loaded tile (through this wave's LDS strip when
+  // staged; a wave's LDS accesses complete in order, so no barrier is needed)
   uint8_t* lrow = stg + (wave * 16 + n16) * T::PITCH;
-  auto operands = [&](int u) -> typename T::Raw {
+  auto operands = [&](const Loaded& rl) -> typename T::Raw {
     if constexpr (T::kStaged) {
-      T::stage(lrow, raw[u], kg);
-      return T::unstage(lrow, kg, raw[u].s);
+      T::stage(lrow, rl, kg);
+      return T::unstage(lrow, kg, rl.s);
     } else {
-      return raw[u];
+      return rl;
     }
   };
-  load_tiles(wave);
+  load_tiles(rawA, wave);
   // keep these loads ahead of the q loads below (both latencies then overlap
   // in the set-up's first barrier instead of following one another)
   __asm__ volatile("" ::: "memory");
@@ -555,14 +558,13 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   // ---------------------------------------------------------------- phase 1: scores
   // Scores go to LDS; each lane keeps an online (max, sum exp2) of its two heads.
   float m0 = -INFINITY, l0 = 0.f, m1 = -INFINITY, l1 = 0.f;
-  for (int t0 = wave; t0 < ntiles; t0 += kWaves * U) {
-    if (t0 != wave) load_tiles(t0);
+  auto score_batch = [&](const Loaded* raw, int t0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = t0 + u * kWaves;
       if (t >= ntiles) break;                   // uniform across the wave
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-      const typename T::Raw ru = operands(u);
+      const typename T::Raw ru = operands(raw[u]);
       if constexpr (T::kRowScale) {
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb)
@@ -586,6 +588,21 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
       const float s1 = valid ? (acc[2] + acc[3]) * hs1 : -INFINITY;
       if (j0 < G) { sc[j0 * P + lp] = s0; online_add(m0, l0, s0); }
       if (j1 < G) { sc[j1 * P + lp] = s1; online_add(m1, l1, s1); }
+    }
+  };
+  constexpr int STRIDE = kWaves * U;                  // tiles between a wave's batches
+  if constexpr (kDouble) {
+    for (int t0 = wave; t0 < ntiles; t0 += 2 * STRIDE) {
+      if (t0 + STRIDE < ntiles) load_tiles(rawB, t0 + STRIDE);
+      score_batch(rawA, t0);
+      if (t0 + STRIDE >= ntiles) break;
+      if (t0 + 2 * STRIDE < ntiles) load_tiles(rawA, t0 + 2 * STRIDE);
+      score_batch(rawB, t0 + STRIDE);
+    }
+  } else {
+    for (int t0 = wave; t0 < ntiles; t0 += STRIDE) {
+      if (t0 != wave) load_tiles(rawA, t0);
+      score_batch(rawA, t0);
     }
   }
   // split statistics: merge over the 16 lanes of a lane group, then over waves
@@ -669,6 +686,7 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   const int pair = wave >> 1, side = wave & 1;
   const int jb = G > 1 ? side * HALF : 0;
   const bool do_p = G > 1 || side == 0;
+  const bool tau_normal = tau >= 1.17549435e-38f;    // FLT_MIN
   float o0[G], o1[G], mass[G];
 #pragma unroll
   for (int j = 0; j < G; ++j) { o0[j] = 0.f; o1[j] = 0.f; mass[j] = 0.f; }
@@ -685,7 +703,10 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
 #pragma unroll
       for (int jj = 0; jj < HALF; ++jj) {
         const int j = jb + jj;
-        const float p = valid ? exp2f(sc[j * P + lp] - lsej[jj]) : 0.f;
+        // the hardware exp flushes results below 2^-126; any normal threshold
+        // decides above that, so it gives the same keep bits and weights
+        const float x = sc[j * P + lp] - lsej[jj];
+        const float p = valid ? (tau_normal ? ex2(x) : exp2f(x)) : 0.f;
         const bool keep = valid && (p >= tau);
         sc[j * P + lp] = keep ? p : 0.f;          // kept weight replaces the score in place
         any |= keep;
@@ -717,25 +738,51 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   }
   stamp(a, 8);
   {
-    // this wave's rows, 16 rows of loads in flight at once (the list was
-    // written by this wave, and its LDS accesses complete in order)
+    // this wave's rows in batches of 16: the rows are read with 16-byte loads
+    // (one or two instructions per batch) into this wave's LDS strip, then
+    // each lane takes its two dims from there (the list and the strip are
+    // written and read by this wave only, and its LDS accesses complete in
+    // order)
     constexpr int VB = 16;
+    constexpr int NL = T::CB / 16;                  // 16-byte pieces per row
+    constexpr int NI = (VB * NL + 63) / 64;         // load instructions per batch
+    uint8_t* vst = stg + wave * 16 * T::PITCH;
     for (int k = 0; k < nmine; k += VB) {
-      typename T::VRaw vr[VB];
+      uint4 cv[NI];
+      int rr[NI], ch[NI];
+      bool ok[NI];
 #pragma unroll
-      for (int u = 0; u < VB; ++u) {
-        if (k + u < nmine) {
-          const int64_t row = row0 + pos0 + mylist[k + u];
-          vr[u] = T::vload(a.vc + row * T::CB, a.vs + row * T::SB, lane);
-        } else {
-          vr[u] = typename T::VRaw{};
+      for (int i = 0; i < NI; ++i) {
+        const int piece = 64 * i + lane;
+        rr[i] = piece / NL;
+        ch[i] = piece - rr[i] * NL;
+        ok[i] = piece < VB * NL && k + rr[i] < nmine;
+        if (ok[i]) {
+          const int64_t row = row0 + pos0 + mylist[k + rr[i]];
+          cv[i] = *reinterpret_cast<const uint4*>(a.vc + row * T::CB + 16 * ch[i]);
         }
+      }
+      const bool sok = lane < VB && k + lane < nmine;
+      uint2 sv = make_uint2(0u, 0u);
+      if (sok) {
+        const int64_t row = row0 + pos0 + mylist[k + lane];
+        if constexpr (T::SB == 8) sv = *reinterpret_cast<const uint2*>(a.vs + row * 8);
+        else sv.x = *reinterpret_cast<const uint16_t*>(a.vs + row * T::SB);
+      }
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        if (ok[i]) *reinterpret_cast<uint4*>(vst + rr[i] * T::PITCH + 16 * ch[i]) = cv[i];
+      if (sok) {
+        if constexpr (T::SB == 8) *reinterpret_cast<uint2*>(vst + lane * T::PITCH + T::CB) = sv;
+        else *reinterpret_cast<uint16_t*>(vst + lane * T::PITCH + T::CB) = uint16_t(sv.x);
       }
 #pragma unroll
       for (int u = 0; u < VB; ++u) {
         if (k + u >= nmine) break;
+        const uint8_t* lr = vst + u * T::PITCH;
+        const typename T::VRaw vr = T::vload(lr, lr + T::CB, lane);
         float v0, v1;
-        T::vdeq(vr[u], table, v0, v1);
+        T::vdeq(vr, table, v0, v1);
         const int pr = mylist[k + u];
 #pragma unroll
         for (int j = 0; j < G; ++j) {
@@ -865,14 +912,24 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     __syncthreads();
     // one wave per sum: lane l adds splits l, l+64, ... in order, then a
     // fixed tree over the lanes (deterministic)
-    for (int job = wave; job < ne + nh; job += kWaves) {
-      const float* src = job < ne ? pv + job * S : pm + (job - ne) * S;
-      float v = 0.f;
-      for (int sp = lane; sp < S; sp += 64) v += src[sp];
-      v = sum_wave(v);
-      if (lane == 0) {
+    if (S <= 16) {                                   // few splits: one thread per sum, in split order
+      for (int job = tid; job < ne + nh; job += kThreads) {
+        const float* src = job < ne ? pv + job * S : pm + (job - ne) * S;
+        float v = 0.f;
+        for (int sp = 0; sp < S; ++sp) v += src[sp];
         if (job < ne) a.out[int64_t(bg) * NE + e0 + job] = v;
         else a.kept_mass[int64_t(bg) * G + split + (job - ne) * S] = v;
+      }
+    } else {
+      for (int job = wave; job < ne + nh; job += kWaves) {
+        const float* src = job < ne ? pv + job * S : pm + (job - ne) * S;
+        float v = 0.f;
+        for (int sp = lane; sp < S; sp += 64) v += src[sp];
+        v = sum_wave(v);
+        if (lane == 0) {
+          if (job < ne) a.out[int64_t(bg) * NE + e0 + job] = v;
+          else a.kept_mass[int64_t(bg) * G + split + (job - ne) * S] = v;
+        }
       }
     }
     if (master && wave == kWaves - 1) {
@@ -899,7 +956,9 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
 size_t gqa_lds_bytes(int fmt, int G, int P, int S) {
   const size_t sc = size_t(gqa_sc_floats(G, P, S));
   const size_t list_cap = 32 * ((P / kChunk + kWaves / 2 - 1) / (kWaves / 2));
-  const size_t pitch = fmt == KVQ_Q4_0 ? Traits<KVQ_Q4_0>::PITCH : fmt == KVQ_Q8_0 ? Traits<KVQ_Q8_0>::PITCH : 0;
+  const size_t pitch = fmt == KVQ_Q4_0 ? Traits<KVQ_Q4_0>::PITCH
+                     : fmt == KVQ_Q8_0 ? Traits<KVQ_Q8_0>::PITCH
+                                       : Traits<KVQ_LUT3>::PITCH;
   return sc * 4 + 16 * 128 * 2 + 64 * 4 + 3 * 8 * 4 + 2 * kWaves * 4 + size_t(kWaves) * G * 4 +
          size_t(kWaves) * 8 * 8 + (kWaves + 4) * 4 + size_t(P / kChunk) * 8 + size_t(kWaves) * list_cap * 2 + 16 +
          size_t(kWaves) * 16 * pitch + 64;
