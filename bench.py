@@ -54,6 +54,45 @@ def load_traffic(mode: str):
     return None if m is None else m.get("bytes_per_launch")
 
 
+def write_traffic(base: str) -> dict:
+    """Turn six rocprofv3 --pmc runs under `base` (fs/ws: FETCH_SIZE and
+    WRITE_SIZE at threshold 1e-6, fd/wd: the same at threshold 0, cf/cw: the
+    plain device copy of --copy-calibration) into calibrated HBM bytes per
+    launch of the grouped kernel, stamped with the kernel source hash."""
+    import csv
+    import glob
+
+    def per_dispatch(sub, name):
+        (path,) = glob.glob(os.path.join(base, sub, "*counter_collection.csv"))
+        vals = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if name in r["Kernel_Name"]:
+                    vals.setdefault(r["Dispatch_Id"], 0.0)
+                    vals[r["Dispatch_Id"]] += float(r["Counter_Value"])
+        if not vals:
+            raise SystemExit(f"no {name} dispatches in {path}")
+        return len(vals), sum(vals.values()) / len(vals)
+
+    n = 512 << 20
+    _, cf = per_dispatch("cf", "copyBuffer")
+    _, cw = per_dispatch("cw", "copyBuffer")
+    ff, wf = n / 1024 / cf, n / 1024 / cw
+    t = {"kernel": "kvq::gqa_fused<q4_0, G=8>",
+         "workload": "long-ctx q4_0: batch 1, 32/4 heads, dim 128, ctx 32768",
+         "kernel_sha256_16": kernel_hash(),
+         "calibration": {"copy_bytes_each_way": n, "copy_FETCH_SIZE_KiB": cf, "copy_WRITE_SIZE_KiB": cw,
+                         "fetch_factor": ff, "write_factor": wf}}
+    for mode, fs, ws in (("sparse", "fs", "ws"), ("dense", "fd", "wd")):
+        nd, fk = per_dispatch(fs, "gqa_fused")
+        _, wk = per_dispatch(ws, "gqa_fused")
+        t[mode] = {"FETCH_SIZE_KiB": fk, "WRITE_SIZE_KiB": wk, "dispatches": nd,
+                   "bytes_per_launch": int(round((fk * ff + wk * wf) * 1024))}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(t, f, indent=1)
+    return t
+
+
 def time_mode(att, q, caches, ctx, tau, steps, warmup, out, stream):
     """Time `steps` calls. The timed region replays the steps captured in one
     HIP graph (no host launch cost between calls), bracketed by device
@@ -199,7 +238,13 @@ def main():
     ap.add_argument("--workload", choices=["long", "tiny", "sweep", "lut3", "mla", "stress"], default="long",
                     help="long (default) prints the metric line; the others print one line per "
                          "configuration (sweep: one per context length)")
+    ap.add_argument("--write-traffic", metavar="DIR",
+                    help="no GPU work: summarize rocprofv3 counter runs under DIR (fs ws fd wd cf cw) "
+                         "into the committed traffic file")
     args = ap.parse_args()
+    if args.write_traffic:
+        print(json.dumps(write_traffic(args.write_traffic)), flush=True)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU; multi-GPU sharding is not implemented "
               "(see DESIGN.md for how the path would shard).", file=sys.stderr)
