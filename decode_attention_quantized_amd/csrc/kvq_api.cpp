@@ -95,7 +95,7 @@ int32_t make_mla_plan(const kvq_cache* k, const kvq_launch* l, int32_t ctx_len, 
   plan->Dv = 512;
   plan->lds = lds;
   plan->nwg = k->batch * S;
-  plan->threads = 2 * H;
+  plan->threads = 4 * H;                                 // two waves per 32-head block
   plan->mws = kvq::mla_ws_layout(k->batch, H, S, P);
   plan->total = plan->mws.total;
   return KVQ_OK;

@@ -9,14 +9,17 @@
 // every head are never read.
 //
 // Two launches on the caller's stream:
-//  mla_scores  (one workgroup per (sequence, split); wave w owns heads
-//              32w..32w+31 with q resident in registers as bf16 MFMA operands)
+//  mla_scores  (one workgroup per (sequence, split); two waves per 32-head
+//              block, each holding the bf16 query of its block for one half
+//              of the latent (288 dims) in registers as MFMA operands, so two
+//              waves share every SIMD)
 //    1. streams 32-row latent tiles into a 4-deep LDS ring with direct
-//       global->LDS loads (three tiles in flight), scores them with
-//       v_mfma_f32_32x32x16_bf16 (fp8 -> bf16 with the hardware converter,
-//       exact), applies the per-group fp32 scale to the fp32 accumulators,
-//       keeps per-head (max, sum exp2) and a per-(head, 64-position tile)
-//       maximum;
+//       global->LDS loads (three tiles in flight); each wave scores its half
+//       with v_mfma_f32_32x32x16_bf16 (fp8 -> bf16 with the hardware
+//       converter, exact), applies the per-group fp32 scales to the fp32
+//       accumulators and hands the rows the other wave finishes over through
+//       LDS; the finished scores feed per-head (max, sum exp2) and a
+//       per-(head, 64-position tile) maximum, one tile behind the MFMAs;
 //    2. the group's split statistics are merged into per-head log-sum-exps
 //       (head h by split h mod S) and exchanged as epoch-tagged words;
 //    3. re-scores only the 64-position tiles whose maximum can reach the
@@ -44,7 +47,8 @@ typedef unsigned long long u64;
 
 constexpr int D = 576;          // latent width (scores)
 constexpr int DV = 512;         // value width
-constexpr int KSTEPS = D / 16;  // 36 MFMA k-steps of 16 dims
+constexpr int HPAIRS = 9;       // MFMA step pairs (32 dims each) per latent half
+constexpr int HSTEPS = 2 * HPAIRS;  // MFMA k-steps of 16 dims per latent half
 constexpr int NGROUPS = 5;      // scale groups: 4 x 128 + 1 x 64
 constexpr int ROW_LDS = 592;    // LDS pitch of a staged latent row: 37 x 16 bytes (odd), so the 16-byte
                                 // reads of 8 consecutive rows hit distinct bank groups
@@ -94,38 +98,44 @@ template <int CTRL>
 __device__ inline float dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
-// lane j <- lane j ^ 16 within each half of the wave (swizzle, bit-mask mode)
-__device__ inline float swz16(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+// The values of lanes j and j ^ 16 (rows 0 and 1, 2 and 3 of the wave):
+// permlane16 swap of v with itself gives row 0 in rows 0 and 1 and row 1 in
+// the second result (likewise rows 2 and 3).
+__device__ inline float2 rows16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v),
+                                                  false, false);
+  return make_float2(__builtin_bit_cast(float, unsigned(r[0])), __builtin_bit_cast(float, unsigned(r[1])));
 }
 
-// Reduce 16 independent values over the 32 lanes of each wave half (max or
-// sum), every lane getting the result. Steps: neighbour in quad, other pair
-// in quad, mirrored quad in the 8-lane half row, mirrored half row, other row.
-template <bool MAX>
-__device__ inline void reduce32x16(float (&v)[16]) {
+// Reduce N independent values over the 32 lanes of each wave half (max or
+// sum), every lane getting the same bits. Steps: neighbour in quad, other
+// pair in quad, mirrored quad in the 8-lane half row, mirrored half row, then
+// the two rows combined in one order for both.
+template <bool MAX, int N>
+__device__ inline void reduce32(float (&v)[N]) {
   auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
-  float t[16];
+  float t[N];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) t[e] = dpp<0xB1>(v[e]);     // quad_perm [1,0,3,2]
+  for (int e = 0; e < N; ++e) t[e] = dpp<0xB1>(v[e]);     // quad_perm [1,0,3,2]
 #pragma unroll
-  for (int e = 0; e < 16; ++e) v[e] = op(v[e], t[e]);
+  for (int e = 0; e < N; ++e) v[e] = op(v[e], t[e]);
 #pragma unroll
-  for (int e = 0; e < 16; ++e) t[e] = dpp<0x4E>(v[e]);     // quad_perm [2,3,0,1]
+  for (int e = 0; e < N; ++e) t[e] = dpp<0x4E>(v[e]);     // quad_perm [2,3,0,1]
 #pragma unroll
-  for (int e = 0; e < 16; ++e) v[e] = op(v[e], t[e]);
+  for (int e = 0; e < N; ++e) v[e] = op(v[e], t[e]);
 #pragma unroll
-  for (int e = 0; e < 16; ++e) t[e] = dpp<0x141>(v[e]);    // row_half_mirror
+  for (int e = 0; e < N; ++e) t[e] = dpp<0x141>(v[e]);    // row_half_mirror
 #pragma unroll
-  for (int e = 0; e < 16; ++e) v[e] = op(v[e], t[e]);
+  for (int e = 0; e < N; ++e) v[e] = op(v[e], t[e]);
 #pragma unroll
-  for (int e = 0; e < 16; ++e) t[e] = dpp<0x140>(v[e]);    // row_mirror
+  for (int e = 0; e < N; ++e) t[e] = dpp<0x140>(v[e]);    // row_mirror
 #pragma unroll
-  for (int e = 0; e < 16; ++e) v[e] = op(v[e], t[e]);
+  for (int e = 0; e < N; ++e) v[e] = op(v[e], t[e]);
 #pragma unroll
-  for (int e = 0; e < 16; ++e) t[e] = swz16(v[e]);
-#pragma unroll
-  for (int e = 0; e < 16; ++e) v[e] = op(v[e], t[e]);
+  for (int e = 0; e < N; ++e) {
+    const float2 r = rows16(v[e]);
+    v[e] = op(r.x, r.y);
+  }
 }
 
 // 8 fp8 e4m3 bytes -> 8 bf16 (exact: every e4m3 value, subnormals included,
@@ -158,19 +168,33 @@ __device__ inline void wait_tiles(int k, int wave) {
   }
 }
 
-// Barrier between the waves of the workgroup without a memory fence (a fence
-// would wait for every load in flight, including the tiles being prefetched);
-// the empty asm keeps the compiler from moving memory accesses across it.
-__device__ inline void bar_nofence() {
-  __builtin_amdgcn_s_barrier();
-  __asm__ volatile("" ::: "memory");
-}
-
+// Where this lane's direct loads of a tile come from: the sequence's code and
+// scale planes, and per wave instruction i (instruction j = wave + NW * i of
+// the tile) the row within the tile (or, for a scale instruction, the float
+// within the tile's scales) and the byte offset within the row.
+template <int NW>
 struct TileSrc {
-  const uint8_t* kc;
+  static constexpr int NI = (NDMA + NW - 1) / NW;
+  const uint8_t* kc;                  // row 0 of the sequence
   const float* ks;
-  int64_t row0;
   int ctx;
+  int r[NI];
+  int c[NI];
+  __device__ TileSrc(const uint8_t* kc_, const float* ks_, int ctx_, int wave, int lane) : kc(kc_), ks(ks_), ctx(ctx_) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int j = wave + NW * i;
+      if (j < NCHUNK_I) {
+        const int sl = 64 * j + lane;
+        const int rr = sl / PITCH16;
+        r[i] = min(rr, TILE - 1);
+        c[i] = 16 * min(sl - rr * PITCH16, D / 16 - 1);
+      } else {
+        r[i] = min(64 * (j - NCHUNK_I) + lane, TILE * NGROUPS - 1);
+        c[i] = 0;
+      }
+    }
+  }
 };
 
 // Issue this wave's direct loads of the tile starting at position `first`
@@ -178,109 +202,151 @@ struct TileSrc {
 // chunk of row ctx-1, so every instruction runs with all lanes and the
 // per-wave instruction count is the same for every tile.
 template <int NW>
-__device__ __attribute__((always_inline)) inline void issue_tile(uint8_t* __restrict__ dst, const TileSrc& src,
-                                                                 int first, int wave, int lane) {
-  for (int j = wave; j < NDMA; j += NW) {
+__device__ __attribute__((always_inline)) inline void issue_tile(uint8_t* __restrict__ dst, const TileSrc<NW>& src,
+                                                                 int first, int wave) {
+#pragma unroll
+  for (int i = 0; i < TileSrc<NW>::NI; ++i) {
+    const int j = wave + NW * i;
     if (j < NCHUNK_I) {
-      const int sl = 64 * j + lane;
-      int r = sl / PITCH16, c = sl - r * PITCH16;
-      r = min(r, TILE - 1);
-      c = min(c, D / 16 - 1);
-      const int pos = min(first + r, src.ctx - 1);
-      __builtin_amdgcn_global_load_lds(src.kc + (src.row0 + pos) * D + c * 16, dst + j * 1024, 16, 0, 0);
-    } else {
-      const int i = 64 * (j - NCHUNK_I) + lane;
-      int64_t gi = (src.row0 + first) * NGROUPS + min(i, TILE * NGROUPS - 1);
-      gi = min(gi, (src.row0 + src.ctx) * NGROUPS - 1);
-      __builtin_amdgcn_global_load_lds(src.ks + gi, dst + SC_OFF + (j - NCHUNK_I) * 256, 4, 0, 0);
+      const int pos = min(first + src.r[i], src.ctx - 1);
+      const uint8_t* g = src.kc + int64_t(pos) * D + src.c[i];
+      __builtin_amdgcn_global_load_lds(g, dst + j * 1024, 16, 0, 0);
+    } else if (j < NDMA) {
+      const int gi = min(first * NGROUPS + src.r[i], src.ctx * NGROUPS - 1);
+      const float* g = src.ks + gi;
+      __builtin_amdgcn_global_load_lds(g, dst + SC_OFF + (j - NCHUNK_I) * 256, 4, 0, 0);
     }
   }
 }
 
-// Scores of one staged tile (log2 domain): 16 heads of this lane x its
-// column. MFMA k order: step ks = 2p + e takes, in k-half kh, the latent dims
-// 32p + 16kh + 8e .. +7, so one 16-byte LDS read of chunk 2p + kh of a row
-// feeds steps 2p and 2p + 1, and every step stays inside one scale group
-// (group g = steps 8g .. 8g + 7, the last group has 4). The groups accumulate
-// separately (their fp32 scales differ per row); the operands of the next
-// group are read while the current group's MFMAs run.
-__device__ __attribute__((always_inline)) inline void score_tile(const uint8_t* __restrict__ buf,
-                                                                 const bf16x8 (&A)[KSTEPS], float hs, int col, int kh,
-                                                                 bool valid, float (&s2)[16]) {
+// Partial scores of one staged tile over latent half dh for the 32 heads of
+// this wave's block x 32 positions, the fp32 group scales applied (log2
+// domain). Half 0 holds scale groups 0 and 1 and the first 32 dims of group
+// 4, half 1 groups 2 and 3 and the last 32 dims of group 4, so both halves
+// have the same shape (segments of 4, 4 and 1 step pairs) and the code has
+// no branch on dh. MFMA k order: step pair p (dims 32p..32p+31) takes, in
+// k-half kh, the 16-byte chunk 2p + kh of the row, whose low 8 bytes feed
+// step 2p and high 8 bytes step 2p + 1. The lane's 16 results are rows
+// 8i + 4kh + j (i = 0..3); rows i = 0, 1 are the ones this wave finishes and
+// rows i = 2, 3 go to the other half's wave. The half-1 wave holds its heads
+// in the order h ^ 16, so that its rows i = 0, 1 are the heads the half-0
+// wave hands over and the other way round.
+__device__ __attribute__((always_inline)) inline void score_half(const uint8_t* __restrict__ buf,
+                                                                 const bf16x8 (&A)[HSTEPS], float hs, int col, int kh,
+                                                                 int dh, float (&own)[8], float (&send)[8]) {
   const uint8_t* src = buf + col * ROW_LDS + 16 * kh;
-  const float* sc = reinterpret_cast<const float*>(buf + SC_OFF) + col * NGROUPS;
-  constexpr int NP = KSTEPS / 2;                     // 18 step pairs
-  uint4 cur[4], nxt[4];
+  uint4 ch[HPAIRS];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) cur[j] = *reinterpret_cast<const uint4*>(src + 32 * j);
-  floatx16 cg[NGROUPS];
+  for (int j = 0; j < 8; ++j) ch[j] = *reinterpret_cast<const uint4*>(src + 256 * dh + 32 * j);
+  ch[8] = *reinterpret_cast<const uint4*>(src + 512 + 32 * dh);
+  floatx16 c0 = {}, c1 = {}, c2 = {};
 #pragma unroll
-  for (int g = 0; g < NGROUPS; ++g) {
-    const int np = g < 4 ? 4 : 2;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (4 * (g + 1) + j < NP) nxt[j] = *reinterpret_cast<const uint4*>(src + 32 * (4 * (g + 1) + j));
-    floatx16 c = {};
-#pragma unroll
-    for (int j = 0; j < np; ++j) {
-      const int p = 4 * g + j;
-      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[2 * p], fp8x8_to_bf16(cur[j].x, cur[j].y), c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[2 * p + 1], fp8x8_to_bf16(cur[j].z, cur[j].w), c, 0, 0, 0);
+  for (int j = 0; j < HPAIRS; ++j) {
+    const bf16x8 lo = fp8x8_to_bf16(ch[j].x, ch[j].y), hi = fp8x8_to_bf16(ch[j].z, ch[j].w);
+    if (j < 4) {
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[2 * j], lo, c0, 0, 0, 0);
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[2 * j + 1], hi, c0, 0, 0, 0);
+    } else if (j < 8) {
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[2 * j], lo, c1, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[2 * j + 1], hi, c1, 0, 0, 0);
+    } else {
+      c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[2 * j], lo, c2, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[2 * j + 1], hi, c2, 0, 0, 0);
     }
-    cg[g] = c;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) cur[j] = nxt[j];
   }
-  const float g0 = sc[0] * hs, g1 = sc[1] * hs, g2 = sc[2] * hs, g3 = sc[3] * hs, g4 = sc[4] * hs;
+  const float* sc = reinterpret_cast<const float*>(buf + SC_OFF) + col * NGROUPS;
+  const float ga = sc[2 * dh] * hs, gb = sc[2 * dh + 1] * hs, gc = sc[4] * hs;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    float v = g0 * cg[0][e];
-    v = fmaf(g1, cg[1][e], v);
-    v = fmaf(g2, cg[2][e], v);
-    v = fmaf(g3, cg[3][e], v);
-    v = fmaf(g4, cg[4][e], v);
-    s2[e] = valid ? v : -INFINITY;
+    const float v = fmaf(gc, c2[e], fmaf(gb, c1[e], ga * c0[e]));
+    if (e < 8) own[e] = v; else send[e - 8] = v;
+  }
+}
+
+// Both halves of one tile: this wave's own partial plus the one the other
+// half's wave handed over (the sum is the same whichever wave adds), -inf
+// past the context.
+__device__ inline void finish_scores(const float (&own)[8], const float4* __restrict__ xr, bool valid,
+                                     float (&s)[8]) {
+  const float4 p0 = xr[0], p1 = xr[64];
+  s[0] = own[0] + p0.x; s[1] = own[1] + p0.y; s[2] = own[2] + p0.z; s[3] = own[3] + p0.w;
+  s[4] = own[4] + p1.x; s[5] = own[5] + p1.y; s[6] = own[6] + p1.z; s[7] = own[7] + p1.w;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s[e] = valid ? s[e] : -INFINITY;
+}
+
+__device__ inline void hand_over(const float (&send)[8], float4* __restrict__ xw) {
+  xw[0] = make_float4(send[0], send[1], send[2], send[3]);
+  xw[64] = make_float4(send[4], send[5], send[6], send[7]);
+}
+
+// Split statistics of the finished tiles 2u and 2u + 1 (8 head rows of this
+// lane x its column each), which form 64-position liveness tile u: its
+// maximum per head, reduced over the 32 columns, goes to the tile-maximum
+// table (lane col writes row e = col mod 8 of its half; lanes with equal e
+// hold equal values) and becomes the running reference m; every lane adds
+// exp2(s - m) of its own two scores to a lane-local sum l (rescaled when m
+// grows). No branch: lanes select their table value arithmetically.
+__device__ __attribute__((always_inline)) inline void tile_stats(int u, const float (&s0)[8], const float (&s1)[8],
+                                                                 float* __restrict__ tslot, int nlt, int esel,
+                                                                 float (&m)[8], float (&l)[8]) {
+  float tm[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) tm[e] = fmaxf(s0[e], s1[e]);
+  reduce32<true, 8>(tm);
+  float tv = tm[0];
+#pragma unroll
+  for (int e = 1; e < 8; ++e) tv = esel == e ? tm[e] : tv;
+  tslot[u] = tv;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float mn = fmaxf(m[e], tm[e]);
+    const float ms = mn == -INFINITY ? 0.f : mn;  // nothing valid yet: every term is 0
+    l[e] = l[e] * ex2(m[e] - ms) + ex2(s0[e] - ms) + ex2(s1[e] - ms);
+    m[e] = mn;
   }
 }
 
 // One tile of the scoring pass: start the direct loads of a later tile into
-// `wr` (when given), score the tile staged in `rd`, and fold it into the
-// split statistics. The restrict qualifiers state that the buffer being
-// filled, the buffer being read and the tile-maximum table are disjoint, so
-// the compiler adds no wait for the loads in flight; the waits that order a
-// tile's loads before its reads are explicit (wait_tiles + bar_nofence).
-template <int NW>
+// `wr` (when given), score this wave's half of the tile staged in `rd`, finish
+// the previous tile with the half the other wave handed over through `xr`,
+// and hand over this tile's other half through `xw`. CLOSE: the previous tile
+// closes a liveness tile (fold the pair into the statistics), else it opens
+// one (keep its scores in sprev). The restrict qualifiers state that the
+// buffer being filled, the buffer being read, the exchange slots and the
+// tile-maximum table are disjoint, so the compiler adds no wait for the
+// direct loads in flight; the waits that order a tile's loads before its
+// reads are explicit. Everything after the load issue is one basic block, so
+// the scheduler can interleave the statistics with the MFMAs.
+template <int NW, bool CLOSE>
 __device__ __attribute__((always_inline)) inline void scoring_step(
-    uint8_t* __restrict__ wr, const uint8_t* __restrict__ rd, float* __restrict__ tmax, const TileSrc& src,
-    int next_first, int wave, int lane, int t, int pos, int nlt, const bf16x8 (&A)[KSTEPS], float hs,
-    float (&m)[16], float (&l)[16], float (&sprev)[16]) {
+    uint8_t* __restrict__ wr, const uint8_t* __restrict__ rd, const float4* __restrict__ xr,
+    float4* __restrict__ xw, float* __restrict__ tslot, const TileSrc<NW>& src, int next_first, int wave, int lane,
+    int dh, int tprev, bool prev_valid, int nlt, int esel, const bf16x8 (&A)[HSTEPS], float hs, float (&own)[8],
+    float (&m)[8], float (&l)[8], float (&sprev)[8]) {
   const int col = lane & 31, kh = lane >> 5;
-  if (wr) issue_tile<NW>(wr, src, next_first, wave, lane);
-  float s2[16];
-  score_tile(rd, A, hs, col, kh, pos < src.ctx, s2);
-  if ((t & 1) == 0) {
+  if (wr) issue_tile<NW>(wr, src, next_first, wave);
+  float cur[8], send[8], s[8];
+  score_half(rd, A, hs, col, kh, dh, cur, send);
+  finish_scores(own, xr, prev_valid, s);
+  if constexpr (CLOSE) {
+    tile_stats(tprev >> 1, sprev, s, tslot, nlt, esel, m, l);
+  } else {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sprev[e] = s2[e];
-    return;
-  }
-  // end of a 64-position liveness tile: its maximum per head becomes the
-  // running reference of the lane-local sums
-  float tm[16];
-#pragma unroll
-  for (int e = 0; e < 16; ++e) tm[e] = fmaxf(sprev[e], s2[e]);
-  reduce32x16<true>(tm);
-  if (col == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) tmax[(32 * wave + 8 * i + 4 * kh + j) * nlt + (t >> 1)] = tm[4 * i + j];
+    for (int e = 0; e < 8; ++e) sprev[e] = s[e];
   }
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const float mn = fmaxf(m[e], tm[e]);
-    const float ms = mn == -INFINITY ? 0.f : mn;  // nothing valid yet: every term is 0
-    l[e] = l[e] * ex2(m[e] - ms) + ex2(sprev[e] - ms) + ex2(s2[e] - ms);
-    m[e] = mn;
+  for (int e = 0; e < 8; ++e) own[e] = cur[e];
+  hand_over(send, xw);
+  // Schedule: the LDS reads first, then every MFMA followed by a few vector
+  // instructions (conversions for the next MFMA, statistics of the previous
+  // tile), so the vector work issues while the MFMA runs.
+  __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+  __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+#pragma unroll
+  for (int i = 0; i < 2 * HPAIRS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, CLOSE ? 9 : 5, 0);
   }
 }
 
@@ -288,29 +354,43 @@ __device__ inline void stamp_mla(const MlaArgs& a, int k) {
   if (a.times && threadIdx.x == 0) a.times[int64_t(blockIdx.x) * 16 + k] = wall_clock64();
 }
 
+// s_waitcnt lgkmcnt(0) (this wave's LDS accesses are complete) then s_barrier
+__device__ inline void bar_lds() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
 }  // namespace mla
 
 using namespace mla;
 
 // ----------------------------------------------------------------------------- scores
+// NW waves = 2 per 32-head block: wave w takes head block w mod NB and latent
+// half w / NB; the two waves of a block exchange partial scores through LDS.
 template <int NW>
 __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
   constexpr int NT = 64 * NW;         // threads
-  constexpr int H = 32 * NW;          // heads
+  constexpr int NB = NW / 2;          // 32-head blocks
+  constexpr int H = 32 * NB;          // heads
   extern __shared__ __align__(16) unsigned char smem[];
   const int P = a.P;
   const int NLT = P / LTILE;          // liveness tiles per split
   uint8_t* ring = smem;                                                  // [NBUF][BUF_BYTES]
-  float* tmax = reinterpret_cast<float*>(ring + NBUF * BUF_BYTES);       // [H][NLT]
+  float4* xbuf = reinterpret_cast<float4*>(ring + NBUF * BUF_BYTES);     // [2][NW][2][64] handed-over halves
+  float* tmax = reinterpret_cast<float*>(xbuf + 2 * NW * 128);           // [H][NLT]
   float* lse = tmax + H * NLT;                                           // [H]
   int* live = reinterpret_cast<int*>(lse + H);                           // [NLT (+pad)]
-  unsigned* keepmask = reinterpret_cast<unsigned*>(live + ((NLT + 3) & ~3));  // [TILE]
-  int* misc = reinterpret_cast<int*>(keepmask + TILE);                   // [8]
+  unsigned* keepmask = reinterpret_cast<unsigned*>(live + ((NLT + 3) & ~3));  // [2][TILE]
+  int* misc = reinterpret_cast<int*>(keepmask + 2 * TILE);               // [8]
   float2* mlbuf = reinterpret_cast<float2*>(misc + 8);                   // [H + S] scratch (16-B aligned)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int hb = wave % NB;           // head block
+  const int dh = wave / NB;           // latent half
+  const int partner = hb + NB * (1 - dh);
   const int b = blockIdx.x / a.S;
   const int split = blockIdx.x - b * a.S;
   const int pos0 = split * P;
@@ -319,7 +399,8 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
   const uint32_t epoch = __hip_atomic_load(&a.hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
   const int col = lane & 31;          // MFMA column / A row
   const int kh = lane >> 5;           // k half (0: dims 0..7 of a k-step, 1: 8..15)
-  const int head_a = 32 * wave + col; // head of this lane's A operand row
+  const int head_a = 32 * hb + (col ^ (16 * dh));  // head of this lane's A operand row (half 1: h ^ 16)
+  const int hrow = 32 * hb + 16 * dh + 4 * kh;   // first head of this lane's finished rows (+8i + j)
 
   stamp_mla(a, 0);
   if (blockIdx.x == 0 && tid == 0) {
@@ -330,87 +411,76 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
     a.hdr->v_row_bytes = DV + 4 * (DV / 128);           // its value part
   }
 
-  // ---------------------------------------------------------------- tile staging
-  // Register staging of one tile into buffer 0 (the re-scoring pass).
-  constexpr int CHUNKS = TILE * (D / 16);
-  constexpr int PER = (CHUNKS + NT - 1) / NT;
-  constexpr int NSC = TILE * NGROUPS;
-  constexpr int PERS = (NSC + NT - 1) / NT;
-  auto stage = [&](int t) {
-    uint4 v[PER];
-    float sv[PERS];
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int i = tid + k * NT;
-      const int r = i / (D / 16), c = i - r * (D / 16);
-      const int pos = pos0 + t * TILE + r;
-      v[k] = (i < CHUNKS && pos < ctx) ? *reinterpret_cast<const uint4*>(a.kc + (row0 + pos) * D + c * 16)
-                                       : make_uint4(0u, 0u, 0u, 0u);
-    }
-#pragma unroll
-    for (int k = 0; k < PERS; ++k) {
-      const int i = tid + k * NT;
-      const int r = i / NGROUPS, gi = i - r * NGROUPS;
-      const int pos = pos0 + t * TILE + r;
-      sv[k] = (i < NSC && pos < ctx) ? reinterpret_cast<const float*>(a.ks + (row0 + pos) * (4 * NGROUPS))[gi] : 0.f;
-    }
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int i = tid + k * NT;
-      if (i < CHUNKS) {
-        const int r = i / (D / 16), c = i - r * (D / 16);
-        *reinterpret_cast<uint4*>(ring + r * ROW_LDS + c * 16) = v[k];
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < PERS; ++k)
-      if (tid + k * NT < NSC) reinterpret_cast<float*>(ring + SC_OFF)[tid + k * NT] = sv[k];
-  };
-  const TileSrc src{a.kc, reinterpret_cast<const float*>(a.ks), row0, ctx};
+  const TileSrc<NW> src(a.kc + row0 * D, reinterpret_cast<const float*>(a.ks) + row0 * NGROUPS, ctx, wave, lane);
   const int T = P / TILE;
   // the first three tiles start loading before the query is set up
-  for (int t = 0; t < 3 && t < T; ++t) issue_tile<NW>(ring + t * BUF_BYTES, src, pos0 + t * TILE, wave, lane);
+  for (int t = 0; t < 3 && t < T; ++t) issue_tile<NW>(ring + t * BUF_BYTES, src, pos0 + t * TILE, wave);
 
   // ---------------------------------------------------------------- q operands
-  // The bf16 query is the A operand as it is, in the k order of score_tile.
-  bf16x8 A[KSTEPS];
+  // The bf16 query is the A operand as it is, in the k order of score_half:
+  // local step pair j < 8 is pair 8 dh + j of the latent, pair 8 is 16 + dh.
+  bf16x8 A[HSTEPS];
   {
     const uint16_t* qh = reinterpret_cast<const uint16_t*>(a.q) + (int64_t(b) * H + head_a) * D + 16 * kh;
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks)
-      A[ks] = *reinterpret_cast<const bf16x8*>(qh + 32 * (ks >> 1) + 8 * (ks & 1));
+    for (int ks = 0; ks < HSTEPS; ++ks) {
+      const int gp = (ks >> 1) < 8 ? 8 * dh + (ks >> 1) : 16 + dh;
+      A[ks] = *reinterpret_cast<const bf16x8*>(qh + 32 * gp + 8 * (ks & 1));
+    }
   }
   const float hs = a.sigma_log2e;     // score scale: softmax scale * log2 e
 
   // ---------------------------------------------------------------- phase 1
-  // Per 64-position tile: the tile maximum per head (reduced over the 32
-  // columns) becomes the running reference m, every lane adds exp2(s - m) of
-  // its own two scores to a lane-local sum l (rescaled when m grows).
   stamp_mla(a, 1);
-  float m[16], l[16], sprev[16];
+  float m[8], l[8], sprev[8], own[8];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) { m[e] = -INFINITY; l[e] = 0.f; sprev[e] = -INFINITY; }
-  for (int t = 0; t < T; ++t) {
-    wait_tiles<NW>(min(2, T - 1 - t), wave);       // this wave's loads of tile t have landed
-    bar_nofence();                                  // everyone's have; buffer (t+3) % NBUF is free
-    uint8_t* wr = t + 3 < T ? ring + ((t + 3) % NBUF) * BUF_BYTES : nullptr;
-    scoring_step<NW>(wr, ring + (t % NBUF) * BUF_BYTES, tmax, src, pos0 + (t + 3) * TILE, wave, lane, t,
-                     pos0 + t * TILE + col, NLT, A, hs, m, l, sprev);
+  for (int e = 0; e < 8; ++e) { m[e] = -INFINITY; l[e] = 0.f; sprev[e] = -INFINITY; own[e] = 0.f; }
+  const int esel = col & 7;                          // the tile-maximum row this lane writes
+  float* tslot = tmax + (hrow + 8 * (esel >> 2) + (esel & 3)) * NLT;
+  auto xr_of = [&](int t) { return xbuf + ((t & 1) * NW + partner) * 128 + lane; };
+  auto xw_of = [&](int t) { return xbuf + ((t & 1) * NW + wave) * 128 + lane; };
+  auto wr_of = [&](int t) { return t + 3 < T ? ring + ((t + 3) % NBUF) * BUF_BYTES : nullptr; };
+  // Step t scores tile t and finishes tile t - 1; a liveness tile closes at
+  // even t >= 2. Step 0 finishes nothing (its "previous" scores are dropped).
+  // Before each step: this wave's loads of tile t have landed (wait_tiles),
+  // then everyone's have and tile t - 1's halves are handed over (barrier),
+  // and buffer (t + 3) mod NBUF is free.
+  wait_tiles<NW>(min(2, T - 1), wave);
+  bar_lds();
+  scoring_step<NW, false>(wr_of(0), ring, xr_of(1), xw_of(0), tslot, src, pos0 + 3 * TILE, wave, lane, dh, -1, false,
+                          NLT, esel, A, hs, own, m, l, sprev);
+  for (int t = 1; t < T; t += 2) {
+    wait_tiles<NW>(min(2, T - 1 - t), wave);
+    bar_lds();
+    scoring_step<NW, false>(wr_of(t), ring + (t % NBUF) * BUF_BYTES, xr_of(t - 1), xw_of(t), tslot, src,
+                            pos0 + (t + 3) * TILE, wave, lane, dh, t - 1, pos0 + (t - 1) * TILE + col < ctx, NLT,
+                            esel, A, hs, own, m, l, sprev);
+    if (t + 1 < T) {
+      wait_tiles<NW>(min(2, T - 2 - t), wave);
+      bar_lds();
+      scoring_step<NW, true>(wr_of(t + 1), ring + ((t + 1) % NBUF) * BUF_BYTES, xr_of(t), xw_of(t + 1), tslot, src,
+                             pos0 + (t + 4) * TILE, wave, lane, dh, t, pos0 + t * TILE + col < ctx, NLT, esel, A, hs,
+                             own, m, l, sprev);
+    }
+  }
+  bar_lds();
+  {
+    float s[8];
+    finish_scores(own, xr_of(T - 1), pos0 + (T - 1) * TILE + col < ctx, s);
+    tile_stats((T - 1) >> 1, sprev, s, tslot, NLT, esel, m, l);
   }
   __syncthreads();
   stamp_mla(a, 2);
   // split statistics per head: m is already common to the 32 columns; sum l
-  reduce32x16<false>(l);
+  reduce32<false, 8>(l);
   if (col == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int h = 32 * wave + 8 * i + 4 * kh + j;
-        u64* dst = a.split_ml + ((int64_t(b) * a.S + split) * H + h) * 2;
-        put_tagged_f(dst, epoch, m[4 * i + j]);
-        put_tagged_f(dst + 1, epoch, l[4 * i + j]);
-      }
+    for (int e = 0; e < 8; ++e) {
+      const int h = hrow + 8 * (e >> 2) + (e & 3);
+      u64* dst = a.split_ml + ((int64_t(b) * a.S + split) * H + h) * 2;
+      put_tagged_f(dst, epoch, m[e]);
+      put_tagged_f(dst + 1, epoch, l[e]);
+    }
   }
 
   // ---------------------------------------------------------------- phase 2: LSE
@@ -445,7 +515,7 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
   // ---------------------------------------------------------------- phase 3: live tiles
   // A 64-position tile is live when some head's tile maximum can reach the
   // threshold (a small margin keeps the test conservative); only live tiles
-  // are re-read and re-scored.
+  // are re-read and re-scored, with the same code and so the same bits.
   const float log2tau = a.tau > 0.f ? log2f(a.tau) : -INFINITY;
   if (tid == 0) misc[0] = 0;
   __syncthreads();
@@ -455,60 +525,113 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
       for (int h = 0; h < H && !lv; ++h) lv = tmax[h * NLT + u] >= lse[h] + log2tau - 0.01f;
     if (lv) live[atomicAdd(&misc[0], 1)] = u;
   }
+  if (tid < 2 * TILE) keepmask[tid] = 0u;
+  if (tid == 0) misc[2] = 0;                           // kept pairs
   __syncthreads();
   const int nlive = misc[0];
   // sort the (few) live tile ids so the published rows come out in position order
   if (tid == 0)
     for (int i = 1; i < nlive; ++i)
       for (int j = i; j > 0 && live[j - 1] > live[j]; --j) { const int x = live[j]; live[j] = live[j - 1]; live[j - 1] = x; }
-  if (tid == 1) { misc[1] = 0; misc[2] = 0; }        // kept rows, kept pairs
   __syncthreads();
-  int kept_pairs = 0;
-  const int64_t kbase = int64_t(b) * a.S + split;
-  for (int li = 0; li < nlive; ++li) {
-    const int u = live[li];
-    for (int half = 0; half < 2; ++half) {
-      const int t = 2 * u + half;
-      stage(t);
-      if (tid < TILE) keepmask[tid] = 0u;
-      __syncthreads();
-      float s2[16];
-      score_tile(ring, A, hs, col, kh, pos0 + t * TILE + col < ctx, s2);
-      // normalized weights and keep bits
-      unsigned bits = 0u;
-      float p[16];
+
+  // Register staging of 32-position tiles into ring buffers 0 and 1, one
+  // tile ahead of the one being scored.
+  constexpr int CHUNKS = TILE * (D / 16);
+  constexpr int PER = (CHUNKS + NT - 1) / NT;
+  constexpr int NSC = TILE * NGROUPS;
+  constexpr int PERS = (NSC + NT - 1) / NT;
+  uint4 sv[PER];
+  float ss[PERS];
+  auto fetch = [&](int t) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int e = 4 * i + j;
-          const float pe = exp2f(s2[e] - lse[32 * wave + 8 * i + 4 * kh + j]);   // denormal-exact
-          const bool keep = (s2[e] != -INFINITY) && pe >= a.tau;
-          p[e] = keep ? pe : 0.f;
-          bits |= keep ? 1u : 0u;
-          kept_pairs += keep ? 1 : 0;
-        }
-      if (bits) atomicOr(&keepmask[col], 1u);
-      __syncthreads();
-      // compaction: row index of each kept column within this split's list
-      if (tid == 0) {
-        int n = misc[1];
-        for (int c = 0; c < TILE; ++c) {
-          if (keepmask[c]) { keepmask[c] = 0x80000000u | unsigned(n); a.kpos[kbase * P + n] = pos0 + t * TILE + c; ++n; }
-        }
-        misc[1] = n;
-      }
-      __syncthreads();
-      const unsigned km = keepmask[col];
-      if (km & 0x80000000u) {
-        float* dst = a.kp + (kbase * P + (km & 0x7FFFFFFFu)) * H;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) dst[32 * wave + 8 * i + 4 * kh + j] = p[4 * i + j];
-      }
-      __syncthreads();
+    for (int k = 0; k < PER; ++k) {
+      const int i = tid + k * NT;
+      const int r = i / (D / 16), c = i - r * (D / 16);
+      const int pos = pos0 + t * TILE + r;
+      sv[k] = (i < CHUNKS && pos < ctx) ? *reinterpret_cast<const uint4*>(a.kc + (row0 + pos) * D + c * 16)
+                                        : make_uint4(0u, 0u, 0u, 0u);
     }
+#pragma unroll
+    for (int k = 0; k < PERS; ++k) {
+      const int i = tid + k * NT;
+      const int r = i / NGROUPS, gi = i - r * NGROUPS;
+      const int pos = pos0 + t * TILE + r;
+      ss[k] = (i < NSC && pos < ctx) ? reinterpret_cast<const float*>(a.ks + (row0 + pos) * (4 * NGROUPS))[gi] : 0.f;
+    }
+  };
+  auto put = [&](uint8_t* buf) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int i = tid + k * NT;
+      if (i < CHUNKS) {
+        const int r = i / (D / 16), c = i - r * (D / 16);
+        *reinterpret_cast<uint4*>(buf + r * ROW_LDS + c * 16) = sv[k];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < PERS; ++k)
+      if (tid + k * NT < NSC) reinterpret_cast<float*>(buf + SC_OFF)[tid + k * NT] = ss[k];
+  };
+  // normalized weights of a finished tile and its keep bits (OR-ed per column)
+  int kept_pairs = 0;
+  auto weigh = [&](int k, int t, float (&p)[8]) {     // k: place in the list (slots), t: tile in the split
+    float s[8];
+    finish_scores(own, xbuf + ((k & 1) * NW + partner) * 128 + lane, pos0 + t * TILE + col < ctx, s);
+    bool any = false;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float pe = exp2f(s[e] - lse[hrow + 8 * (e >> 2) + (e & 3)]);   // denormal-exact
+      const bool keep = (s[e] != -INFINITY) && pe >= a.tau;
+      p[e] = keep ? pe : 0.f;
+      any |= keep;
+      kept_pairs += keep ? 1 : 0;
+    }
+    if (any) atomicOr(&keepmask[(k & 1) * TILE + col], 1u);
+  };
+  // row index of each kept column: the running count plus the kept columns
+  // before it (every wave derives the same numbers from the same bits)
+  const int64_t kbase = int64_t(b) * a.S + split;
+  int nkept = 0;
+  auto publish = [&](int k, int t, const float (&p)[8]) {
+    const unsigned km = lane < TILE ? keepmask[(k & 1) * TILE + lane] : 0u;
+    const unsigned cm = unsigned(__ballot(km != 0u));
+    if ((cm >> col) & 1u) {
+      const int idx = nkept + __popc(cm & ((1u << col) - 1u));
+      if (wave == 0 && kh == 0) a.kpos[kbase * P + idx] = pos0 + t * TILE + col;
+      float* dst = a.kp + (kbase * P + idx) * H + hrow;
+      *reinterpret_cast<float4*>(dst) = make_float4(p[0], p[1], p[2], p[3]);
+      *reinterpret_cast<float4*>(dst + 8) = make_float4(p[4], p[5], p[6], p[7]);
+    }
+    nkept += __popc(cm);
+  };
+  const int n3 = 2 * nlive;                           // 32-position tiles to re-score
+  auto tile_at = [&](int k) { return 2 * live[k >> 1] + (k & 1); };
+  if (n3 > 0) {
+    fetch(tile_at(0));
+    put(ring);
+  }
+  for (int k = 0; k < n3; ++k) {
+    if (k + 1 < n3) fetch(tile_at(k + 1));
+    bar_lds();                                         // tile k staged; tile k - 1's halves handed over
+    if (k >= 2 && wave == 0 && lane < TILE) keepmask[(k & 1) * TILE + lane] = 0u;   // read two tiles ago
+    float cur[8], send[8];
+    score_half(ring + (k & 1) * BUF_BYTES, A, hs, col, kh, dh, cur, send);
+    float p[8];
+    if (k > 0) weigh(k - 1, tile_at(k - 1), p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) own[e] = cur[e];
+    hand_over(send, xbuf + ((k & 1) * NW + wave) * 128 + lane);
+    if (k + 1 < n3) put(ring + ((k + 1) & 1) * BUF_BYTES);
+    bar_lds();                                         // keep bits of tile k - 1 complete
+    if (k > 0) publish(k - 1, tile_at(k - 1), p);
+  }
+  if (n3 > 0) {
+    bar_lds();
+    float p[8];
+    weigh(n3 - 1, tile_at(n3 - 1), p);
+    bar_lds();
+    publish(n3 - 1, tile_at(n3 - 1), p);
   }
   // kept pairs of the split
 #pragma unroll
@@ -516,7 +639,7 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
   if (lane == 0) atomicAdd(&misc[2], kept_pairs);
   __syncthreads();
   if (tid == 0) {
-    a.kcount[kbase] = misc[1];
+    a.kcount[kbase] = nkept;
     a.kpairs[kbase] = misc[2];
   }
   stamp_mla(a, 4);
@@ -712,14 +835,15 @@ __global__ __launch_bounds__(256) void mla_out(MlaArgs a) {
 // the sizes below guarantee (every earlier region is a multiple of 16 bytes).
 size_t mla_lds_bytes(int H, int P, int S) {
   const int NLT = P / LTILE;
-  return size_t(NBUF) * BUF_BYTES + size_t(H) * NLT * 4 + size_t(H) * 4 +
-         size_t((NLT + 3) & ~3) * 4 + TILE * 4 + 8 * 4 + size_t(H + S) * 8 + 64;
+  const int NW = 2 * (H / 32);
+  return size_t(NBUF) * BUF_BYTES + size_t(2) * NW * 128 * 16 + size_t(H) * NLT * 4 + size_t(H) * 4 +
+         size_t((NLT + 3) & ~3) * 4 + 2 * TILE * 4 + 8 * 4 + size_t(H + S) * 8 + 64;
 }
 
 const void* mla_scores_kernel(int H) {
-  if (H == 32) return reinterpret_cast<const void*>(&mla_scores<1>);
-  if (H == 64) return reinterpret_cast<const void*>(&mla_scores<2>);
-  if (H == 128) return reinterpret_cast<const void*>(&mla_scores<4>);
+  if (H == 32) return reinterpret_cast<const void*>(&mla_scores<2>);
+  if (H == 64) return reinterpret_cast<const void*>(&mla_scores<4>);
+  if (H == 128) return reinterpret_cast<const void*>(&mla_scores<8>);
   return nullptr;
 }
 const void* mla_out_kernel() { return reinterpret_cast<const void*>(&mla_out); }
