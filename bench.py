@@ -224,6 +224,67 @@ def run_config(w, steps, warmup, splits=0):
     return line
 
 
+def run_append(steps, warmup):
+    """The device append packer (kvq_append): one decode step's new K and V rows
+    (one row per (sequence, kv head) each, as the long-context and latent
+    workloads append them) and a bulk prefill of a whole long-context cache.
+    Events around one graph replay of the timed calls give the time per call;
+    bytes are float32 rows read plus packed rows written."""
+    import numpy as np
+    import torch
+    import decode_attention_quantized_amd as kvq
+    import synth
+
+    stream = torch.cuda.Stream()
+    lines = []
+    # (name, fmt, dim, rows per call, caches per call (2: kvq_append_kv), cache rows)
+    cases = [("step long q4_0 K+V (one launch)", "q4_0", 128, 1 * 4, 2, 4 * 32768),
+             ("step latent fp8 (B8)", "fp8_b128", 576, 8, 1, 8 * 65536),
+             ("step lut3 K+V (B8, one launch)", "lut3", 128, 8 * 4, 2, 8 * 4 * 32768),
+             ("prefill long q4_0 K+V (one launch)", "q4_0", 128, 4 * 32768, 2, 4 * 32768)]
+    for name, fmt, dim, n, ncache, rows in cases:
+        cb, sb = kvq.kvq_row_bytes(fmt, dim)
+        planes = [(torch.zeros((rows, cb), dtype=torch.uint8, device="cuda"),
+                   torch.zeros((rows, sb), dtype=torch.uint8, device="cuda")) for _ in range(ncache)]
+        srcs = [torch.randn((n, dim), dtype=torch.float32, device="cuda") for _ in range(ncache)]
+        dst = torch.arange(n, dtype=torch.int64, device="cuda") * (rows // n) + (rows // n - 1)
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+        def call():
+            if ncache == 2:
+                kvq.kvq_append_kv(fmt, srcs[0], srcs[1], dst, *planes[0], *planes[1], status, stream.cuda_stream)
+            else:
+                kvq.kvq_append(fmt, srcs[0], dst, *planes[0], status, stream.cuda_stream)
+
+        with torch.cuda.stream(stream):
+            for _ in range(warmup):
+                call()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for _ in range(steps):
+                    call()
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+        per_call = e0.elapsed_time(e1) / 1e3 / steps
+        nbytes = ncache * n * (dim * 4 + cb + sb)
+        assert int(status.item()) == 0
+        for (codes, scales), src in zip(planes, srcs):       # spot check against the host packer
+            hc, hs = kvq.kvq_pack(fmt, src[:4].cpu().numpy())
+            assert np.array_equal(codes[dst[:4]].cpu().numpy(), hc)
+            assert np.array_equal(scales[dst[:4]].cpu().numpy(), hs)
+        lines.append({"workload": "append", "case": name, "fmt": fmt, "rows_per_cache": n, "caches": ncache,
+                      "us_per_call": round(per_call * 1e6, 3), "rows_per_s": round(ncache * n / per_call, 1),
+                      "bytes_per_call": nbytes, "achieved_gbs": round(nbytes / per_call / 1e9, 1),
+                      "frac_hbm": round(nbytes / per_call / 1e9 / HBM_PEAK_GBS, 4)})
+    return lines
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -235,7 +296,8 @@ def main():
                     help="which threshold(s) to time (a profiler run can restrict to one)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy 5 times (reference for HBM byte counters)")
-    ap.add_argument("--workload", choices=["long", "tiny", "sweep", "lut3", "mla", "stress"], default="long",
+    ap.add_argument("--workload", choices=["long", "tiny", "sweep", "lut3", "mla", "stress", "append"],
+                    default="long",
                     help="long (default) prints the metric line; the others print one line per "
                          "configuration (sweep: one per context length)")
     ap.add_argument("--write-traffic", metavar="DIR",
@@ -267,6 +329,10 @@ def main():
     import synth
     from decode_attention_quantized_amd.runtime import DecodeAttention, PackedCache
 
+    if args.workload == "append":
+        for line in run_append(min(args.steps, 50), min(args.warmup, 5)):
+            print(json.dumps(line), flush=True)
+        return
     if args.workload != "long":
         names = [f"sweep_{n}" for n in synth.SWEEP] if args.workload == "sweep" else [args.workload]
         for nm in names:

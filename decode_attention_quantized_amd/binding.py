@@ -49,7 +49,8 @@ class kvq_stats_t(ctypes.Structure):
                 ("batch", ctypes.c_int32), ("q_heads", ctypes.c_int32)]
 
 
-EXPORTS = ["kvq_row_bytes", "kvq_pack", "kvq_unpack", "kvq_lut3_levels", "kvq_workspace_bytes",
+EXPORTS = ["kvq_row_bytes", "kvq_pack", "kvq_unpack", "kvq_lut3_levels", "kvq_append", "kvq_append_kv",
+           "kvq_workspace_bytes",
            "kvq_decode_attn", "kvq_stats", "kvq_phase_count", "kvq_strerror"]
 
 _lib = None
@@ -68,6 +69,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_pack.argtypes = [i32, vp, i64, i32, vp, vp]
         L.kvq_unpack.argtypes = [i32, vp, vp, i64, i32, vp]
         L.kvq_lut3_levels.argtypes = [vp]
+        L.kvq_append.argtypes = [i32, vp, i64, i32, vp, vp, vp, i64, vp, vp]
+        L.kvq_append_kv.argtypes = [i32, vp, vp, i64, i32, vp, vp, vp, vp, vp, i64, vp, vp]
         L.kvq_workspace_bytes.argtypes = [i32, ctypes.POINTER(kvq_cache), ctypes.POINTER(kvq_launch), i32,
                                           ctypes.POINTER(i64)]
         L.kvq_decode_attn.argtypes = [vp, ctypes.POINTER(kvq_cache), ctypes.POINTER(kvq_cache), i32, i32,
@@ -128,6 +131,44 @@ def kvq_lut3_levels():
     out = np.zeros(4, np.uint16)
     _check(lib().kvq_lut3_levels(out.ctypes.data), "kvq_lut3_levels")
     return out
+
+
+def kvq_append(fmt, src, dst_rows, codes, scales, status=None, stream=None):
+    """Pack device float32 rows ``src`` [n, dim] into the device planes ``codes`` /
+    ``scales`` (tensors whose leading dimensions hold ``cache_rows`` rows) at the
+    plane rows ``dst_rows`` (device int64 [n], or None for rows 0..n-1).
+    ``status``: optional device int32 tensor that receives the skipped-row bits."""
+    dim = int(src.shape[-1])
+    n = src.numel() // dim if dim else 0
+    cb, sb = kvq_row_bytes(fmt, dim)
+    cache_rows = codes.numel() // cb
+    if scales.numel() // sb != cache_rows:
+        raise KvqError(-1, "kvq_append: code and scale planes hold different row counts")
+    if dst_rows is not None and dst_rows.numel() != n:
+        raise KvqError(-1, "kvq_append: one destination row per source row")
+    _check(lib().kvq_append(_fmt(fmt), src.data_ptr(), n, dim, None if dst_rows is None else dst_rows.data_ptr(),
+                            codes.data_ptr(), scales.data_ptr(), cache_rows,
+                            None if status is None else status.data_ptr(), stream), "kvq_append")
+
+
+def kvq_append_kv(fmt, k_src, v_src, dst_rows, k_codes, k_scales, v_codes, v_scales, status=None, stream=None):
+    """kvq_append for a key and a value cache in one launch (same rows, same
+    destination rows, same format and width)."""
+    dim = int(k_src.shape[-1])
+    n = k_src.numel() // dim if dim else 0
+    if v_src.shape != k_src.shape:
+        raise KvqError(-1, "kvq_append_kv: key and value rows differ in shape")
+    cb, sb = kvq_row_bytes(fmt, dim)
+    cache_rows = k_codes.numel() // cb
+    for p, b in ((k_scales, sb), (v_codes, cb), (v_scales, sb)):
+        if p.numel() // b != cache_rows:
+            raise KvqError(-1, "kvq_append_kv: planes hold different row counts")
+    if dst_rows is not None and dst_rows.numel() != n:
+        raise KvqError(-1, "kvq_append_kv: one destination row per source row")
+    _check(lib().kvq_append_kv(_fmt(fmt), k_src.data_ptr(), v_src.data_ptr(), n, dim,
+                               None if dst_rows is None else dst_rows.data_ptr(), k_codes.data_ptr(),
+                               k_scales.data_ptr(), v_codes.data_ptr(), v_scales.data_ptr(), cache_rows,
+                               None if status is None else status.data_ptr(), stream), "kvq_append_kv")
 
 
 def make_cache(codes, scales, dim: int) -> kvq_cache:

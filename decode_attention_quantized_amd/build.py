@@ -33,6 +33,8 @@ SOURCES = [
     # needs no input quieting and folds into DPP reductions
     ("kvq_gqa.hip", HIP_FLAGS + ["-ffp-contract=fast", "-fno-honor-nans"]),
     ("kvq_mla.hip", HIP_FLAGS + ["-ffp-contract=fast", "-fno-honor-nans"]),
+    # the device packer rounds exactly as the host packer: no contraction
+    ("kvq_append.hip", HIP_FLAGS + ["-ffp-contract=off", "-fno-fast-math"]),
 ]
 
 

@@ -36,6 +36,38 @@ class PackedCache:
     def clone(self) -> "PackedCache":
         return PackedCache(self.codes.clone(), self.scales.clone(), self.fmt, self.dim)
 
+    @classmethod
+    def empty(cls, fmt, batch: int, heads: int, capacity: int, dim: int, device="cuda"):
+        cb, sb = B.kvq_row_bytes(fmt, dim)
+        c = torch.zeros((batch, heads, capacity, cb), dtype=torch.uint8, device=device)
+        s = torch.zeros((batch, heads, capacity, sb), dtype=torch.uint8, device=device)
+        return cls(c, s, fmt, dim)
+
+    def append(self, rows: torch.Tensor, positions: torch.Tensor, status: torch.Tensor | None = None,
+               stream=None):
+        """Quantize one new row per (batch, head) on the GPU into position
+        ``positions[b]`` of sequence b: ``rows`` is float32 [batch][heads][dim]
+        on the device, ``positions`` int64 [batch] on the device."""
+        Bn, H, cap = self.shape
+        assert rows.shape == (Bn, H, self.dim) and rows.dtype == torch.float32 and rows.is_contiguous()
+        bh = torch.arange(Bn * H, device=rows.device, dtype=torch.int64).view(Bn, H)
+        dst = (bh * cap + positions.to(torch.int64).view(Bn, 1)).contiguous()
+        B.kvq_append(self.fmt, rows, dst, self.codes, self.scales, status, stream)
+
+
+def append_kv(k: PackedCache, v: PackedCache, k_rows: torch.Tensor, v_rows: torch.Tensor, positions: torch.Tensor,
+              status: torch.Tensor | None = None, stream=None):
+    """One decode step's appends in one launch: the new key and value rows
+    (float32 [batch][heads][dim] on the device) go to position ``positions[b]``
+    of sequence b in both caches (same format, shape and width)."""
+    Bn, H, cap = k.shape
+    assert v.shape == k.shape and v.dim == k.dim and v.fmt == k.fmt
+    assert k_rows.shape == (Bn, H, k.dim) and v_rows.shape == k_rows.shape
+    bh = torch.arange(Bn * H, device=k_rows.device, dtype=torch.int64).view(Bn, H)
+    dst = (bh * cap + positions.to(torch.int64).view(Bn, 1)).contiguous()
+    B.kvq_append_kv(k.fmt, k_rows.contiguous(), v_rows.contiguous(), dst, k.codes, k.scales, v.codes, v.scales,
+                    status, stream)
+
 
 class DecodeAttention:
     """One decode-attention configuration with its own workspace."""

@@ -112,6 +112,36 @@ int32_t kvq_unpack(int32_t fmt, const uint8_t* codes, const uint8_t* scales,
 /* The four LUT3 magnitudes as fp16 bit patterns (host out[4]). */
 int32_t kvq_lut3_levels(uint16_t* out4);
 
+/* Pack float32 rows that are in device memory straight into device planes:
+ * the per-step append of a decode loop (the new token's key or value rows,
+ * quantized on the GPU before the attention reads them), or a whole prefill.
+ * Each row is packed exactly as kvq_pack packs it (same bytes), by a kernel
+ * that shares kvq_pack's per-element and per-scale steps.
+ *  src        device float32 [n_rows][dim], row-major, 4-byte aligned
+ *  dst_rows   device int64 [n_rows]: the plane row each source row goes to,
+ *             e.g. (b*heads + h)*capacity + position in a kvq_cache layout;
+ *             NULL writes row r to plane row r (then n_rows <= cache_rows)
+ *  codes, scales  device planes of cache_rows rows (kvq_row_bytes each),
+ *             16-byte aligned; only the destination rows are written
+ *  status     optional device int32: a row holding a NaN or infinity (1),
+ *             whose scale overflows fp16 (2) or whose destination is outside
+ *             [0, cache_rows) (4) is left unwritten and its bits are OR-ed in
+ *  stream     hipStream_t (NULL = default stream); asynchronous
+ * Errors (checked before any device work): ARG (bad fmt, null planes or
+ * source, negative counts), UNSUPPORTED (dim, as kvq_row_bytes), ALIGN,
+ * RANGE (dst_rows NULL and n_rows > cache_rows), LAUNCH. */
+int32_t kvq_append(int32_t fmt, const float* src, int64_t n_rows, int32_t dim, const int64_t* dst_rows,
+                   void* codes, void* scales, int64_t cache_rows, int32_t* status, void* stream);
+
+/* kvq_append for a key and a value cache in one launch (a decode step's two
+ * appends): k_src and v_src are both device float32 [n_rows][dim], the rows
+ * go to the same dst_rows of (k_codes, k_scales) and (v_codes, v_scales),
+ * each cache_rows rows of the same format and dim. Arguments, status bits
+ * and errors as kvq_append. */
+int32_t kvq_append_kv(int32_t fmt, const float* k_src, const float* v_src, int64_t n_rows, int32_t dim,
+                      const int64_t* dst_rows, void* k_codes, void* k_scales, void* v_codes, void* v_scales,
+                      int64_t cache_rows, int32_t* status, void* stream);
+
 /* ------------------------------------------------------------------ decode */
 
 /* A packed cache in device memory. Row r of (batch b, head h) is at

@@ -72,3 +72,34 @@ def test_workspace_query_validation():
     launch = B.kvq_launch(4, 0, 0.0, 0, None, 0, None, None, 0, 0, None)
     assert L.kvq_workspace_bytes(B.KVQ_Q4_0, ctypes.byref(_cache()), ctypes.byref(launch), 0, ctypes.byref(b)) == -3
     assert L.kvq_workspace_bytes(B.KVQ_Q4_0, ctypes.byref(_cache()), ctypes.byref(launch), 10, None) == -1
+
+
+def test_append_argument_validation_without_gpu():
+    L = B.lib()
+    src, dst, c, s = 0x10000, 0x20000, 0x30000, 0x40000   # fake aligned addresses: never dereferenced
+    assert L.kvq_append(9, src, 4, 128, dst, c, s, 16, None, None) == -1          # bad fmt
+    assert L.kvq_append(B.KVQ_Q4_0, src, 4, 100, dst, c, s, 16, None, None) == -7  # dim % 32
+    assert L.kvq_append(B.KVQ_LUT3, src, 4, 64, dst, c, s, 16, None, None) == -7   # lut3 is 128 wide
+    assert L.kvq_append(B.KVQ_Q8_0, src, -1, 128, dst, c, s, 16, None, None) == -1
+    assert L.kvq_append(B.KVQ_Q8_0, src, 4, 128, dst, c, s, -1, None, None) == -1
+    assert L.kvq_append(B.KVQ_Q8_0, src, 0, 128, dst, c, s, 16, None, None) == 0   # nothing to do
+    assert L.kvq_append(B.KVQ_Q8_0, None, 4, 128, dst, c, s, 16, None, None) == -1
+    assert L.kvq_append(B.KVQ_Q8_0, src, 4, 128, dst, None, s, 16, None, None) == -1
+    assert L.kvq_append(B.KVQ_Q8_0, src, 4, 128, dst, c, None, 16, None, None) == -1
+    assert L.kvq_append(B.KVQ_Q8_0, src + 2, 4, 128, dst, c, s, 16, None, None) == -2   # ALIGN
+    assert L.kvq_append(B.KVQ_Q8_0, src, 4, 128, dst + 4, c, s, 16, None, None) == -2
+    assert L.kvq_append(B.KVQ_Q8_0, src, 4, 128, dst, c + 8, s, 16, None, None) == -2
+    assert L.kvq_append(B.KVQ_Q8_0, src, 4, 128, dst, c, s + 8, 16, None, None) == -2
+    assert L.kvq_append(B.KVQ_Q8_0, src, 17, 128, None, c, s, 16, None, None) == -3    # RANGE: n > cache rows
+
+
+def test_append_kv_argument_validation_without_gpu():
+    L = B.lib()
+    k, v, dst = 0x10000, 0x18000, 0x20000
+    kc, ks, vc, vs = 0x30000, 0x40000, 0x50000, 0x60000
+    assert L.kvq_append_kv(9, k, v, 4, 128, dst, kc, ks, vc, vs, 16, None, None) == -1
+    assert L.kvq_append_kv(B.KVQ_Q4_0, k, None, 4, 128, dst, kc, ks, vc, vs, 16, None, None) == -1
+    assert L.kvq_append_kv(B.KVQ_Q4_0, k, v, 4, 128, dst, kc, ks, None, vs, 16, None, None) == -1
+    assert L.kvq_append_kv(B.KVQ_Q4_0, k, v, 4, 128, dst, kc, ks, vc, vs + 4, 16, None, None) == -2
+    assert L.kvq_append_kv(B.KVQ_Q4_0, k, v + 2, 4, 128, dst, kc, ks, vc, vs, 16, None, None) == -2
+    assert L.kvq_append_kv(B.KVQ_Q4_0, k, v, 0, 128, dst, kc, ks, vc, vs, 16, None, None) == 0
