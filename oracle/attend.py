@@ -98,6 +98,76 @@ def attend(q, k_codes, k_scales, v_codes, v_scales, *, fmt, dim, v_dim, ctx_len,
                   union=union, kept_pairs=int(mask.sum()), rows_fetched=int(union.sum()), vmax=vmax)
 
 
+def running_keep(S, positions_per_split, block, tau):
+    """The single-pass (in-loop) skip rule on a score matrix S [G][n] (float64,
+    natural-log domain): the context is cut into splits of
+    ``positions_per_split`` positions, each split is walked in blocks of
+    ``block`` positions in position order, and position i is kept when its
+    weight under the softmax of its split's positions up to the end of i's
+    block reaches ``tau``:
+        p_run_i = exp(s_i - m_r) / sum_{j in split, j <= end of block(i)} exp(s_j - m_r),
+        m_r = max over the same positions.
+    This is the weight a flash-attention loop sees when it decides at block i
+    with its running max and sum ([SV] "Решение — не ускорять, а
+    пропускать": the skip is decided from the weights inside the loop); since
+    the running denominator only grows, p_run_i >= p_i for the final
+    normalized weight, so the kept set contains the exact rule's.
+    Returns (p_run [G][n], keep [G][n])."""
+    S = np.asarray(S, dtype=np.float64)
+    G, n = S.shape
+    p_run = np.zeros_like(S)
+    for s0 in range(0, n, positions_per_split):
+        s1 = min(s0 + positions_per_split, n)
+        for b0 in range(s0, s1, block):
+            b1 = min(b0 + block, s1)
+            pre = S[:, s0:b1]                                  # the split's prefix through this block
+            m = pre.max(axis=1, keepdims=True)
+            den = np.exp(pre - m).sum(axis=1, keepdims=True)
+            p_run[:, b0:b1] = np.exp(S[:, b0:b1] - m) / den
+    return p_run, p_run >= float(np.float32(tau))
+
+
+def attend_running(q, k_codes, k_scales, v_codes, v_scales, *, fmt, dim, v_dim, ctx_len, sigma, threshold,
+                   positions_per_split, block=64) -> tuple[Result, np.ndarray]:
+    """``attend`` with the single-pass keep rule of ``running_keep``: out =
+    sum over kept i of p_i * v_i with p_i the exact normalized weight (only the
+    set of kept positions changes). Returns (result, p_run [B][Hq][n])."""
+    q = np.asarray(q)
+    B, Hq, D = q.shape
+    assert D == dim
+    Hkv = k_codes.shape[1]
+    n = int(ctx_len)
+    sig = float(np.float32(sigma))
+    tau = float(np.float32(threshold))
+    out64 = np.zeros((B, Hq, v_dim), dtype=np.float64)
+    P = np.zeros((B, Hq, n), dtype=np.float64)
+    PR = np.zeros((B, Hq, n), dtype=np.float64)
+    mask = np.zeros((B, Hq, n), dtype=bool)
+    kept = np.zeros((B, Hq), dtype=np.float64)
+    union = np.zeros((B, Hkv, n), dtype=bool)
+    vmax = np.zeros((B, Hkv), dtype=np.float64)
+    for b in range(B):
+        kh = dequant_cache(fmt, k_codes[b:b + 1], k_scales[b:b + 1], dim, n)[0]
+        vh = dequant_cache(fmt, v_codes[b:b + 1], v_scales[b:b + 1], v_dim, n)[0]
+        for g in range(Hkv):
+            heads = [h for h in range(Hq) if (h * Hkv) // Hq == g]
+            S = sig * (q[b, heads].astype(np.float64) @ kh[g].T)
+            m = S.max(axis=1, keepdims=True)
+            E = np.exp(S - m)
+            p = E / E.sum(axis=1, keepdims=True)
+            p_run, keep = running_keep(S, positions_per_split, block, tau)
+            out64[b, heads] = (p * keep) @ vh[g]
+            P[b, heads] = p
+            PR[b, heads] = p_run
+            mask[b, heads] = keep
+            kept[b, heads] = (p * keep).sum(axis=1)
+            union[b, g] = keep.any(axis=0)
+            vmax[b, g] = np.abs(vh[g]).max()
+    res = Result(out=out64.astype(np.float32), out64=out64, p=P, mask=mask, kept_mass=kept,
+                 union=union, kept_pairs=int(mask.sum()), rows_fetched=int(union.sum()), vmax=vmax)
+    return res, PR
+
+
 def attend_inputs(inp, *, threshold=None, ctx_len=None, packed=None) -> tuple[Result, dict]:
     """Pack a ``synth.Inputs`` with the oracle's own packer and attend.
 
