@@ -202,6 +202,11 @@ def run_config(w, steps, warmup, splits=0):
                           v_dim=w.v_dim if latent else 0)
     res = {m: time_mode(att, q, caches, w.ctx, tau, steps, warmup, out, stream)
            for m, tau in (("sparse", w.threshold), ("dense", 0.0))}
+    if not latent:                                   # the single-pass skip rule (grouped formats)
+        att_run = DecodeAttention(K0, V0, w.q_heads, ctx_len=w.ctx, softmax_scale=w.sigma, splits=splits,
+                                  stream=stream, q_dtype=kvq.KVQ_Q_BF16 if w.q_bf16 else kvq.KVQ_Q_F32,
+                                  running=True)
+        res["single_pass"] = time_mode(att_run, q, caches, w.ctx, w.threshold, steps, warmup, out, stream)
     qo = w.batch * w.q_heads * (w.dim * q.element_size() + w.v_dim * 4)
     k_bytes = (w.batch * w.ctx if latent else w.batch * w.kv_heads * w.ctx) * row
     line = {"workload": w.name, "fmt": str(w.fmt), "batch": w.batch,
@@ -221,6 +226,9 @@ def run_config(w, steps, warmup, splits=0):
             d["frac_mfma_bf16"] = round(flops / r["kernel_mean"] / 1e12 / 2500.0, 4)
         line[m] = d
     line["speedup_sparse_vs_dense"] = round(res["dense"]["wall"] / res["sparse"]["wall"], 3)
+    if "single_pass" in res:
+        line["single_pass"]["extra_rows_vs_exact"] = (res["single_pass"]["stats"]["rows_fetched"]
+                                                      - res["sparse"]["stats"]["rows_fetched"])
     return line
 
 
@@ -292,7 +300,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile-mode", choices=["sparse", "dense", "both"], default="both",
+    ap.add_argument("--profile-mode", choices=["sparse", "dense", "single_pass", "both"], default="both",
                     help="which threshold(s) to time (a profiler run can restrict to one)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy 5 times (reference for HBM byte counters)")
@@ -358,13 +366,15 @@ def main():
     att = DecodeAttention(K0, V0, w.q_heads, ctx_len=w.ctx, softmax_scale=w.sigma, splits=args.splits,
                           stream=stream)
 
-    modes = {"sparse": w.threshold, "dense": 0.0}
+    att_run = DecodeAttention(K0, V0, w.q_heads, ctx_len=w.ctx, softmax_scale=w.sigma, splits=args.splits,
+                              stream=stream, running=True)
+    modes = {"sparse": (att, w.threshold), "dense": (att, 0.0), "single_pass": (att_run, w.threshold)}
     if args.profile_mode != "both":
         modes = {args.profile_mode: modes[args.profile_mode]}
     res = {}
     outs = {}
-    for name, tau in modes.items():
-        res[name] = time_mode(att, q, caches, w.ctx, tau, args.steps, args.warmup, out, stream)
+    for name, (at, tau) in modes.items():
+        res[name] = time_mode(at, q, caches, w.ctx, tau, args.steps, args.warmup, out, stream)
         outs[name] = out.cpu().numpy().copy()
 
     qo_bytes = w.batch * w.q_heads * w.dim * 4 + w.batch * w.q_heads * w.v_dim * 4
@@ -435,6 +445,20 @@ def main():
             "traffic": load_traffic("dense"),
         }
         line["speedup_sparse_vs_dense"] = round(d["wall"] / r["wall"], 3)
+    if "single_pass" in res and main_mode == "sparse":
+        sp = res["single_pass"]
+        abs_ = alg_bytes("single_pass")
+        line["single_pass"] = {
+            "rule": "keep when the split's running softmax weight (64-position blocks) reaches the threshold",
+            "tokens_per_s": round(w.batch / sp["wall"], 1),
+            "ms_per_step": round(sp["wall"] * 1e3, 5),
+            "kernel_us_mean": round(sp["kernel_mean"] * 1e6, 3),
+            "achieved_gbs_kernel": round(abs_ / sp["kernel_mean"] / 1e9, 1),
+            "frac_hbm": round(abs_ / sp["kernel_mean"] / 1e9 / HBM_PEAK_GBS, 4),
+            "rows_fetched": sp["stats"]["rows_fetched"],
+            "extra_rows_vs_exact": sp["stats"]["rows_fetched"] - r["stats"]["rows_fetched"],
+            "kept_pairs": sp["stats"]["kept_pairs"],
+        }
     if not args.no_cpu_baseline:
         cb_, ref, (okc, oks) = cpu_baseline(inp)
         line["cpu_baseline"] = cb_

@@ -15,7 +15,7 @@
 
 namespace kvq {
 size_t gqa_lds_bytes(int fmt, int G, int P, int S);
-const void* gqa_kernel(int fmt, int G);
+const void* gqa_kernel(int fmt, int G, bool run);
 size_t mla_lds_bytes(int H, int P, int S);
 const void* mla_scores_kernel(int H);
 const void* mla_out_kernel();
@@ -249,11 +249,14 @@ extern "C" int32_t kvq_decode_attn(const void* q, const kvq_cache* kcache, const
                                    const kvq_launch* l) {
   if (!q || !kcache || !out || !l) return KVQ_ERR_ARG;
   if (!(threshold >= 0.0f) || !(threshold < 1.0f)) return KVQ_ERR_RANGE;   // also rejects NaN
-  if (l->flags & ~int32_t(KVQ_LAUNCH_COOPERATIVE)) return KVQ_ERR_ARG;
+  if (l->flags & ~int32_t(KVQ_LAUNCH_COOPERATIVE | KVQ_SKIP_RUNNING)) return KVQ_ERR_ARG;
   Plan plan;
   int32_t rc = make_plan(fmt, kcache, l, ctx_len, &plan);
   if (rc) return rc;
-  if (plan.mla) return launch_mla(q, kcache, vcache, ctx_len, threshold, out, l, plan);
+  if (plan.mla) {
+    if (l->flags & KVQ_SKIP_RUNNING) return KVQ_ERR_UNSUPPORTED;   // latent kernels use the exact rule only
+    return launch_mla(q, kcache, vcache, ctx_len, threshold, out, l, plan);
+  }
   if (!vcache) return KVQ_ERR_UNSUPPORTED;                 // latent caches: not in this kernel family
   if (vcache->batch != kcache->batch || vcache->heads != kcache->heads ||
       vcache->capacity != kcache->capacity || vcache->dim != 128)
@@ -296,7 +299,7 @@ extern "C" int32_t kvq_decode_attn(const void* q, const kvq_cache* kcache, const
   a.tau = threshold;
   a.times = reinterpret_cast<unsigned long long*>(l->phase_times);
 
-  const void* kern = kvq::gqa_kernel(fmt, plan.G);
+  const void* kern = kvq::gqa_kernel(fmt, plan.G, (l->flags & KVQ_SKIP_RUNNING) != 0);
   if (!kern) return KVQ_ERR_UNSUPPORTED;
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kvq::kThreads, plan.lds) != hipSuccess)

@@ -384,7 +384,15 @@ template <class T> struct LoadedOf<T, true> { using type = typename T::Raw16; };
 // runs its own V pass and sums one slice of the group's output; split 0 of
 // each group also counts its group towards publishing the next epoch (once
 // past the LSE exchange every workgroup of the group has read the epoch).
-template <int FMT, int G>
+//
+// RUN selects the single-pass skip rule: a position is kept when its weight
+// under the softmax of its split's positions up to the end of its 64-position
+// block reaches the threshold (the weight an in-loop flash-attention kernel
+// sees with its running max and sum). That decision needs nothing from other
+// workgroups, so the V pass runs right after the scores with weights relative
+// to the split's own max, and the group's LSE is gathered afterwards only to
+// scale the partial output (its wait overlaps the V pass).
+template <int FMT, int G, bool RUN>
 __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   using T = Traits<FMT>;
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
@@ -624,6 +632,7 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
       u64* dst = a.split_ml + ((int64_t(bg) * a.S + split) * G + j) * 2;
       put_tagged_f(dst, epoch, acc.x);
       put_tagged_f(dst + 1, epoch, acc.y);
+      if constexpr (RUN) lse[j] = acc.x;             // the split's max: reference of its weights
     }
   }
   __syncthreads();                                   // wml is reused below
@@ -632,44 +641,79 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   // Every workgroup gathers all split statistics of its group and merges
   // them itself (128 threads per head, fixed pattern, so every workgroup of
   // the group computes the same bits); no workgroup waits on another's LSE.
-  {
-    float2 acc = make_float2(-INFINITY, 0.f);
-    const int j = tid >> 7, ln = tid & 127;
-    if (j < G) {
-      for (int s0 = ln; s0 < a.S; s0 += 4 * 128) {
-        u64 w[8];
-        const u64* src[8];
-        bool use[8];
+  auto gather_lse = [&](float* dst) {
+    {
+      float2 acc = make_float2(-INFINITY, 0.f);
+      const int j = tid >> 7, ln = tid & 127;
+      if (j < G) {
+        for (int s0 = ln; s0 < a.S; s0 += 4 * 128) {
+          u64 w[8];
+          const u64* src[8];
+          bool use[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int sp = s0 + 128 * u;
-          src[2 * u] = a.split_ml + ((int64_t(bg) * a.S + (sp < a.S ? sp : 0)) * G + j) * 2;
-          src[2 * u + 1] = src[2 * u] + 1;
-          use[2 * u] = use[2 * u + 1] = sp < a.S;
-          w[2 * u] = use[2 * u] ? peek(src[2 * u]) : 0ull;
-          w[2 * u + 1] = use[2 * u] ? peek(src[2 * u + 1]) : 0ull;
+          for (int u = 0; u < 4; ++u) {
+            const int sp = s0 + 128 * u;
+            src[2 * u] = a.split_ml + ((int64_t(bg) * a.S + (sp < a.S ? sp : 0)) * G + j) * 2;
+            src[2 * u + 1] = src[2 * u] + 1;
+            use[2 * u] = use[2 * u + 1] = sp < a.S;
+            w[2 * u] = use[2 * u] ? peek(src[2 * u]) : 0ull;
+            w[2 * u + 1] = use[2 * u] ? peek(src[2 * u + 1]) : 0ull;
+          }
+          settle_all(w, src, use, epoch, a.hdr);
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (use[2 * u]) acc = lse_merge(acc, make_float2(__uint_as_float(uint32_t(w[2 * u])),
+                                                             __uint_as_float(uint32_t(w[2 * u + 1]))));
         }
-        settle_all(w, src, use, epoch, a.hdr);
+        acc = merge_row16(acc);                        // lane 16r holds row r's merge
+        float2 row[3];                                 // rows 1..3, read before any merging
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (use[2 * u]) acc = lse_merge(acc, make_float2(__uint_as_float(uint32_t(w[2 * u])),
-                                                           __uint_as_float(uint32_t(w[2 * u + 1]))));
+        for (int r = 1; r < 4; ++r) {
+          row[r - 1].x = __shfl(acc.x, 16 * r);
+          row[r - 1].y = __shfl(acc.y, 16 * r);
+        }
+#pragma unroll
+        for (int r = 0; r < 3; ++r) acc = lse_merge(acc, row[r]);
+        if (lane == 0) wml[wave] = acc;                 // two waves per head
       }
-      acc = merge_row16(acc);                        // lane 16r holds row r's merge
-      float2 row[3];                                 // rows 1..3, read before any merging
-#pragma unroll
-      for (int r = 1; r < 4; ++r) {
-        row[r - 1].x = __shfl(acc.x, 16 * r);
-        row[r - 1].y = __shfl(acc.y, 16 * r);
+      __syncthreads();
+      if (tid < G) {
+        const float2 v = lse_merge(wml[2 * tid], wml[2 * tid + 1]);
+        dst[tid] = v.x + log2f(v.y);
       }
+      __syncthreads();
+    }
+  };
+  const int nch = P / kChunk;                        // 64-position blocks of the split
+  // single-pass rule: running LSE per (head, block) [G][nch] after block
+  // summaries [G][nch], both in the K staging strip (free until the V pass)
+  float2* csum = reinterpret_cast<float2*>(stg);
+  float* rl = reinterpret_cast<float*>(csum + G * nch);
+  if constexpr (!RUN) {
+    gather_lse(lse);
+  } else {
+    // block summaries: four adjacent threads per (head, block), 16 positions
+    // each, combined with two exchanges (kThreads is a multiple of 64, so the
+    // four are lanes of one wave in every pass of the loop)
+    for (int it = tid; it < G * nch * 4; it += kThreads) {
+      const int q4 = it & 3, jc = it >> 2;
+      const int j = jc / nch, c = jc - j * nch;
+      float m = -INFINITY, l = 0.f;
+      const float* src = sc + j * P + c * kChunk + 16 * q4;
 #pragma unroll
-      for (int r = 0; r < 3; ++r) acc = lse_merge(acc, row[r]);
-      if (lane == 0) wml[wave] = acc;                 // two waves per head
+      for (int i = 0; i < 16; ++i) online_add(m, l, src[i]);
+      float2 v = make_float2(m, l);
+      v = lse_merge(v, make_float2(__shfl_xor(v.x, 1), __shfl_xor(v.y, 1)));
+      v = lse_merge(v, make_float2(__shfl_xor(v.x, 2), __shfl_xor(v.y, 2)));
+      if (q4 == 0) csum[jc] = v;
     }
     __syncthreads();
-    if (tid < G) {
-      const float2 v = lse_merge(wml[2 * tid], wml[2 * tid + 1]);
-      lse[tid] = v.x + log2f(v.y);
+    if (tid < G) {                                   // prefix over the blocks in position order
+      float2 acc = make_float2(-INFINITY, 0.f);
+      for (int c = 0; c < nch; ++c) {
+        acc = lse_merge(acc, csum[tid * nch + c]);
+        rl[tid * nch + c] = acc.x + log2f(acc.y);
+      }
     }
     __syncthreads();
   }
@@ -705,10 +749,13 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
         const int j = jb + jj;
         // the hardware exp flushes results below 2^-126; any normal threshold
         // decides above that, so it gives the same keep bits and weights
-        const float x = sc[j * P + lp] - lsej[jj];
+        const float sv = sc[j * P + lp];
+        const float x = sv - (RUN ? rl[j * nch + c] : lsej[jj]);
         const float p = valid ? (tau_normal ? ex2(x) : exp2f(x)) : 0.f;
         const bool keep = valid && (p >= tau);
-        sc[j * P + lp] = keep ? p : 0.f;          // kept weight replaces the score in place
+        // kept weight replaces the score in place (single-pass rule: relative
+        // to the split's max, rescaled when the partial is published)
+        sc[j * P + lp] = keep ? (RUN ? ex2(sv - lsej[jj]) : p) : 0.f;
         any |= keep;
         const unsigned long long bal = __ballot(keep);
         kept_cnt += __popcll(bal);
@@ -816,6 +863,14 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   }
   nact = __popc(act);
   const int64_t pbase = int64_t(bg) * a.S + split;
+  float* fac = qmax;                                  // single-pass rule: per-head factor to the group LSE
+  if constexpr (RUN) {
+    // every workgroup takes part (the exchange also proves to the epoch
+    // counter below that the whole group has read the epoch)
+    gather_lse(fac);
+    if (tid < G) fac[tid] = exp2f(lse[tid] - fac[tid]);
+    __syncthreads();
+  }
   if (nact == 0) {                                    // uniform: nothing kept, publish zeros
     for (int i = tid; i < G * 128; i += kThreads) put_tagged_f(a.partial + pbase * G * 128 + i, epoch, 0.f);
     if (tid < G) put_tagged_f(a.pmass + pbase * G + tid, epoch, 0.f);
@@ -835,12 +890,14 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     for (int i = tid; i < G * 128; i += kThreads) {
       float s = 0.f;
       for (int k = 0; k < nact; ++k) s += red[k * G * 128 + i];
+      if constexpr (RUN) s *= fac[i >> 7];
       put_tagged_f(a.partial + pbase * G * 128 + i, epoch, s);
     }
     if (tid < G) {
       float s = 0.f;
       for (int w = 0; w < kWaves; ++w)
         if ((act >> w) & 1u) s += wmass[w * G + tid];
+      if constexpr (RUN) s *= fac[tid];
       put_tagged_f(a.pmass + pbase * G + tid, epoch, s);
     }
   }
@@ -964,8 +1021,11 @@ size_t gqa_lds_bytes(int fmt, int G, int P, int S) {
          size_t(kWaves) * 16 * pitch + 64;
 }
 
-const void* gqa_kernel(int fmt, int G) {
-#define KVQ_SEL(F, GG) if (fmt == F && G == GG) return reinterpret_cast<const void*>(&gqa_fused<F, GG>);
+const void* gqa_kernel(int fmt, int G, bool run) {
+#define KVQ_SEL(F, GG)                                                                      \
+  if (fmt == F && G == GG)                                                                  \
+    return run ? reinterpret_cast<const void*>(&gqa_fused<F, GG, true>)                     \
+               : reinterpret_cast<const void*>(&gqa_fused<F, GG, false>);
   KVQ_SEL(KVQ_Q4_0, 1) KVQ_SEL(KVQ_Q4_0, 2) KVQ_SEL(KVQ_Q4_0, 4) KVQ_SEL(KVQ_Q4_0, 8)
   KVQ_SEL(KVQ_Q8_0, 1) KVQ_SEL(KVQ_Q8_0, 2) KVQ_SEL(KVQ_Q8_0, 4) KVQ_SEL(KVQ_Q8_0, 8)
   KVQ_SEL(KVQ_LUT3, 1) KVQ_SEL(KVQ_LUT3, 2) KVQ_SEL(KVQ_LUT3, 4) KVQ_SEL(KVQ_LUT3, 8)

@@ -74,7 +74,7 @@ class DecodeAttention:
 
     def __init__(self, k: PackedCache, v: PackedCache | None, q_heads: int, *, ctx_len: int,
                  q_dtype=B.KVQ_Q_F32, softmax_scale: float = 0.0, v_dim: int = 0, splits: int = 0,
-                 stream=None, cooperative: bool = False):
+                 stream=None, cooperative: bool = False, running: bool = False):
         self.k, self.v = k, v
         self.q_heads = q_heads
         self.fmt = k.fmt
@@ -82,7 +82,8 @@ class DecodeAttention:
         self.stream = stream
         self.launch_proto = dict(q_dtype=q_dtype, softmax_scale=softmax_scale,
                                  v_dim=v_dim if v is None else 0, splits=splits,
-                                 flags=B.KVQ_LAUNCH_COOPERATIVE if cooperative else 0)
+                                 flags=(B.KVQ_LAUNCH_COOPERATIVE if cooperative else 0)
+                                 | (B.KVQ_SKIP_RUNNING if running else 0))
         probe = B.make_launch(q_heads, **self.launch_proto)
         nbytes = B.kvq_workspace_bytes(self.fmt, k.struct(), probe, ctx_len)
         self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=k.codes.device)

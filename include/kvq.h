@@ -168,21 +168,32 @@ typedef struct kvq_launch {
   uint32_t* mask_out;     /* optional device [batch][q_heads][ceil(ctx_len/32)]: bit i%32 of
                              word i/32 = position i kept by that head; NULL to skip */
   int32_t splits;         /* 0 = automatic; otherwise context splits per (batch, kv head) */
-  int32_t flags;          /* 0 or KVQ_LAUNCH_COOPERATIVE */
+  int32_t flags;          /* 0 or KVQ_LAUNCH_COOPERATIVE | KVQ_SKIP_RUNNING */
   uint64_t* phase_times;  /* optional device [workgroups][16] buffer (profiling aid; NULL to skip):
                              each workgroup stores the 100 MHz device wall clock at its phase
                              boundaries (see kvq_phase_count) */
 } kvq_launch;
 
-/* kvq_launch.flags. The workgroups of one call exchange data while they run,
- * so all of them must be resident at once; the plan never launches more than
- * one workgroup per compute unit. By default the kernel is launched normally
- * (lowest latency), and every wait is bounded (about half a second) so a call
- * that cannot get its workgroups resident, e.g. because another kernel holds
- * the compute units, ends with KVQ_ERR_DEVICE from kvq_stats rather than a
- * hang. KVQ_LAUNCH_COOPERATIVE asks the runtime to guarantee co-residency
- * (hipLaunchCooperativeKernel), at roughly 20 us extra per call. */
-enum { KVQ_LAUNCH_COOPERATIVE = 1 };
+/* kvq_launch.flags (bits). The workgroups of one call exchange data while they
+ * run, so all of them must be resident at once; the plan never launches more
+ * than one workgroup per compute unit. By default the kernel is launched
+ * normally (lowest latency), and every wait is bounded (about half a second)
+ * so a call that cannot get its workgroups resident, e.g. because another
+ * kernel holds the compute units, ends with KVQ_ERR_DEVICE from kvq_stats
+ * rather than a hang. KVQ_LAUNCH_COOPERATIVE asks the runtime to guarantee
+ * co-residency (hipLaunchCooperativeKernel), at roughly 20 us extra per call.
+ *
+ * KVQ_SKIP_RUNNING selects the single-pass skip rule of an in-loop
+ * flash-attention kernel ([SV] "Решение — не ускорять, а пропускать": the
+ * skip is decided from the weights inside the loop): the context is cut into
+ * the plan's splits (kvq_stats.splits; P = ceil(ctx_len / splits) rounded up
+ * to a multiple of 64 positions), each walked in blocks of 64 positions, and
+ * position i is kept when its weight under the softmax of its split's
+ * positions up to the end of its block reaches the threshold. That weight is
+ * never smaller than the normalized weight, so the kept set contains the
+ * default rule's; the output still uses the normalized weights of the kept
+ * positions. Grouped formats only (UNSUPPORTED for the fp8 latent). */
+enum { KVQ_LAUNCH_COOPERATIVE = 1, KVQ_SKIP_RUNNING = 2 };
 
 /* Device workspace bytes kvq_decode_attn needs for these shapes on the
  * current device (bytes: host out-pointer). */

@@ -19,7 +19,7 @@ def say(*a):
     sys.stdout.flush()
 
 
-def run_gpu(inp, threshold, *, ctx_len=None, splits=0, q_bf16=False, repeat=1, cooperative=False):
+def run_gpu(inp, threshold, *, ctx_len=None, splits=0, q_bf16=False, repeat=1, cooperative=False, running=False):
     """Pack with the library, run kvq_decode_attn on cuda:0. Returns dict."""
     import torch
 
@@ -38,7 +38,7 @@ def run_gpu(inp, threshold, *, ctx_len=None, splits=0, q_bf16=False, repeat=1, c
         V = None
     att = DecodeAttention(K, V, w.q_heads, ctx_len=n, softmax_scale=w.sigma, splits=splits,
                           q_dtype=kvq.KVQ_Q_BF16 if q_bf16 else kvq.KVQ_Q_F32,
-                          v_dim=w.v_dim if V is None else 0, cooperative=cooperative)
+                          v_dim=w.v_dim if V is None else 0, cooperative=cooperative, running=running)
     q = torch.from_numpy(inp.q).cuda()
     if q_bf16:
         q = q.to(torch.bfloat16)
