@@ -804,10 +804,10 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
         rr[i] = piece / NL;
         ch[i] = piece - rr[i] * NL;
         ok[i] = piece < VB * NL && k + rr[i] < nmine;
-        if (ok[i]) {
-          const int64_t row = row0 + pos0 + mylist[k + rr[i]];
-          cv[i] = *reinterpret_cast<const uint4*>(a.vc + row * T::CB + 16 * ch[i]);
-        }
+        // every lane loads (pieces past the batch re-read the batch's first
+        // row), so the loads are not branched around and stay in registers
+        const int64_t row = row0 + pos0 + mylist[ok[i] ? k + rr[i] : k];
+        cv[i] = *reinterpret_cast<const uint4*>(a.vc + row * T::CB + 16 * (ok[i] ? ch[i] : 0));
       }
       const bool sok = lane < VB && k + lane < nmine;
       uint2 sv = make_uint2(0u, 0u);
