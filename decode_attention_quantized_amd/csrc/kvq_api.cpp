@@ -186,7 +186,6 @@ int32_t launch_mla(const void* q, const kvq_cache* kcache, const kvq_cache* vcac
   a.kept_mass = reinterpret_cast<float*>(ws + plan.mws.kept_mass);
   a.bgstat = reinterpret_cast<unsigned long long*>(ws + plan.mws.bgstat);
   a.split_ml = reinterpret_cast<unsigned long long*>(ws + plan.mws.split_ml);
-  a.lse = reinterpret_cast<unsigned long long*>(ws + plan.mws.lse);
   a.kcount = reinterpret_cast<int32_t*>(ws + plan.mws.kcount);
   a.kpairs = reinterpret_cast<int32_t*>(ws + plan.mws.kpairs);
   a.kpos = reinterpret_cast<int32_t*>(ws + plan.mws.kpos);

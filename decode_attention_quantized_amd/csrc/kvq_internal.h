@@ -100,7 +100,6 @@ struct MlaArgs {
   float* kept_mass;               // [B][H]
   unsigned long long* bgstat;     // [B][2]
   unsigned long long* split_ml;   // tagged [B][S][H][2]
-  unsigned long long* lse;        // tagged [B][H]
   int32_t* kcount;                // [B][S] kept rows published by each split
   int32_t* kpairs;                // [B][S] kept (head, position) pairs per split
   int32_t* kpos;                  // [B][S][P] positions of kept rows
@@ -113,7 +112,7 @@ struct MlaArgs {
 };
 
 struct MlaLayout {
-  int64_t kept_mass, bgstat, split_ml, lse, kcount, kpairs, kpos, kp, total;
+  int64_t kept_mass, bgstat, split_ml, kcount, kpairs, kpos, kp, total;
 };
 
 // The first two regions match ws_layout() so kvq_stats reads both families alike.
@@ -123,7 +122,6 @@ inline MlaLayout mla_ws_layout(int B, int H, int S, int P) {
   w.kept_mass = off; off = align256(off + int64_t(B) * H * 4);
   w.bgstat = off;    off = align256(off + int64_t(B) * 16);
   w.split_ml = off;  off = align256(off + int64_t(B) * S * H * 16);
-  w.lse = off;       off = align256(off + int64_t(B) * H * 8);
   w.kcount = off;    off = align256(off + int64_t(B) * S * 4);
   w.kpairs = off;    off = align256(off + int64_t(B) * S * 4);
   w.kpos = off;      off = align256(off + int64_t(B) * S * P * 4);

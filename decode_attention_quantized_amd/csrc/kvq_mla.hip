@@ -383,7 +383,6 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
   int* live = reinterpret_cast<int*>(lse + H);                           // [NLT (+pad)]
   unsigned* keepmask = reinterpret_cast<unsigned*>(live + ((NLT + 3) & ~3));  // [2][TILE]
   int* misc = reinterpret_cast<int*>(keepmask + 2 * TILE);               // [8]
-  float2* mlbuf = reinterpret_cast<float2*>(misc + 8);                   // [H + S] scratch (16-B aligned)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -484,30 +483,39 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
   }
 
   // ---------------------------------------------------------------- phase 2: LSE
-  // head h is merged by split (h mod S) over all splits, in split order
+  // Every workgroup merges the split statistics of all heads of its sequence
+  // itself (one exchange, no second round trip): four threads per head, thread
+  // q merging splits q, q + 4, ... in order, then the four results in a fixed
+  // order, so every workgroup of the sequence computes the same bits.
   {
-    const int nh = (H - split + a.S - 1) / a.S;      // heads this split merges: split, split + S, ...
-    for (int it = tid; it < nh * a.S; it += NT) {
-      const int hl = it / a.S, sp = it - hl * a.S;
-      const int h = split + hl * a.S;
-      const u64* src = a.split_ml + ((int64_t(b) * a.S + sp) * H + h) * 2;
-      const u64 w0 = peek(src), w1 = peek(src + 1);
-      float2 v;
-      v.x = settle_f(w0, src, epoch, a.hdr);
-      v.y = settle_f(w1, src + 1, epoch, a.hdr);
-      // scratch: [hl][sp], fits because nh * S <= H + S - 1 <= mlbuf size checked by the host
-      mlbuf[it] = v;
+    const int h = tid >> 2, q = tid & 3;              // NT = 4 * H
+    float2 acc = make_float2(-INFINITY, 0.f);
+    constexpr int SB = 8;                             // splits per batch of loads
+    for (int s0 = q; s0 < a.S; s0 += 4 * SB) {
+      u64 w[2 * SB];
+      const u64* src[2 * SB];
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        const int sp = s0 + 4 * u;
+        src[2 * u] = a.split_ml + ((int64_t(b) * a.S + (sp < a.S ? sp : 0)) * H + h) * 2;
+        src[2 * u + 1] = src[2 * u] + 1;
+        w[2 * u] = sp < a.S ? peek(src[2 * u]) : 0ull;
+        w[2 * u + 1] = sp < a.S ? peek(src[2 * u + 1]) : 0ull;
+      }
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        if (s0 + 4 * u >= a.S) break;
+        const float m = settle_f(w[2 * u], src[2 * u], epoch, a.hdr);
+        const float l = settle_f(w[2 * u + 1], src[2 * u + 1], epoch, a.hdr);
+        acc = lse_merge(acc, make_float2(m, l));
+      }
     }
-    __syncthreads();
-    if (tid < nh) {
-      float2 acc = make_float2(-INFINITY, 0.f);
-      for (int sp = 0; sp < a.S; ++sp) acc = lse_merge(acc, mlbuf[tid * a.S + sp]);
-      put_tagged_f(a.lse + int64_t(b) * H + split + tid * a.S, epoch, acc.x + log2f(acc.y));
-    }
-    if (tid < H) {
-      const u64* src = a.lse + int64_t(b) * H + tid;
-      lse[tid] = settle_f(peek(src), src, epoch, a.hdr);
-    }
+    // (q0 + q1) + (q2 + q3): lanes 4h.. of one wave
+    const float2 x1 = make_float2(__shfl_xor(acc.x, 1), __shfl_xor(acc.y, 1));
+    const float2 p = (q & 1) ? lse_merge(x1, acc) : lse_merge(acc, x1);
+    const float2 x2 = make_float2(__shfl_xor(p.x, 2), __shfl_xor(p.y, 2));
+    const float2 r = (q & 2) ? lse_merge(x2, p) : lse_merge(p, x2);
+    if (q == 0) lse[h] = r.x + log2f(r.y);
     __syncthreads();
   }
   stamp_mla(a, 3);
@@ -535,43 +543,47 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
       for (int j = i; j > 0 && live[j - 1] > live[j]; --j) { const int x = live[j]; live[j] = live[j - 1]; live[j - 1] = x; }
   __syncthreads();
 
-  // Register staging of 32-position tiles into ring buffers 0 and 1, one
-  // tile ahead of the one being scored.
+  // Register staging of 32-position tiles into ring buffers 0 and 1, two
+  // register sets, so two tiles are in flight while one is scored.
   constexpr int CHUNKS = TILE * (D / 16);
   constexpr int PER = (CHUNKS + NT - 1) / NT;
   constexpr int NSC = TILE * NGROUPS;
   constexpr int PERS = (NSC + NT - 1) / NT;
-  uint4 sv[PER];
-  float ss[PERS];
-  auto fetch = [&](int t) {
+  struct Stage {
+    uint4 v[PER];
+    float s[PERS];
+  };
+  Stage st0, st1;
+  auto fetch = [&](Stage& st, int t) {
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int i = tid + k * NT;
       const int r = i / (D / 16), c = i - r * (D / 16);
       const int pos = pos0 + t * TILE + r;
-      sv[k] = (i < CHUNKS && pos < ctx) ? *reinterpret_cast<const uint4*>(a.kc + (row0 + pos) * D + c * 16)
-                                        : make_uint4(0u, 0u, 0u, 0u);
+      st.v[k] = (i < CHUNKS && pos < ctx) ? *reinterpret_cast<const uint4*>(a.kc + (row0 + pos) * D + c * 16)
+                                          : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int k = 0; k < PERS; ++k) {
       const int i = tid + k * NT;
       const int r = i / NGROUPS, gi = i - r * NGROUPS;
       const int pos = pos0 + t * TILE + r;
-      ss[k] = (i < NSC && pos < ctx) ? reinterpret_cast<const float*>(a.ks + (row0 + pos) * (4 * NGROUPS))[gi] : 0.f;
+      st.s[k] = (i < NSC && pos < ctx) ? reinterpret_cast<const float*>(a.ks + (row0 + pos) * (4 * NGROUPS))[gi]
+                                       : 0.f;
     }
   };
-  auto put = [&](uint8_t* buf) {
+  auto put = [&](const Stage& st, uint8_t* buf) {
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int i = tid + k * NT;
       if (i < CHUNKS) {
         const int r = i / (D / 16), c = i - r * (D / 16);
-        *reinterpret_cast<uint4*>(buf + r * ROW_LDS + c * 16) = sv[k];
+        *reinterpret_cast<uint4*>(buf + r * ROW_LDS + c * 16) = st.v[k];
       }
     }
 #pragma unroll
     for (int k = 0; k < PERS; ++k)
-      if (tid + k * NT < NSC) reinterpret_cast<float*>(buf + SC_OFF)[tid + k * NT] = ss[k];
+      if (tid + k * NT < NSC) reinterpret_cast<float*>(buf + SC_OFF)[tid + k * NT] = st.s[k];
   };
   // normalized weights of a finished tile and its keep bits (OR-ed per column)
   int kept_pairs = 0;
@@ -607,13 +619,20 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
   };
   const int n3 = 2 * nlive;                           // 32-position tiles to re-score
   auto tile_at = [&](int k) { return 2 * live[k >> 1] + (k & 1); };
-  if (n3 > 0) {
-    fetch(tile_at(0));
-    put(ring);
-  }
-  for (int k = 0; k < n3; ++k) {
-    if (k + 1 < n3) fetch(tile_at(k + 1));
+  // tile k is scored from buffer k % 2; even tiles are staged through st0,
+  // odd ones through st1. Step k first stages tile k + 1 (loaded two steps
+  // earlier) into the buffer tile k - 1 used and starts loading tile k + 3
+  // into the set it came from.
+  if (n3 > 0) fetch(st0, tile_at(0));
+  if (n3 > 1) fetch(st1, tile_at(1));
+  if (n3 > 0) put(st0, ring);
+  if (n3 > 2) fetch(st0, tile_at(2));
+  auto step = [&](int k, Stage& nx) {
     bar_lds();                                         // tile k staged; tile k - 1's halves handed over
+    if (k + 1 < n3) {
+      put(nx, ring + ((k + 1) & 1) * BUF_BYTES);
+      if (k + 3 < n3) fetch(nx, tile_at(k + 3));
+    }
     if (k >= 2 && wave == 0 && lane < TILE) keepmask[(k & 1) * TILE + lane] = 0u;   // read two tiles ago
     float cur[8], send[8];
     score_half(ring + (k & 1) * BUF_BYTES, A, hs, col, kh, dh, cur, send);
@@ -622,9 +641,12 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) own[e] = cur[e];
     hand_over(send, xbuf + ((k & 1) * NW + wave) * 128 + lane);
-    if (k + 1 < n3) put(ring + ((k + 1) & 1) * BUF_BYTES);
     bar_lds();                                         // keep bits of tile k - 1 complete
     if (k > 0) publish(k - 1, tile_at(k - 1), p);
+  };
+  for (int k = 0; k < n3; k += 2) {
+    step(k, st1);
+    if (k + 1 < n3) step(k + 1, st0);
   }
   if (n3 > 0) {
     bar_lds();
@@ -831,13 +853,13 @@ __global__ __launch_bounds__(256) void mla_out(MlaArgs a) {
   }
 }
 
-// LDS bytes of mla_scores; the float2 scratch must start 8-byte aligned, which
-// the sizes below guarantee (every earlier region is a multiple of 16 bytes).
+// LDS bytes of mla_scores (every region is a multiple of 16 bytes).
 size_t mla_lds_bytes(int H, int P, int S) {
   const int NLT = P / LTILE;
   const int NW = 2 * (H / 32);
+  (void)S;
   return size_t(NBUF) * BUF_BYTES + size_t(2) * NW * 128 * 16 + size_t(H) * NLT * 4 + size_t(H) * 4 +
-         size_t((NLT + 3) & ~3) * 4 + 2 * TILE * 4 + 8 * 4 + size_t(H + S) * 8 + 64;
+         size_t((NLT + 3) & ~3) * 4 + 2 * TILE * 4 + 8 * 4 + 64;
 }
 
 const void* mla_scores_kernel(int H) {
