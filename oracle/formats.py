@@ -31,7 +31,8 @@ Q8_0 = "q8_0"
 Q4_0 = "q4_0"
 LUT3 = "lut3"
 FP8 = "fp8_b128"
-FORMATS = (Q8_0, Q4_0, LUT3, FP8)
+LUT3_WHT = "lut3_wht"
+FORMATS = (Q8_0, Q4_0, LUT3, FP8, LUT3_WHT)
 
 BLOCK = 32          # q8_0 / q4_0 block length
 FP8_GROUP = 128     # fp8 scale group length (the last group may be shorter)
@@ -50,7 +51,7 @@ def row_bytes(fmt: str, dim: int) -> tuple[int, int]:
     if fmt == Q4_0:
         _need(dim % BLOCK == 0, "q4_0 needs dim % 32 == 0")
         return dim // 2, 2 * (dim // BLOCK)
-    if fmt == LUT3:
+    if fmt in (LUT3, LUT3_WHT):
         _need(dim == 128, "lut3 rows are 128 wide")
         return 48, 2
     if fmt == FP8:
@@ -169,6 +170,13 @@ def lut3_table():
 
 
 def pack_lut3(x: np.ndarray):
+    """LUT3 of float32 rows (see _pack_lut3_f64)."""
+    x64 = np.asarray(x, dtype=np.float32).astype(np.float64)
+    _check_finite(x64)
+    return _pack_lut3_f64(x64)
+
+
+def _pack_lut3_f64(x64: np.ndarray):
     """LUT3: a 128-wide row becomes 128 three-bit codes (top bit = sign, low two
     bits = magnitude index into M) and one fp16 scalar nu.
 
@@ -182,8 +190,6 @@ def pack_lut3(x: np.ndarray):
     Row = 48 B: the 128 codes as one little-endian 384-bit string, element i at
     bits 3i..3i+2 (code = sign << 2 | magnitude index); scale plane = nu.
     """
-    x64 = np.asarray(x, dtype=np.float32).astype(np.float64)
-    _check_finite(x64)
     R, D = x64.shape
     row_bytes(LUT3, D)
     M, thr = lut3_table()
@@ -230,6 +236,52 @@ def unpack_lut3(codes, scales, dim=128):
     nu = scales.view("<f2").astype(np.float64).reshape(-1, 1)
     val = np.where(sign == 1, -M[mag], M[mag])
     return (nu * val) / math.sqrt(128.0)
+
+
+# --------------------------------------------------------------------------- LUT3 with a Walsh-Hadamard rotation
+# [SV] "Почему это работает для любой квантизации": turbo3 rotates the row with
+# a Walsh-Hadamard transform before its codebook quantization (the page names
+# it as the reason turbo3's dequantization is the most expensive). Reading
+# taken here: the orthonormal transform y = H x / sqrt(128) with H the 128x128
+# Sylvester Hadamard matrix (H[i][j] = (-1)^popcount(i & j)), applied in
+# float64 as the butterfly network below, then LUT3 of y. The transform is its
+# own inverse, so a decoded row is H LUT3^-1(codes) / sqrt(128).
+
+WHT_SCALE = 1.0 / math.sqrt(128.0)           # float64, one rounding
+
+
+def fwht(x64: np.ndarray) -> np.ndarray:
+    """H x along the last axis (length 128), as butterflies in a fixed order:
+    for h = 1, 2, 4, ..., 64 and every pair (j, j + h) with j mod 2h < h,
+    (a, b) -> (a + b, a - b), each a single float64 addition."""
+    y = np.array(x64, dtype=np.float64, copy=True)
+    n = y.shape[-1]
+    h = 1
+    while h < n:
+        v = y.reshape(y.shape[:-1] + (n // (2 * h), 2, h))
+        a = v[..., 0, :].copy()
+        b = v[..., 1, :].copy()
+        v[..., 0, :] = a + b
+        v[..., 1, :] = a - b
+        h *= 2
+    return y
+
+
+def wht_rotate(x64: np.ndarray) -> np.ndarray:
+    """y = H x / sqrt(128): the butterflies, then one multiply by WHT_SCALE."""
+    return fwht(x64) * WHT_SCALE
+
+
+def pack_lut3_wht(x: np.ndarray):
+    """LUT3 of the rotated float32 rows (the rotated row stays float64)."""
+    x64 = np.asarray(x, dtype=np.float32).astype(np.float64)
+    _check_finite(x64)
+    _need(x64.shape[1] == 128, "lut3 rows are 128 wide")
+    return _pack_lut3_f64(wht_rotate(x64))
+
+
+def unpack_lut3_wht(codes, scales, dim=128):
+    return wht_rotate(unpack_lut3(codes, scales, dim))
 
 
 # --------------------------------------------------------------------------- e4m3
@@ -319,7 +371,7 @@ def pack(fmt: str, x: np.ndarray):
     x = np.asarray(x)
     shape = x.shape
     x2 = x.reshape(-1, shape[-1])
-    fn = {Q8_0: pack_q8_0, Q4_0: pack_q4_0, LUT3: pack_lut3, FP8: pack_fp8}[fmt]
+    fn = {Q8_0: pack_q8_0, Q4_0: pack_q4_0, LUT3: pack_lut3, FP8: pack_fp8, LUT3_WHT: pack_lut3_wht}[fmt]
     c, s = fn(x2)
     return c.reshape(shape[:-1] + (c.shape[-1],)), s.reshape(shape[:-1] + (s.shape[-1],))
 
@@ -329,5 +381,5 @@ def unpack(fmt: str, codes, scales, dim: int):
     lead = codes.shape[:-1]
     c2 = np.ascontiguousarray(codes).reshape(-1, codes.shape[-1])
     s2 = np.ascontiguousarray(scales).reshape(-1, scales.shape[-1])
-    fn = {Q8_0: unpack_q8_0, Q4_0: unpack_q4_0, LUT3: unpack_lut3, FP8: unpack_fp8}[fmt]
+    fn = {Q8_0: unpack_q8_0, Q4_0: unpack_q4_0, LUT3: unpack_lut3, FP8: unpack_fp8, LUT3_WHT: unpack_lut3_wht}[fmt]
     return fn(c2, s2, dim).reshape(lead + (dim,))
