@@ -247,7 +247,7 @@ def unpack_lut3(codes, scales, dim=128):
 # float64 as the butterfly network below, then LUT3 of y. The transform is its
 # own inverse, so a decoded row is H LUT3^-1(codes) / sqrt(128).
 
-WHT_SCALE = 1.0 / math.sqrt(128.0)           # float64, one rounding
+WHT_SCALE = float("0.08838834764831844055010554526310613")   # the float64 nearest 1/sqrt(128)
 
 
 def fwht(x64: np.ndarray) -> np.ndarray:
