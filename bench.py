@@ -304,7 +304,7 @@ def main():
                     help="which threshold(s) to time (a profiler run can restrict to one)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy 5 times (reference for HBM byte counters)")
-    ap.add_argument("--workload", choices=["long", "tiny", "sweep", "lut3", "mla", "stress", "append"],
+    ap.add_argument("--workload", choices=["long", "tiny", "sweep", "lut3", "lut3_wht", "mla", "stress", "append"],
                     default="long",
                     help="long (default) prints the metric line; the others print one line per "
                          "configuration (sweep: one per context length)")

@@ -14,11 +14,11 @@ import numpy as np
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
 
-KVQ_Q8_0, KVQ_Q4_0, KVQ_LUT3, KVQ_FP8_B128 = 0, 1, 2, 3
+KVQ_Q8_0, KVQ_Q4_0, KVQ_LUT3, KVQ_FP8_B128, KVQ_LUT3_WHT = 0, 1, 2, 3, 4
 KVQ_Q_F32, KVQ_Q_BF16 = 0, 1
 KVQ_LAUNCH_COOPERATIVE = 1
 KVQ_SKIP_RUNNING = 2
-FMT = {"q8_0": KVQ_Q8_0, "q4_0": KVQ_Q4_0, "lut3": KVQ_LUT3, "fp8_b128": KVQ_FP8_B128}
+FMT = {"q8_0": KVQ_Q8_0, "q4_0": KVQ_Q4_0, "lut3": KVQ_LUT3, "fp8_b128": KVQ_FP8_B128, "lut3_wht": KVQ_LUT3_WHT}
 
 ERRORS = {0: "OK", -1: "ARG", -2: "ALIGN", -3: "RANGE", -4: "NONFINITE", -5: "WORKSPACE",
           -6: "LAUNCH", -7: "UNSUPPORTED", -8: "DEVICE"}

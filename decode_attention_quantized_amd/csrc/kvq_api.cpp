@@ -58,7 +58,9 @@ struct Plan {
   int64_t total = 0;
 };
 
-bool is_gqa_fmt(int fmt) { return fmt == KVQ_Q8_0 || fmt == KVQ_Q4_0 || fmt == KVQ_LUT3; }
+bool is_gqa_fmt(int fmt) {
+  return fmt == KVQ_Q8_0 || fmt == KVQ_Q4_0 || fmt == KVQ_LUT3 || fmt == KVQ_LUT3_WHT;
+}
 
 // MLA shape: H query heads over one 576-wide fp8 latent per sequence, values =
 // the first 512 dims, bf16 queries. One 4-wave workgroup per CU by default.
@@ -104,7 +106,7 @@ int32_t make_mla_plan(const kvq_cache* k, const kvq_launch* l, int32_t ctx_len, 
 // Validate shapes shared by every entry point and pick splits.
 int32_t make_plan(int32_t fmt, const kvq_cache* k, const kvq_launch* l, int32_t ctx_len, Plan* plan) {
   if (!k || !l || !plan) return KVQ_ERR_ARG;
-  if (fmt < KVQ_Q8_0 || fmt > KVQ_FP8_B128) return KVQ_ERR_ARG;
+  if (fmt < KVQ_Q8_0 || fmt > KVQ_LUT3_WHT) return KVQ_ERR_ARG;
   if (k->batch <= 0 || k->heads <= 0 || k->dim <= 0 || k->capacity <= 0) return KVQ_ERR_ARG;
   if (l->q_heads <= 0 || l->q_heads % k->heads) return KVQ_ERR_ARG;
   if (l->q_dtype != KVQ_Q_F32 && l->q_dtype != KVQ_Q_BF16) return KVQ_ERR_ARG;

@@ -193,12 +193,33 @@ __device__ void fp8_row(const Row& r) {
     for (int g0 = 0; g0 < r.dim; g0 += 8 * 128) fp8_groups<8>(r, g0);
 }
 
+// The Walsh-Hadamard rotation of kvq_formats.h's wht128 on a row held as
+// elements (lane, lane + 64): the same butterflies in the same stage order
+// (stages h < 64 pair lanes l and l ^ h, stage 64 the two elements of a
+// lane), each one float64 addition, then the one multiply.
+__device__ inline void wht_lanes(int lane, double& v0, double& v1) {
+  for (int h = 1; h < 64; h *= 2) {
+    const double p0 = __shfl_xor(v0, h), p1 = __shfl_xor(v1, h);
+    const bool upper = lane & h;
+    v0 = upper ? p0 - v0 : v0 + p0;
+    v1 = upper ? p1 - v1 : v1 + p1;
+  }
+  const double a = v0, b = v1;
+  v0 = a + b;
+  v1 = a - b;
+  v0 = v0 * kWhtScale;
+  v1 = v1 * kWhtScale;
+}
+
 // LUT3 (128-wide rows): norm from the sequential float64 sum of squares,
 // magnitude indices against the level midpoints, and the row scalar that
 // keeps the decoded norm; one pass, written only when the scalar fits fp16.
+// ROTATE: LUT3_WHT, the row is rotated first (and stays float64).
 // `sq` is this wave's 128 doubles of LDS, `cb` its 128 bytes.
+template <bool ROTATE>
 __device__ int lut3_row(const Row& r, double* sq, uint8_t* cb) {
-  const double v0 = r.x[r.lane], v1 = r.x[r.lane + 64];
+  double v0 = r.x[r.lane], v1 = r.x[r.lane + 64];
+  if (ROTATE) wht_lanes(r.lane, v0, v1);
   sq[r.lane] = v0 * v0;
   sq[r.lane + 64] = v1 * v1;
   wave_lds_order();
@@ -267,7 +288,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void append_rows(int32_t fmt, 
       switch (fmt) {
         case KVQ_Q8_0: e = q_row_any<KVQ_Q8_0>(r); break;
         case KVQ_Q4_0: e = q_row_any<KVQ_Q4_0>(r); break;
-        case KVQ_LUT3: e = lut3_row(r, sq[wave], cbuf[wave]); break;
+        case KVQ_LUT3: e = lut3_row<false>(r, sq[wave], cbuf[wave]); break;
+        case KVQ_LUT3_WHT: e = lut3_row<true>(r, sq[wave], cbuf[wave]); break;
         case KVQ_FP8_B128: fp8_row(r); break;
       }
       err |= e;

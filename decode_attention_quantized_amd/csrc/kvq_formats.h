@@ -129,6 +129,24 @@ KVQ_HD inline int lut3_index(double v, double r) {
   return idx;
 }
 
+// y = H x / sqrt(128) for a 128-wide row, H the Sylvester Hadamard matrix
+// (H[i][j] = (-1)^popcount(i & j)): butterflies (a, b) -> (a + b, a - b) for
+// h = 1, 2, ..., 64 over pairs (j, j + h) with j mod 2h < h, each one float64
+// addition, then one multiply by the float64 value of 1/sqrt(128). The
+// transform is its own inverse.
+constexpr double kWhtScale = 0.088388347648318440550;      // 1/sqrt(128), correctly rounded
+
+KVQ_HD inline void wht128(double* y) {
+  for (int h = 1; h < 128; h *= 2)
+    for (int j0 = 0; j0 < 128; j0 += 2 * h)
+      for (int j = j0; j < j0 + h; ++j) {
+        const double a = y[j], b = y[j + h];
+        y[j] = a + b;
+        y[j + h] = a - b;
+      }
+  for (int i = 0; i < 128; ++i) y[i] = y[i] * kWhtScale;
+}
+
 }  // namespace fmt
 }  // namespace kvq
 

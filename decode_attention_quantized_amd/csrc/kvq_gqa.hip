@@ -376,6 +376,26 @@ template <> struct Traits<KVQ_LUT3> {
   }
 };
 
+// LUT3 of Walsh-Hadamard-rotated rows: the stored rows decode as LUT3; the
+// kernel rotates q once (scores are inner products, and the rotation is
+// orthonormal and symmetric) and each workgroup's partial output once.
+template <> struct Traits<KVQ_LUT3_WHT> : Traits<KVQ_LUT3> {};
+
+// y = H x / sqrt(128) in float32 on a 128-vector held as elements (lane,
+// lane + 64) of a wave (H the Sylvester Hadamard matrix, as the packers)
+__device__ inline void wht_wave(int lane, float& v0, float& v1) {
+#pragma unroll
+  for (int h = 1; h < 64; h *= 2) {
+    const float p0 = __shfl_xor(v0, h), p1 = __shfl_xor(v1, h);
+    const bool upper = lane & h;
+    v0 = upper ? p0 - v0 : v0 + p0;
+    v1 = upper ? p1 - v1 : v1 + p1;
+  }
+  const float a = v0, b = v1;
+  v0 = (a + b) * 0.08838834764831845f;
+  v1 = (a - b) * 0.08838834764831845f;
+}
+
 template <class T, bool kStaged> struct LoadedOf { using type = typename T::Raw; };
 template <class T> struct LoadedOf<T, true> { using type = typename T::Raw16; };
 
@@ -395,6 +415,7 @@ template <class T> struct LoadedOf<T, true> { using type = typename T::Raw16; };
 template <int FMT, int G, bool RUN>
 __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   using T = Traits<FMT>;
+  constexpr bool kRot = FMT == KVQ_LUT3_WHT;           // rotate q in, partial outputs out
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
   extern __shared__ __align__(16) unsigned char smem[];
   // LDS: scores [G][P] (then kept weights in place; then the cross-wave
@@ -439,7 +460,7 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
 
   const int n16 = lane & 15;     // MFMA column (position within a tile)
   const int kg = lane >> 4;      // lane group
-  const uint32_t table = (FMT == KVQ_LUT3) ? lut3_pair_entry(lane) : 0u;
+  const uint32_t table = (FMT == KVQ_LUT3 || FMT == KVQ_LUT3_WHT) ? lut3_pair_entry(lane) : 0u;
   // issue the first K tiles before the q set-up so their latency overlaps it
   const int ntiles = P / 16;
   constexpr int U = 4;
@@ -502,6 +523,23 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
       } else {                                         // one 16-byte load
         const float4 r = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.q) + qoff);
         qv[0] = r.x; qv[1] = r.y; qv[2] = r.z; qv[3] = r.w;
+      }
+      if constexpr (kRot) {
+        // q' = H q / sqrt(128): dims 4ln + e; stages 1 and 2 inside the
+        // thread, stages 4..64 with the thread ln ^ (h / 4) of the same head
+        float t0 = qv[0] + qv[1], t1 = qv[0] - qv[1], t2 = qv[2] + qv[3], t3 = qv[2] - qv[3];
+        qv[0] = t0 + t2; qv[1] = t1 + t3; qv[2] = t0 - t2; qv[3] = t1 - t3;
+#pragma unroll
+        for (int hh = 1; hh < 32; hh *= 2) {
+          const bool upper = ln & hh;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p = __shfl_xor(qv[e], hh, 32);
+            qv[e] = upper ? p - qv[e] : qv[e] + p;
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qv[e] *= 0.08838834764831845f;
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(qv[e]));
@@ -887,11 +925,29 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
       }
     }
     __syncthreads();
-    for (int i = tid; i < G * 128; i += kThreads) {
-      float s = 0.f;
-      for (int k = 0; k < nact; ++k) s += red[k * G * 128 + i];
-      if constexpr (RUN) s *= fac[i >> 7];
-      put_tagged_f(a.partial + pbase * G * 128 + i, epoch, s);
+    if constexpr (kRot) {
+      // the summed partial of every head is rotated back by one wave
+      float* rot = reinterpret_cast<float*>(qop);    // [G][128] (the q operands are in registers)
+      for (int i = tid; i < G * 128; i += kThreads) {
+        float s = 0.f;
+        for (int k = 0; k < nact; ++k) s += red[k * G * 128 + i];
+        if constexpr (RUN) s *= fac[i >> 7];
+        rot[i] = s;
+      }
+      __syncthreads();
+      if (wave < G) {
+        float v0 = rot[wave * 128 + lane], v1 = rot[wave * 128 + 64 + lane];
+        wht_wave(lane, v0, v1);
+        put_tagged_f(a.partial + pbase * G * 128 + wave * 128 + lane, epoch, v0);
+        put_tagged_f(a.partial + pbase * G * 128 + wave * 128 + 64 + lane, epoch, v1);
+      }
+    } else {
+      for (int i = tid; i < G * 128; i += kThreads) {
+        float s = 0.f;
+        for (int k = 0; k < nact; ++k) s += red[k * G * 128 + i];
+        if constexpr (RUN) s *= fac[i >> 7];
+        put_tagged_f(a.partial + pbase * G * 128 + i, epoch, s);
+      }
     }
     if (tid < G) {
       float s = 0.f;
@@ -1015,7 +1071,7 @@ size_t gqa_lds_bytes(int fmt, int G, int P, int S) {
   const size_t list_cap = 32 * ((P / kChunk + kWaves / 2 - 1) / (kWaves / 2));
   const size_t pitch = fmt == KVQ_Q4_0 ? Traits<KVQ_Q4_0>::PITCH
                      : fmt == KVQ_Q8_0 ? Traits<KVQ_Q8_0>::PITCH
-                                       : Traits<KVQ_LUT3>::PITCH;
+                                       : Traits<KVQ_LUT3>::PITCH;     // LUT3 and LUT3_WHT
   return sc * 4 + 16 * 128 * 2 + 64 * 4 + 3 * 8 * 4 + 2 * kWaves * 4 + size_t(kWaves) * G * 4 +
          size_t(kWaves) * 8 * 8 + (kWaves + 4) * 4 + size_t(P / kChunk) * 8 + size_t(kWaves) * list_cap * 2 + 16 +
          size_t(kWaves) * 16 * pitch + 64;
@@ -1029,6 +1085,7 @@ const void* gqa_kernel(int fmt, int G, bool run) {
   KVQ_SEL(KVQ_Q4_0, 1) KVQ_SEL(KVQ_Q4_0, 2) KVQ_SEL(KVQ_Q4_0, 4) KVQ_SEL(KVQ_Q4_0, 8)
   KVQ_SEL(KVQ_Q8_0, 1) KVQ_SEL(KVQ_Q8_0, 2) KVQ_SEL(KVQ_Q8_0, 4) KVQ_SEL(KVQ_Q8_0, 8)
   KVQ_SEL(KVQ_LUT3, 1) KVQ_SEL(KVQ_LUT3, 2) KVQ_SEL(KVQ_LUT3, 4) KVQ_SEL(KVQ_LUT3, 8)
+  KVQ_SEL(KVQ_LUT3_WHT, 1) KVQ_SEL(KVQ_LUT3_WHT, 2) KVQ_SEL(KVQ_LUT3_WHT, 4) KVQ_SEL(KVQ_LUT3_WHT, 8)
 #undef KVQ_SEL
   return nullptr;
 }

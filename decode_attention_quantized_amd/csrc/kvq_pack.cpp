@@ -64,7 +64,9 @@ int32_t pack_q4_0(const float* x, int32_t dim, uint8_t* codes, uint8_t* scales) 
   return KVQ_OK;
 }
 
-int32_t pack_lut3(const float* x, uint8_t* codes, uint8_t* scales) {
+// LUT3 of a float64 row (the input row widened, or the rotated row of
+// LUT3-WHT, which stays float64)
+int32_t pack_lut3_f64(const double* x, uint8_t* codes, uint8_t* scales) {
   double M[4];
   for (int k = 0; k < 4; ++k) M[k] = f16_to_f64(kLut3Bits[k]);
   double ss = 0.0;
@@ -87,6 +89,13 @@ int32_t pack_lut3(const float* x, uint8_t* codes, uint8_t* scales) {
   if ((nu & 0x7C00u) == 0x7C00u) return KVQ_ERR_RANGE;
   put_u16(scales, nu);
   return KVQ_OK;
+}
+
+int32_t pack_lut3(const float* x, uint8_t* codes, uint8_t* scales, bool rotate) {
+  double y[128];
+  for (int i = 0; i < 128; ++i) y[i] = x[i];
+  if (rotate) wht128(y);
+  return pack_lut3_f64(y, codes, scales);
 }
 
 int32_t pack_fp8(const float* x, int32_t dim, uint8_t* codes, uint8_t* scales) {
@@ -114,6 +123,7 @@ extern "C" int32_t kvq_row_bytes(int32_t fmt, int32_t dim, int64_t* code_bytes, 
       if (dim <= 0 || dim % 32) return KVQ_ERR_UNSUPPORTED;
       *code_bytes = dim / 2; *scale_bytes = 2 * (dim / 32); return KVQ_OK;
     case KVQ_LUT3:
+    case KVQ_LUT3_WHT:
       if (dim != 128) return KVQ_ERR_UNSUPPORTED;
       *code_bytes = 48; *scale_bytes = 2; return KVQ_OK;
     case KVQ_FP8_B128:
@@ -142,7 +152,8 @@ extern "C" int32_t kvq_pack(int32_t fmt, const float* src, int64_t n_rows, int32
     switch (fmt) {
       case KVQ_Q8_0: e = pack_q8_0(x, dim, c, s); break;
       case KVQ_Q4_0: e = pack_q4_0(x, dim, c, s); break;
-      case KVQ_LUT3: e = pack_lut3(x, c, s); break;
+      case KVQ_LUT3: e = pack_lut3(x, c, s, false); break;
+      case KVQ_LUT3_WHT: e = pack_lut3(x, c, s, true); break;
       case KVQ_FP8_B128: e = pack_fp8(x, dim, c, s); break;
     }
     if (e) return e;
@@ -174,16 +185,20 @@ extern "C" int32_t kvq_unpack(int32_t fmt, const uint8_t* codes, const uint8_t* 
           y[i] = static_cast<float>((code - 8) * f16_to_f64(get_u16(s + 2 * (i / 32))));
         }
         break;
-      case KVQ_LUT3: {
+      case KVQ_LUT3:
+      case KVQ_LUT3_WHT: {
         const double nu = f16_to_f64(get_u16(s));
+        double t[128];
         for (int i = 0; i < 128; ++i) {
           unsigned code = 0;
           for (int k = 0; k < 3; ++k) code |= ((c[(3 * i + k) / 8] >> ((3 * i + k) % 8)) & 1u) << k;
           const int idx = code & 3;
           const bool neg = (code >> 2) & 1;
           const double m = f16_to_f64(kLut3Bits[idx]);
-          y[i] = static_cast<float>((nu * (neg ? -m : m)) / std::sqrt(128.0));
+          t[i] = (nu * (neg ? -m : m)) / std::sqrt(128.0);
         }
+        if (fmt == KVQ_LUT3_WHT) wht128(t);           // the rotation is its own inverse
+        for (int i = 0; i < 128; ++i) y[i] = static_cast<float>(t[i]);
         break;
       }
       case KVQ_FP8_B128:

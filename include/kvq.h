@@ -60,6 +60,15 @@ extern "C" {
  *             Row: 48 B = the 128 codes as one little-endian 384-bit string,
  *             element i at bits 3i..3i+2 (code = sign << 2 | index); scale
  *             plane: nu (fp16).
+ * KVQ_LUT3_WHT ([SV] "Почему это работает для любой квантизации": turbo3
+ *             rotates rows with a Walsh-Hadamard transform). LUT3 of
+ *             y = H x / sqrt(128), H the 128x128 Sylvester Hadamard matrix
+ *             (H[i][j] = (-1)^popcount(i & j)), computed in float64 as the
+ *             butterflies (a, b) -> (a + b, a - b) for h = 1, 2, ..., 64 over
+ *             pairs (j, j + h), j mod 2h < h, then one multiply by the float64
+ *             nearest 1/sqrt(128); y is not rounded to float32 before LUT3.
+ *             Decoding rotates the LUT3 value back with the same transform.
+ *             Same row bytes as KVQ_LUT3.
  * KVQ_FP8_B128 ([MLA] BlockWise1x128). Groups of 128 along the row (the last
  *             may be shorter): s = fp32(max|x|/448); code =
  *             e4m3fn(clamp(x/s, -448, 448)) (OCP E4M3, nearest-even);
@@ -70,7 +79,8 @@ enum {
   KVQ_Q8_0 = 0,
   KVQ_Q4_0 = 1,
   KVQ_LUT3 = 2,
-  KVQ_FP8_B128 = 3
+  KVQ_FP8_B128 = 3,
+  KVQ_LUT3_WHT = 4
 };
 
 /* query element types */
@@ -92,7 +102,7 @@ enum {
 /* Bytes per packed row of `dim` elements for `fmt`.
  * code_bytes/scale_bytes: host out-pointers. Errors: ARG (bad fmt, null),
  * UNSUPPORTED (dim not allowed for fmt: q8_0/q4_0 need dim % 32 == 0, LUT3
- * needs dim == 128, FP8 needs 1 <= dim). */
+ * and LUT3_WHT need dim == 128, FP8 needs 1 <= dim). */
 int32_t kvq_row_bytes(int32_t fmt, int32_t dim, int64_t* code_bytes, int64_t* scale_bytes);
 
 /* Pack n_rows float32 rows of `dim` elements (host `src`, row-major) into the

@@ -18,6 +18,8 @@ than 90% of weights fall below 1e-6):
 - ``sweep_<n>`` ``long`` at ctx n in {4096, ..., 65536}, 16*log2(n/1024) hot.
 - ``lut3``      3-bit LUT codebook, batch 8, 32/4 heads, ctx 32768, sequence b
                 has 8*(b+1) hot positions per KV head.
+- ``lut3_wht``  ``lut3`` (same seed, so the same arrays) stored as the
+                Walsh-Hadamard-rotated LUT3 format.
 - ``mla``       128 query heads over one 576-wide latent (512 value dims + 64 rope),
                 fp8 e4m3 blocks of 128, bf16 queries, ctx 65536, batch 8, 96 hot
                 positions per sequence shared by all heads, softmax scale 1/sqrt(192)
@@ -40,6 +42,7 @@ import numpy as np
 FMT_Q8_0 = "q8_0"
 FMT_Q4_0 = "q4_0"
 FMT_LUT3 = "lut3"
+FMT_LUT3_WHT = "lut3_wht"
 FMT_FP8 = "fp8_b128"
 
 THRESHOLD = 1e-6
@@ -87,6 +90,9 @@ def workload(name: str) -> Workload:
     if name == "lut3":
         return Workload(name, FMT_LUT3, 8, 32, 4, 128, 128, 32768, 4, _f32(1 / math.sqrt(128)),
                         hot=lambda b: 8 * (b + 1))
+    if name == "lut3_wht":
+        return Workload(name, FMT_LUT3_WHT, 8, 32, 4, 128, 128, 32768, 4, _f32(1 / math.sqrt(128)),
+                        hot=lambda b: 8 * (b + 1))
     if name == "mla":
         return Workload(name, FMT_FP8, 8, 128, 1, 576, 512, 65536, 5, _f32(1 / math.sqrt(192)),
                         q_bf16=True, hot=96)
@@ -97,7 +103,7 @@ def workload(name: str) -> Workload:
 
 
 SWEEP = [4096, 8192, 16384, 32768, 65536]
-ALL = ["tiny", "long"] + [f"sweep_{n}" for n in SWEEP] + ["lut3", "mla", "stress"]
+ALL = ["tiny", "long"] + [f"sweep_{n}" for n in SWEEP] + ["lut3", "lut3_wht", "mla", "stress"]
 
 
 def resized(w: Workload, *, batch=None, q_heads=None, kv_heads=None, ctx=None, hot=None,

@@ -16,7 +16,8 @@ from oracle import formats as F
 pytestmark = pytest.mark.gpu
 
 FMTS = [("q8_0", 128), ("q4_0", 128), ("lut3", 128), ("fp8_b128", 576), ("q8_0", 64), ("q4_0", 256),
-        ("fp8_b128", 200), ("q8_0", 96), ("q4_0", 320), ("q8_0", 1088), ("fp8_b128", 1500), ("fp8_b128", 384)]
+        ("fp8_b128", 200), ("q8_0", 96), ("q4_0", 320), ("q8_0", 1088), ("fp8_b128", 1500), ("fp8_b128", 384),
+        ("lut3_wht", 128)]
 
 
 def _rows(fmt, dim, n, seed):
@@ -58,8 +59,6 @@ def _device_pack(fmt, x, dst=None, cache_rows=None, fill=0):
 
 @pytest.mark.parametrize("fmt,dim", FMTS)
 def test_append_bit_exact_against_oracle(fmt, dim):
-    if fmt == "lut3" and dim != 128:
-        pytest.skip("lut3 rows are 128 wide")
     say("case append", fmt, dim)
     x = _rows(fmt, dim, 6000, zlib.crc32(f"append/{fmt}/{dim}".encode()))
     c, s, st = _device_pack(fmt, x)
@@ -80,7 +79,7 @@ def test_append_every_fp8_code():
     assert len(set(c.ravel().tolist())) == 254
 
 
-@pytest.mark.parametrize("fmt,dim", [("q4_0", 128), ("lut3", 128), ("fp8_b128", 576)])
+@pytest.mark.parametrize("fmt,dim", [("q4_0", 128), ("lut3", 128), ("fp8_b128", 576), ("lut3_wht", 128)])
 def test_append_scatter_leaves_other_rows(fmt, dim):
     say("case append scatter", fmt)
     rng = np.random.default_rng(7)

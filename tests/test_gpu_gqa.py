@@ -124,27 +124,30 @@ def test_sweep_lengths():
         compare(inp, tau, g, r, po)
 
 
+@pytest.mark.parametrize("name", ["lut3", "lut3_wht"])
 @pytest.mark.parametrize("threshold", [1e-6, 0.0])
-def test_lut3_small(threshold):
-    say("case lut3 batch 2 ctx 3000 tau", threshold)
-    inp, tau = _case("lut3", threshold, batch=2, ctx=3000)
+def test_lut3_small(threshold, name):
+    say("case", name, "batch 2 ctx 3000 tau", threshold)
+    inp, tau = _case(name, threshold, batch=2, ctx=3000)
     g = run_gpu(inp, tau)
     r, po = oracle_for(inp, tau)
     compare(inp, tau, g, r, po)
 
 
+@pytest.mark.parametrize("name", ["lut3", "lut3_wht"])
 @pytest.mark.parametrize("ctx", [1, 77, 4100])
-def test_lut3_ragged(ctx):
-    say("case lut3 ragged ctx", ctx)
-    inp, tau = _case("lut3", batch=1, ctx=ctx)
+def test_lut3_ragged(ctx, name):
+    say("case", name, "ragged ctx", ctx)
+    inp, tau = _case(name, batch=1, ctx=ctx)
     g = run_gpu(inp, tau)
     r, po = oracle_for(inp, tau)
     compare(inp, tau, g, r, po)
 
 
-def test_lut3_full_size():
-    say("case lut3 batch 8, 32/4 heads, ctx 32768, 8..64 hot per sequence")
-    inp, tau = _case("lut3")
+@pytest.mark.parametrize("name", ["lut3", "lut3_wht"])
+def test_lut3_full_size(name):
+    say("case", name, "batch 8, 32/4 heads, ctx 32768, 8..64 hot per sequence")
+    inp, tau = _case(name)
     g = run_gpu(inp, tau)
     r, po = oracle_for(inp, tau)
     compare(inp, tau, g, r, po)

@@ -8,7 +8,7 @@ import pytest
 import decode_attention_quantized_amd as kvq
 from oracle import formats as F
 
-FMTS = [("q8_0", 128), ("q4_0", 128), ("lut3", 128), ("fp8_b128", 576), ("q8_0", 64), ("q4_0", 256),
+FMTS = [("q8_0", 128), ("q4_0", 128), ("lut3", 128), ("fp8_b128", 576), ("q8_0", 64), ("q4_0", 256), ("lut3_wht", 128),
         ("fp8_b128", 128), ("fp8_b128", 200)]
 
 
