@@ -74,6 +74,38 @@ __device__ inline float sum_wave(float v) {
   return (v + r1) + (r2 + r3);
 }
 
+// lse_merge over the lanes of equal lane mod C (C = 1, 2, 4 or 8): rotations
+// by C, 2C, .. 8 inside each 16-lane row, then the two rows of each half and
+// the two halves, each in one fixed order, so every lane of a class holds the
+// same bits.
+template <int O>
+__device__ inline float2 row_ror(float2 v) { return dpp2<0x120 + O>(v); }
+__device__ inline float2 swap16(float2 v) {
+  const auto x = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v.x), __builtin_bit_cast(unsigned, v.x),
+                                                  false, false);
+  const auto y = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v.y), __builtin_bit_cast(unsigned, v.y),
+                                                  false, false);
+  return lse_merge(make_float2(__builtin_bit_cast(float, unsigned(x[0])), __builtin_bit_cast(float, unsigned(y[0]))),
+                   make_float2(__builtin_bit_cast(float, unsigned(x[1])), __builtin_bit_cast(float, unsigned(y[1]))));
+}
+__device__ inline float2 swap32(float2 v) {
+  const auto x = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v.x), __builtin_bit_cast(unsigned, v.x),
+                                                  false, false);
+  const auto y = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v.y), __builtin_bit_cast(unsigned, v.y),
+                                                  false, false);
+  return lse_merge(make_float2(__builtin_bit_cast(float, unsigned(x[0])), __builtin_bit_cast(float, unsigned(y[0]))),
+                   make_float2(__builtin_bit_cast(float, unsigned(x[1])), __builtin_bit_cast(float, unsigned(y[1]))));
+}
+template <int C>
+__device__ inline float2 merge_class(float2 v) {
+  if constexpr (C <= 1) v = lse_merge(v, row_ror<1>(v));
+  if constexpr (C <= 2) v = lse_merge(v, row_ror<2>(v));
+  if constexpr (C <= 4) v = lse_merge(v, row_ror<4>(v));
+  v = lse_merge(v, row_ror<8>(v));
+  v = swap16(v);
+  return swap32(v);
+}
+
 // lse_merge over the 16 lanes of each row of the wave (quad neighbours, the
 // other pair of the quad, mirrored quads, mirrored half rows); lane 0 of the
 // row holds the merge of all 16.
@@ -155,6 +187,50 @@ __device__ inline void settle_all(u64 (&w)[N], const u64* const (&p)[N], const b
       __hip_atomic_fetch_or(&h->status, kStatusWaitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return;
     }
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+      if (use[k] && uint32_t(w[k] >> 32) != epoch) w[k] = peek(p[k]);
+  }
+}
+
+// Two adjacent tagged words read by one 16-byte buffer load with the same
+// agent-coherent cache policy as peek() (sc1). Each naturally aligned 8-byte
+// word of it is read as a unit (the load is served from one cache line), so
+// a word's tag still vouches for its payload. Threads that take consecutive
+// 16-byte pieces make a wave read whole lines: polling a group's words costs
+// one request per line instead of one per word.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kCoherentLoad = 16;                    // buffer cache policy: sc1
+__device__ inline __amdgpu_buffer_rsrc_t coherent_rsrc(const u64* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<u64*>(base), 0, bytes, 0x00020000);
+}
+__device__ inline u32x4 peek2(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherentLoad);
+}
+__device__ inline bool stale2(const u32x4& v, uint32_t epoch) { return v.y != epoch || v.w != epoch; }
+
+// settle_all for M peeked pairs of words (16-byte loads at byte offsets
+// off[] of r) plus N single words.
+template <int M, int N>
+__device__ inline void settle_mixed(u32x4 (&v)[M], const bool (&use_v)[M], __amdgpu_buffer_rsrc_t r,
+                                    const int (&off)[M], u64 (&w)[N], const u64* const (&p)[N], const bool (&use)[N],
+                                    uint32_t epoch, WsHeader* h) {
+  uint32_t spins = 0;
+  while (true) {
+    bool stale = false;
+#pragma unroll
+    for (int k = 0; k < M; ++k) stale |= use_v[k] && stale2(v[k], epoch);
+#pragma unroll
+    for (int k = 0; k < N; ++k) stale |= use[k] && uint32_t(w[k] >> 32) != epoch;
+    if (!stale) return;
+    __builtin_amdgcn_s_sleep(1);
+    if (++spins > kSpinLimit) {
+      __hip_atomic_fetch_or(&h->status, kStatusWaitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+#pragma unroll
+    for (int k = 0; k < M; ++k)
+      if (use_v[k] && stale2(v[k], epoch)) v[k] = peek2(r, off[k]);
 #pragma unroll
     for (int k = 0; k < N; ++k)
       if (use[k] && uint32_t(w[k] >> 32) != epoch) w[k] = peek(p[k]);
@@ -680,47 +756,42 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   // them itself (128 threads per head, fixed pattern, so every workgroup of
   // the group computes the same bits); no workgroup waits on another's LSE.
   auto gather_lse = [&](float* dst) {
-    {
-      float2 acc = make_float2(-INFINITY, 0.f);
-      const int j = tid >> 7, ln = tid & 127;
-      if (j < G) {
-        for (int s0 = ln; s0 < a.S; s0 += 4 * 128) {
-          u64 w[8];
-          const u64* src[8];
-          bool use[8];
+    // The group's S*G (max, sum) pairs are contiguous 16-byte pieces (split
+    // sp, head j at piece sp*G + j). Thread t takes pieces t and t + kThreads
+    // (S*G <= 2048: at most 256 splits of at most 8 heads), both of head
+    // t mod G; a wave merges its lanes of equal head with xor steps, the
+    // waves' results are merged in wave order. The pattern is fixed, so every
+    // workgroup of the group computes the same bits.
+    const int nc = a.S * G;
+    const __amdgpu_buffer_rsrc_t r = coherent_rsrc(a.split_ml + int64_t(bg) * nc * 2, nc * 16);
+    u32x4 v[2];
+    bool use[2];
+    int off[2];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int sp = s0 + 128 * u;
-            src[2 * u] = a.split_ml + ((int64_t(bg) * a.S + (sp < a.S ? sp : 0)) * G + j) * 2;
-            src[2 * u + 1] = src[2 * u] + 1;
-            use[2 * u] = use[2 * u + 1] = sp < a.S;
-            w[2 * u] = use[2 * u] ? peek(src[2 * u]) : 0ull;
-            w[2 * u + 1] = use[2 * u] ? peek(src[2 * u + 1]) : 0ull;
-          }
-          settle_all(w, src, use, epoch, a.hdr);
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (use[2 * u]) acc = lse_merge(acc, make_float2(__uint_as_float(uint32_t(w[2 * u])),
-                                                             __uint_as_float(uint32_t(w[2 * u + 1]))));
-        }
-        acc = merge_row16(acc);                        // lane 16r holds row r's merge
-        float2 row[3];                                 // rows 1..3, read before any merging
-#pragma unroll
-        for (int r = 1; r < 4; ++r) {
-          row[r - 1].x = __shfl(acc.x, 16 * r);
-          row[r - 1].y = __shfl(acc.y, 16 * r);
-        }
-#pragma unroll
-        for (int r = 0; r < 3; ++r) acc = lse_merge(acc, row[r]);
-        if (lane == 0) wml[wave] = acc;                 // two waves per head
-      }
-      __syncthreads();
-      if (tid < G) {
-        const float2 v = lse_merge(wml[2 * tid], wml[2 * tid + 1]);
-        dst[tid] = v.x + log2f(v.y);
-      }
-      __syncthreads();
+    for (int k = 0; k < 2; ++k) {
+      const int c = tid + k * kThreads;
+      use[k] = c < nc;
+      off[k] = use[k] ? c * 16 : 0;
+      v[k] = use[k] ? peek2(r, off[k]) : u32x4{0u, epoch, 0u, epoch};
     }
+    u64 none[1] = {0ull};
+    const u64* const nop[1] = {a.split_ml};
+    const bool nouse[1] = {false};
+    settle_mixed(v, use, r, off, none, nop, nouse, epoch, a.hdr);
+    float2 acc = make_float2(-INFINITY, 0.f);
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      if (use[k]) acc = lse_merge(acc, make_float2(__uint_as_float(v[k].x), __uint_as_float(v[k].z)));
+    acc = merge_class<G>(acc);                       // every lane: its head's merge over the wave
+    if (lane < G) wml[wave * 8 + lane] = acc;
+    __syncthreads();
+    if (tid < 128) {                                 // row j of 16 lanes merges head j over the waves
+      const int j = tid >> 4, w = tid & 15;
+      float2 m = (j < G) ? wml[w * 8 + j] : make_float2(-INFINITY, 0.f);
+      m = merge_row16(m);
+      if (w == 0 && j < G) dst[j] = m.x + log2f(m.y);
+    }
+    __syncthreads();
   };
   const int nch = P / kChunk;                        // 64-position blocks of the split
   // single-pass rule: running LSE per (head, block) [G][nch] after block
@@ -970,7 +1041,7 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   {
     constexpr int NE = G * 128;
     const int S = a.S;
-    const int E = (NE + S - 1) / S;
+    const int E = gqa_merge_slice(G, S);
     const int e0 = split * E;
     const int ne = e0 < NE ? (NE - e0 < E ? NE - e0 : E) : 0;
     const int nh = split < G ? (G - split + S - 1) / S : 0;
@@ -980,25 +1051,28 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     uint32_t* fl = reinterpret_cast<uint32_t*>(pm + nh * S);   // [S] (split 0)
     const int64_t gb = int64_t(bg) * S;
     __syncthreads();                                 // sc is free again
-    constexpr int NW = 3 + 2 + 2;                    // partial, mass and flag words per thread
+    // partials: 16-byte pieces (two words); consecutive threads take the
+    // pieces of one split's slice, so a wave reads whole lines
+    const int hc = ne >> 1;                          // pieces per split (ne is even)
+    const bool use_p = tid < hc * S;
+    const int sp_p = use_p ? tid / (hc > 0 ? hc : 1) : 0;
+    const int k_p = use_p ? tid - sp_p * hc : 0;
+    const __amdgpu_buffer_rsrc_t rp = coherent_rsrc(a.partial + gb * NE, S * NE * 8);
+    const int poff[1] = {(sp_p * NE + e0 + 2 * k_p) * 8};
+    const bool puse[1] = {use_p};
+    u32x4 pw[1] = {use_p ? peek2(rp, poff[0]) : u32x4{0u, epoch, 0u, epoch}};
+    constexpr int NW = 2 + 2;                        // mass and flag words per thread
     u64 w[NW];
     const u64* src[NW];
     bool use[NW];
 #pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      const int i = tid + k * kThreads;
-      use[k] = i < ne * S;
-      const int e = e0 + (use[k] ? i / S : 0), sp = use[k] ? i % S : 0;
-      src[k] = a.partial + (gb + sp) * NE + (use[k] ? e : 0);
-    }
-#pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int i = tid + k * kThreads;
-      use[3 + k] = i < nh * S;
-      const int j = use[3 + k] ? split + (i / S) * S : 0, sp = use[3 + k] ? i % S : 0;
-      src[3 + k] = a.pmass + (gb + sp) * G + j;
-      use[5 + k] = i < nf;
-      src[5 + k] = a.flags + gb + (use[5 + k] ? i : 0);
+      use[k] = i < nh * S;
+      const int j = use[k] ? split + (i / S) * S : 0, sp = use[k] ? i % S : 0;
+      src[k] = a.pmass + (gb + sp) * G + j;
+      use[2 + k] = i < nf;
+      src[2 + k] = a.flags + gb + (use[2 + k] ? i : 0);
     }
 #pragma unroll
     for (int k = 0; k < NW; ++k) w[k] = use[k] ? peek(src[k]) : 0ull;
@@ -1008,19 +1082,20 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     uint32_t prev = 0;
     const bool counts = master && tid == 0;
     if (counts) prev = __hip_atomic_fetch_add(&a.hdr->groups_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    settle_all(w, src, use, epoch, a.hdr);
+    settle_mixed(pw, puse, rp, poff, w, src, use, epoch, a.hdr);
     if (counts && prev == uint32_t(a.B * a.Hkv) - 1) {
       __hip_atomic_store(&a.hdr->groups_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&a.hdr->epoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     stamp(a, 5);
-#pragma unroll
-    for (int k = 0; k < 3; ++k)
-      if (use[k]) pv[tid + k * kThreads] = __uint_as_float(uint32_t(w[k]));
+    if (use_p) {
+      pv[(2 * k_p) * S + sp_p] = __uint_as_float(pw[0].x);
+      pv[(2 * k_p + 1) * S + sp_p] = __uint_as_float(pw[0].z);
+    }
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      if (use[3 + k]) pm[tid + k * kThreads] = __uint_as_float(uint32_t(w[3 + k]));
-      if (use[5 + k]) fl[tid + k * kThreads] = uint32_t(w[5 + k]);
+      if (use[k]) pm[tid + k * kThreads] = __uint_as_float(uint32_t(w[k]));
+      if (use[2 + k]) fl[tid + k * kThreads] = uint32_t(w[2 + k]);
     }
     __syncthreads();
     // one wave per sum: lane l adds splits l, l+64, ... in order, then a

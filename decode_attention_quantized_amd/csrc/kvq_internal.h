@@ -136,10 +136,14 @@ constexpr int kStamps = 10;       // phase stamps per workgroup (7..9 split the 
 // cross-wave reduction [kWaves][G][128], and the merge's slice partials
 // [E][S] (E = ceil(G*128 / S)), kept-mass inputs [nh][S] (nh = heads a
 // workgroup sums: 1 if S >= G, else ceil(G / S)) and flags [S].
+// Output elements each workgroup of a group sums in the merge: ceil(G*128/S)
+// rounded up to even, so every slice starts on a 16-byte boundary.
+inline __host__ __device__ int gqa_merge_slice(int G, int S) { return 2 * ((G * 128 + 2 * S - 1) / (2 * S)); }
+
 inline __host__ __device__ int gqa_sc_floats(int G, int P, int S) {
   int n = G * P;
   if (kWaves * G * 128 > n) n = kWaves * G * 128;
-  const int E = (G * 128 + S - 1) / S;
+  const int E = gqa_merge_slice(G, S);
   const int nh = S >= G ? 1 : (G + S - 1) / S;
   const int m = S * (1 + E + nh);
   if (m > n) n = m;
