@@ -38,6 +38,7 @@ namespace kvq {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kSpinLimit = 1u << 23;
 
@@ -456,6 +457,76 @@ template <> struct Traits<KVQ_LUT3> {
 // kernel rotates q once (scores are inner products, and the rotation is
 // orthonormal and symmetric) and each workgroup's partial output once.
 template <> struct Traits<KVQ_LUT3_WHT> : Traits<KVQ_LUT3> {};
+
+// v plus the value of lane l ^ 16 (resp. l ^ 32), the same bits on both lanes
+__device__ inline float sum_pairs16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v),
+                                                  false, false);
+  return __builtin_bit_cast(float, unsigned(r[0])) + __builtin_bit_cast(float, unsigned(r[1]));
+}
+__device__ inline float sum_pairs32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v),
+                                                  false, false);
+  return __builtin_bit_cast(float, unsigned(r[0])) + __builtin_bit_cast(float, unsigned(r[1]));
+}
+
+// ---------------------------------------------------------------- value rows on MFMA
+// A wave with many value rows sums p * v with v_mfma_f32_16x16x16_f16, 16
+// rows per batch: out[h][d] = sum_r (p[h][r] * s[r][d]) * c[r][d] with s the
+// row's scale for dim d and c its code value (q4_0: c - 8, exact in fp16).
+// A rows 0..7 hold the fp16 high parts of p * s for heads 0..7, rows 8..15
+// the low parts (p * s minus the high part), so the two rows of a head add
+// up to p * s within 2^-22 relative; the products with the exact codes are
+// formed and summed in fp32. Tile t (0..7) takes the dims n + 16t (n the
+// MFMA column), all inside scale block t / 2, so each tile has one A operand.
+// A row's 64 code bytes are staged transposed as an 8 x 8 byte matrix,
+// T[8j + a] = R[8a + j], so that the lane of column n finds the nibbles of
+// its dims n + 16a (a = 0..7) in the 8 bytes at 8 * (n / 2).
+template <int FMT> struct VMfma { static constexpr bool kOn = false; };
+template <> struct VMfma<KVQ_Q4_0> {
+  static constexpr bool kOn = true;
+  // code piece ch (row bytes 16ch .. 16ch + 15) -> its transposed places: for
+  // each j the bytes (j, 8 + j) of the piece go to T[8j + 2ch], T[8j + 2ch + 1]
+  __device__ static void stage(uint8_t* lrow, const uint4& cv, int ch) {
+    const uint32_t p01 = __builtin_amdgcn_perm(cv.z, cv.x, 0x05010400u);   // pairs j = 0, 1
+    const uint32_t p23 = __builtin_amdgcn_perm(cv.z, cv.x, 0x07030602u);   // j = 2, 3
+    const uint32_t p45 = __builtin_amdgcn_perm(cv.w, cv.y, 0x05010400u);   // j = 4, 5
+    const uint32_t p67 = __builtin_amdgcn_perm(cv.w, cv.y, 0x07030602u);   // j = 6, 7
+    uint16_t* q = reinterpret_cast<uint16_t*>(lrow + 2 * ch);
+    q[0] = uint16_t(p01); q[4] = uint16_t(p01 >> 16);
+    q[8] = uint16_t(p23); q[12] = uint16_t(p23 >> 16);
+    q[16] = uint16_t(p45); q[20] = uint16_t(p45 >> 16);
+    q[24] = uint16_t(p67); q[28] = uint16_t(p67 >> 16);
+  }
+  // B operands of the 8 tiles for rows 4g .. 4g + 3 of the batch (column n)
+  __device__ static void b_ops(const uint8_t* vst, int g, int n, half4 (&B)[8]) {
+    const int sh = 4 * (n & 1);
+    uint32_t lo[4], hi[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint2 x = *reinterpret_cast<const uint2*>(vst + (4 * g + i) * Traits<KVQ_Q4_0>::PITCH + 8 * (n >> 1));
+      lo[i] = x.x >> sh;
+      hi[i] = x.y >> sh;
+    }
+    const half2v bias = {_Float16(1032.f), _Float16(1032.f)};
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t* w = t < 4 ? lo : hi;
+      const uint32_t sel = 0x0C000C00u | (uint32_t(4 + (t & 3)) << 16) | uint32_t(t & 3);
+      // bytes t of rows (0, 1) and (2, 3) -> nibbles -> fp16 1024 + c -> c - 8
+      const uint32_t r01 = (__builtin_amdgcn_perm(w[1], w[0], sel) & 0x000F000Fu) | 0x64006400u;
+      const uint32_t r23 = (__builtin_amdgcn_perm(w[3], w[2], sel) & 0x000F000Fu) | 0x64006400u;
+      const half2v h01 = __builtin_bit_cast(half2v, r01) - bias;
+      const half2v h23 = __builtin_bit_cast(half2v, r23) - bias;
+      B[t] = half4{h01[0], h01[1], h23[0], h23[1]};
+    }
+  }
+  // scale of block b (dims 32b .. 32b + 31) of a staged row
+  __device__ static float scale(const uint8_t* lrow, int b) {
+    return float(reinterpret_cast<const _Float16*>(lrow + Traits<KVQ_Q4_0>::CB)[b]);
+  }
+  static constexpr int kBlocks = 4;                  // scale blocks (A operands) per row
+};
 
 // y = H x / sqrt(128) in float32 on a 128-vector held as elements (lane,
 // lane + 64) of a wave (H the Sylvester Hadamard matrix, as the packers)
@@ -893,6 +964,13 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     nmine += (n + 1 - side) >> 1;
   }
   stamp(a, 8);
+  using VM = VMfma<FMT>;
+  // a wave with at least 8 rows sums them on MFMA (wave-uniform choice)
+  const bool use_mfma = VM::kOn && nmine >= 8;
+  floatx4 vacc[8];
+  float vmass = 0.f;                                  // lanes of high-part rows: their head's weights
+#pragma unroll
+  for (int t = 0; t < 8; ++t) vacc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
   {
     // this wave's rows in batches of 16: the rows are read with 16-byte loads
     // (one or two instructions per batch) into this wave's LDS strip, then
@@ -903,7 +981,59 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     constexpr int NL = T::CB / 16;                  // 16-byte pieces per row
     constexpr int NI = (VB * NL + 63) / 64;         // load instructions per batch
     uint8_t* vst = stg + wave * 16 * T::PITCH;
-    for (int k = 0; k < nmine; k += VB) {
+    if constexpr (VM::kOn)
+      if (use_mfma)
+        for (int k = 0; k < nmine; k += VB) {
+          // the batch's rows: codes staged transposed, scales as they are
+          uint4 cv[NI];
+          int rr[NI], ch[NI];
+          bool ok[NI];
+#pragma unroll
+          for (int i = 0; i < NI; ++i) {
+            const int piece = 64 * i + lane;
+            rr[i] = piece / NL;
+            ch[i] = piece - rr[i] * NL;
+            ok[i] = piece < VB * NL && k + rr[i] < nmine;
+            const int64_t row = row0 + pos0 + mylist[ok[i] ? k + rr[i] : k];
+            cv[i] = *reinterpret_cast<const uint4*>(a.vc + row * T::CB + 16 * (ok[i] ? ch[i] : 0));
+          }
+          const bool sok = lane < VB && k + lane < nmine;
+          uint2 sv = make_uint2(0u, 0u);
+          if (sok) sv = *reinterpret_cast<const uint2*>(a.vs + (row0 + pos0 + mylist[k + lane]) * 8);
+#pragma unroll
+          for (int i = 0; i < NI; ++i)
+            if (ok[i]) VM::stage(vst + rr[i] * T::PITCH, cv[i], ch[i]);
+          if (sok) *reinterpret_cast<uint2*>(vst + lane * T::PITCH + T::CB) = sv;
+          // operands: lane (g, n) holds rows 4g .. 4g + 3; A row m is head
+          // m & 7, high (m < 8) or low part
+          const int g4 = lane >> 4, n16v = lane & 15, hj = n16v & 7;
+          const bool lo_part = n16v >= 8;
+          half4 B[8];
+          VM::b_ops(vst, g4, n16v, B);
+          float w[4];
+          bool okr[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int kk = k + 4 * g4 + i;
+            okr[i] = kk < nmine;
+            w[i] = (okr[i] && hj < G) ? sc[hj * P + mylist[okr[i] ? kk : k]] : 0.f;
+            if (!lo_part) vmass += w[i];
+          }
+#pragma unroll
+          for (int b = 0; b < VM::kBlocks; ++b) {
+            half4 A;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float x = okr[i] ? w[i] * VM::scale(vst + (4 * g4 + i) * T::PITCH, b) : 0.f;
+              const _Float16 h = _Float16(x);
+              A[i] = lo_part ? _Float16(x - float(h)) : h;
+            }
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+              if (t * VM::kBlocks / 8 == b) vacc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(A, B[t], vacc[t], 0, 0, 0);
+          }
+        }
+    for (int k = 0; k < (use_mfma ? 0 : nmine); k += VB) {
       uint4 cv[NI];
       int rr[NI], ch[NI];
       bool ok[NI];
@@ -950,17 +1080,29 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
       }
     }
   }
+  if (use_mfma) {
+    // head h's weights are on lanes h, h + 16, h + 32, h + 48; a head's high
+    // and low part rows are on lanes l and l + 32
+    vmass = sum_pairs16(vmass);
+    vmass = sum_pairs32(vmass);
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vacc[t][i] = sum_pairs32(vacc[t][i]);
+  }
   stamp(a, 9);
 
   // per-wave counters and kept mass (mass is wave-uniform: summed over the
-  // wave's rows in row order)
+  // wave's rows in row order; on the MFMA path lane h holds head h's)
   if (lane == 0) {
     wcount[wave] = kept_cnt;
     wrows[wave] = rows_cnt;
     wproc[wave] = nmine;
+    if (!use_mfma)
 #pragma unroll
-    for (int j = 0; j < G; ++j) wmass[wave * G + j] = mass[j];
+      for (int j = 0; j < G; ++j) wmass[wave * G + j] = mass[j];
   }
+  if (use_mfma && lane < G) wmass[wave * G + lane] = vmass;
   __syncthreads();                                   // all waves done with sc
   int wg_rows = 0, wg_kept = 0, nact = 0;
   uint32_t act = 0;                                  // waves that summed value rows
@@ -989,10 +1131,22 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     float* red = sc;                                 // [nact][G][128]
     if ((act >> wave) & 1u) {
       const int slot = __popc(act & ((1u << wave) - 1u));
+      if (use_mfma) {
+        // lane (g, n), g < 2: heads 4g + i, dims n + 16t
+        if (lane < 32)
 #pragma unroll
-      for (int j = 0; j < G; ++j) {
-        red[(slot * G + j) * 128 + 2 * lane] = o0[j];
-        red[(slot * G + j) * 128 + 2 * lane + 1] = o1[j];
+          for (int i = 0; i < 4; ++i) {
+            const int h = 4 * (lane >> 4) + i;
+            if (h < G)
+#pragma unroll
+              for (int t = 0; t < 8; ++t) red[(slot * G + h) * 128 + (lane & 15) + 16 * t] = vacc[t][i];
+          }
+      } else {
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          red[(slot * G + j) * 128 + 2 * lane] = o0[j];
+          red[(slot * G + j) * 128 + 2 * lane + 1] = o1[j];
+        }
       }
     }
     __syncthreads();
