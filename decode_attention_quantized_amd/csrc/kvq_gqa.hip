@@ -482,7 +482,10 @@ __device__ inline float sum_pairs32(float v) {
 // A row's 64 code bytes are staged transposed as an 8 x 8 byte matrix,
 // T[8j + a] = R[8a + j], so that the lane of column n finds the nibbles of
 // its dims n + 16a (a = 0..7) in the 8 bytes at 8 * (n / 2).
-template <int FMT> struct VMfma { static constexpr bool kOn = false; };
+template <int FMT> struct VMfma {
+  static constexpr bool kOn = false;
+  __device__ static int dim(int, int) { return 0; }
+};
 template <> struct VMfma<KVQ_Q4_0> {
   static constexpr bool kOn = true;
   // code piece ch (row bytes 16ch .. 16ch + 15) -> its transposed places: for
@@ -498,8 +501,9 @@ template <> struct VMfma<KVQ_Q4_0> {
     q[16] = uint16_t(p45); q[20] = uint16_t(p45 >> 16);
     q[24] = uint16_t(p67); q[28] = uint16_t(p67 >> 16);
   }
+  __device__ static int dim(int n, int t) { return n + 16 * t; }
   // B operands of the 8 tiles for rows 4g .. 4g + 3 of the batch (column n)
-  __device__ static void b_ops(const uint8_t* vst, int g, int n, half4 (&B)[8]) {
+  __device__ static void b_ops(const uint8_t* vst, int g, int n, uint32_t, half4 (&B)[8]) {
     const int sh = 4 * (n & 1);
     uint32_t lo[4], hi[4];
 #pragma unroll
@@ -527,6 +531,46 @@ template <> struct VMfma<KVQ_Q4_0> {
   }
   static constexpr int kBlocks = 4;                  // scale blocks (A operands) per row
 };
+
+// LUT3: one scale per row, so the A operand is p * nu / sqrt(128) and tile t
+// takes the dims 8n + t; rows are staged as they are. The lane of column n
+// reads the 24 code bits of its dims 8n .. 8n + 7 from a row, looks up the
+// four value pairs in the pair table and swaps them into the row order of
+// the B operand. B holds the fp16 table values (exact).
+template <> struct VMfma<KVQ_LUT3> {
+  static constexpr bool kOn = true;
+  static constexpr int kBlocks = 1;
+  __device__ static void stage(uint8_t* lrow, const uint4& cv, int ch) {
+    *reinterpret_cast<uint4*>(lrow + 16 * ch) = cv;
+  }
+  __device__ static int dim(int n, int t) { return 8 * n + t; }
+  __device__ static void b_ops(const uint8_t* vst, int g, int n, uint32_t table, half4 (&B)[8]) {
+    const int w = (24 * n) >> 5, o = (24 * n) & 31;
+    uint32_t pr[4][4];                               // [row][dim pair] value pairs
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t* rw = reinterpret_cast<const uint32_t*>(vst + (4 * g + i) * Traits<KVQ_LUT3>::PITCH);
+      // bits 24n .. 24n + 23 of the row (the word after it is still inside the row's pitch)
+      const uint32_t bits = __builtin_amdgcn_alignbit(rw[w + 1], rw[w], o);
+#pragma unroll
+      for (int tp = 0; tp < 4; ++tp)
+        pr[i][tp] = uint32_t(__builtin_amdgcn_ds_bpermute(int(((bits >> (6 * tp)) << 2) & 0xFCu), int(table)));
+    }
+#pragma unroll
+    for (int tp = 0; tp < 4; ++tp) {
+      const uint32_t e01 = __builtin_amdgcn_perm(pr[1][tp], pr[0][tp], 0x05040100u);   // even dim, rows 0, 1
+      const uint32_t o01 = __builtin_amdgcn_perm(pr[1][tp], pr[0][tp], 0x07060302u);   // odd dim
+      const uint32_t e23 = __builtin_amdgcn_perm(pr[3][tp], pr[2][tp], 0x05040100u);
+      const uint32_t o23 = __builtin_amdgcn_perm(pr[3][tp], pr[2][tp], 0x07060302u);
+      B[2 * tp] = __builtin_bit_cast(half4, make_uint2(e01, e23));
+      B[2 * tp + 1] = __builtin_bit_cast(half4, make_uint2(o01, o23));
+    }
+  }
+  __device__ static float scale(const uint8_t* lrow, int) {
+    return float(*reinterpret_cast<const _Float16*>(lrow + Traits<KVQ_LUT3>::CB)) * Traits<KVQ_LUT3>::kRowMul;
+  }
+};
+template <> struct VMfma<KVQ_LUT3_WHT> : VMfma<KVQ_LUT3> {};
 
 // y = H x / sqrt(128) in float32 on a 128-vector held as elements (lane,
 // lane + 64) of a wave (H the Sylvester Hadamard matrix, as the packers)
@@ -972,44 +1016,95 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
 #pragma unroll
   for (int t = 0; t < 8; ++t) vacc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
   {
-    // this wave's rows in batches of 16: the rows are read with 16-byte loads
-    // (one or two instructions per batch) into this wave's LDS strip, then
-    // each lane takes its two dims from there (the list and the strip are
-    // written and read by this wave only, and its LDS accesses complete in
-    // order)
+    // This wave's rows in batches of 16, read with 16-byte loads (one or two
+    // instructions per batch) that are kept D batches ahead in registers, then
+    // staged in this wave's LDS strip (the list and the strip are written and
+    // read by this wave only, and its LDS accesses complete in order).
     constexpr int VB = 16;
     constexpr int NL = T::CB / 16;                  // 16-byte pieces per row
     constexpr int NI = (VB * NL + 63) / 64;         // load instructions per batch
+    // batches of loads in flight: LUT3 value rows (long dense runs, slow
+    // per-row decode) gain from four; for q4_0 one measured fastest, and
+    // q8_0 (two load instructions per batch) has no registers to spare
+    constexpr int D = (FMT == KVQ_LUT3 || FMT == KVQ_LUT3_WHT) ? 4 : 1;
     uint8_t* vst = stg + wave * 16 * T::PITCH;
-    if constexpr (VM::kOn)
+    static_assert(NI == 1 || NI == 2, "value row pieces per batch");
+    struct VBuf { uint4 cv0, cv1; uint2 sv; };       // cv1 only when NI == 2
+    // every lane loads (pieces past the batch re-read the batch's first row),
+    // so the loads are not branched around and stay in registers
+    auto load_piece = [&](int i, int k) __attribute__((always_inline)) -> uint4 {
+      const int piece = 64 * i + lane, rr = piece / NL, ch = piece - rr * NL;
+      const bool ok = piece < VB * NL && k + rr < nmine;
+      const int64_t row = row0 + pos0 + mylist[ok ? k + rr : k];
+      return *reinterpret_cast<const uint4*>(a.vc + row * T::CB + 16 * (ok ? ch : 0));
+    };
+    auto load_batch = [&](VBuf& vb, int k) __attribute__((always_inline)) {
+      vb.cv0 = load_piece(0, k);
+      if constexpr (NI == 2) vb.cv1 = load_piece(1, k);
+      const bool sok = lane < VB && k + lane < nmine;
+      const int64_t srow = row0 + pos0 + mylist[sok ? k + lane : k];
+      if constexpr (T::SB == 8) vb.sv = *reinterpret_cast<const uint2*>(a.vs + srow * 8);
+      else vb.sv = make_uint2(*reinterpret_cast<const uint16_t*>(a.vs + srow * T::SB), 0u);
+    };
+    // codes to the strip (transposed for the MFMA path of q4_0), scales after them
+    auto stage_piece = [&](int i, const uint4& cv, int k, bool mf) __attribute__((always_inline)) {
+      const int piece = 64 * i + lane, rr = piece / NL, ch = piece - rr * NL;
+      if (piece < VB * NL && k + rr < nmine) {
+        if constexpr (VM::kOn) {
+          if (mf) VM::stage(vst + rr * T::PITCH, cv, ch);
+          else *reinterpret_cast<uint4*>(vst + rr * T::PITCH + 16 * ch) = cv;
+        } else {
+          *reinterpret_cast<uint4*>(vst + rr * T::PITCH + 16 * ch) = cv;
+        }
+      }
+    };
+    auto stage_batch = [&](const VBuf& vb, int k, bool mf) __attribute__((always_inline)) {
+      stage_piece(0, vb.cv0, k, mf);
+      if constexpr (NI == 2) stage_piece(1, vb.cv1, k, mf);
+      if (lane < VB && k + lane < nmine) {
+        if constexpr (T::SB == 8) *reinterpret_cast<uint2*>(vst + lane * T::PITCH + T::CB) = vb.sv;
+        else *reinterpret_cast<uint16_t*>(vst + lane * T::PITCH + T::CB) = uint16_t(vb.sv.x);
+      }
+    };
+    // the batches in order, loads D batches ahead (the ring is D named
+    // buffers, so it stays in registers)
+    auto run_batches = [&](bool mf, auto&& compute) __attribute__((always_inline)) {
+      VBuf v0, v1, v2, v3;                           // the first D are used
+      auto step = [&](VBuf& vb, int k) __attribute__((always_inline)) -> bool {
+        if (k >= nmine) return false;                // uniform across the wave
+        stage_batch(vb, k, mf);
+        if (k + D * VB < nmine) load_batch(vb, k + D * VB);
+        compute(k);
+        return true;
+      };
+      if (nmine == 0) return;                        // no rows: mylist holds nothing to read
+      static_assert(D == 1 || D == 2 || D == 4, "batches in flight");
+      load_batch(v0, 0);
+      if constexpr (D >= 2)
+        if (VB < nmine) load_batch(v1, VB);
+      if constexpr (D == 4) {
+        if (2 * VB < nmine) load_batch(v2, 2 * VB);
+        if (3 * VB < nmine) load_batch(v3, 3 * VB);
+      }
+      for (int k0 = 0; k0 < nmine; k0 += D * VB) {
+        if (!step(v0, k0)) break;
+        if constexpr (D >= 2)
+          if (!step(v1, k0 + VB)) break;
+        if constexpr (D == 4) {
+          if (!step(v2, k0 + 2 * VB)) break;
+          if (!step(v3, k0 + 3 * VB)) break;
+        }
+      }
+    };
+    if constexpr (VM::kOn) {
       if (use_mfma)
-        for (int k = 0; k < nmine; k += VB) {
-          // the batch's rows: codes staged transposed, scales as they are
-          uint4 cv[NI];
-          int rr[NI], ch[NI];
-          bool ok[NI];
-#pragma unroll
-          for (int i = 0; i < NI; ++i) {
-            const int piece = 64 * i + lane;
-            rr[i] = piece / NL;
-            ch[i] = piece - rr[i] * NL;
-            ok[i] = piece < VB * NL && k + rr[i] < nmine;
-            const int64_t row = row0 + pos0 + mylist[ok[i] ? k + rr[i] : k];
-            cv[i] = *reinterpret_cast<const uint4*>(a.vc + row * T::CB + 16 * (ok[i] ? ch[i] : 0));
-          }
-          const bool sok = lane < VB && k + lane < nmine;
-          uint2 sv = make_uint2(0u, 0u);
-          if (sok) sv = *reinterpret_cast<const uint2*>(a.vs + (row0 + pos0 + mylist[k + lane]) * 8);
-#pragma unroll
-          for (int i = 0; i < NI; ++i)
-            if (ok[i]) VM::stage(vst + rr[i] * T::PITCH, cv[i], ch[i]);
-          if (sok) *reinterpret_cast<uint2*>(vst + lane * T::PITCH + T::CB) = sv;
-          // operands: lane (g, n) holds rows 4g .. 4g + 3; A row m is head
-          // m & 7, high (m < 8) or low part
+        run_batches(true, [&](int k) __attribute__((always_inline)) {
+          // lane (g, n) holds rows 4g .. 4g + 3; A row m is head m & 7, high
+          // (m < 8) or low part
           const int g4 = lane >> 4, n16v = lane & 15, hj = n16v & 7;
           const bool lo_part = n16v >= 8;
           half4 B[8];
-          VM::b_ops(vst, g4, n16v, B);
+          VM::b_ops(vst, g4, n16v, table, B);
           float w[4];
           bool okr[4];
 #pragma unroll
@@ -1032,53 +1127,27 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
             for (int t = 0; t < 8; ++t)
               if (t * VM::kBlocks / 8 == b) vacc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(A, B[t], vacc[t], 0, 0, 0);
           }
-        }
-    for (int k = 0; k < (use_mfma ? 0 : nmine); k += VB) {
-      uint4 cv[NI];
-      int rr[NI], ch[NI];
-      bool ok[NI];
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int piece = 64 * i + lane;
-        rr[i] = piece / NL;
-        ch[i] = piece - rr[i] * NL;
-        ok[i] = piece < VB * NL && k + rr[i] < nmine;
-        // every lane loads (pieces past the batch re-read the batch's first
-        // row), so the loads are not branched around and stay in registers
-        const int64_t row = row0 + pos0 + mylist[ok[i] ? k + rr[i] : k];
-        cv[i] = *reinterpret_cast<const uint4*>(a.vc + row * T::CB + 16 * (ok[i] ? ch[i] : 0));
-      }
-      const bool sok = lane < VB && k + lane < nmine;
-      uint2 sv = make_uint2(0u, 0u);
-      if (sok) {
-        const int64_t row = row0 + pos0 + mylist[k + lane];
-        if constexpr (T::SB == 8) sv = *reinterpret_cast<const uint2*>(a.vs + row * 8);
-        else sv.x = *reinterpret_cast<const uint16_t*>(a.vs + row * T::SB);
-      }
-#pragma unroll
-      for (int i = 0; i < NI; ++i)
-        if (ok[i]) *reinterpret_cast<uint4*>(vst + rr[i] * T::PITCH + 16 * ch[i]) = cv[i];
-      if (sok) {
-        if constexpr (T::SB == 8) *reinterpret_cast<uint2*>(vst + lane * T::PITCH + T::CB) = sv;
-        else *reinterpret_cast<uint16_t*>(vst + lane * T::PITCH + T::CB) = uint16_t(sv.x);
-      }
-#pragma unroll
-      for (int u = 0; u < VB; ++u) {
-        if (k + u >= nmine) break;
-        const uint8_t* lr = vst + u * T::PITCH;
-        const typename T::VRaw vr = T::vload(lr, lr + T::CB, lane);
-        float v0, v1;
-        T::vdeq(vr, table, v0, v1);
-        const int pr = mylist[k + u];
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-          const float pj = sc[j * P + pr];        // same for every lane of the wave
-          o0[j] = fmaf(pj, v0, o0[j]);
-          o1[j] = fmaf(pj, v1, o1[j]);
-          mass[j] += pj;
-        }
-      }
+        });
     }
+    if (!use_mfma)
+      run_batches(false, [&](int k) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < VB; ++u) {
+          if (k + u >= nmine) break;
+          const uint8_t* lr = vst + u * T::PITCH;
+          const typename T::VRaw vr = T::vload(lr, lr + T::CB, lane);
+          float v0, v1;
+          T::vdeq(vr, table, v0, v1);
+          const int pr = mylist[k + u];
+#pragma unroll
+          for (int j = 0; j < G; ++j) {
+            const float pj = sc[j * P + pr];        // same for every lane of the wave
+            o0[j] = fmaf(pj, v0, o0[j]);
+            o1[j] = fmaf(pj, v1, o1[j]);
+            mass[j] += pj;
+          }
+        }
+      });
   }
   if (use_mfma) {
     // head h's weights are on lanes h, h + 16, h + 32, h + 48; a head's high
@@ -1139,7 +1208,7 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
             const int h = 4 * (lane >> 4) + i;
             if (h < G)
 #pragma unroll
-              for (int t = 0; t < 8; ++t) red[(slot * G + h) * 128 + (lane & 15) + 16 * t] = vacc[t][i];
+              for (int t = 0; t < 8; ++t) red[(slot * G + h) * 128 + VM::dim(lane & 15, t)] = vacc[t][i];
           }
       } else {
 #pragma unroll

@@ -51,10 +51,11 @@ def test_stress_scattered_mask():
     compare(inp, tau, g, r, po)
 
 
+@pytest.mark.parametrize("threshold", [1e-6, 0.0])
 @pytest.mark.parametrize("ctx", [1, 2, 63, 65, 1000, 4097])
-def test_ragged_contexts(ctx):
-    say("case ragged q4_0 ctx", ctx)
-    inp, tau = _case("long", ctx=ctx, hot=min(4, ctx))
+def test_ragged_contexts(ctx, threshold):
+    say("case ragged q4_0 ctx", ctx, "tau", threshold)
+    inp, tau = _case("long", threshold, ctx=ctx, hot=min(4, ctx))
     g = run_gpu(inp, tau)
     r, po = oracle_for(inp, tau)
     compare(inp, tau, g, r, po)
@@ -72,6 +73,18 @@ def test_ctx_below_capacity():
 def test_group_sizes(G):
     say("case q8_0 group size", G)
     inp, tau = _case("long", fmt="q8_0", q_heads=2 * G, kv_heads=2, ctx=3000, hot=5)
+    g = run_gpu(inp, tau)
+    r, po = oracle_for(inp, tau)
+    compare(inp, tau, g, r, po)
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "lut3"])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_group_sizes_every_row_kept(fmt, G):
+    """Threshold 0 keeps every row, so waves sum their value rows on the
+    matrix cores (16-row batches, the last one partial) for every group size."""
+    say("case", fmt, "group size", G, "tau 0")
+    inp, tau = _case("long", 0.0, fmt=fmt, q_heads=2 * G, kv_heads=2, ctx=3001, hot=5)
     g = run_gpu(inp, tau)
     r, po = oracle_for(inp, tau)
     compare(inp, tau, g, r, po)
@@ -135,10 +148,11 @@ def test_lut3_small(threshold, name):
 
 
 @pytest.mark.parametrize("name", ["lut3", "lut3_wht"])
+@pytest.mark.parametrize("threshold", [1e-6, 0.0])
 @pytest.mark.parametrize("ctx", [1, 77, 4100])
-def test_lut3_ragged(ctx, name):
-    say("case", name, "ragged ctx", ctx)
-    inp, tau = _case(name, batch=1, ctx=ctx)
+def test_lut3_ragged(ctx, threshold, name):
+    say("case", name, "ragged ctx", ctx, "tau", threshold)
+    inp, tau = _case(name, threshold, batch=1, ctx=ctx)
     g = run_gpu(inp, tau)
     r, po = oracle_for(inp, tau)
     compare(inp, tau, g, r, po)
