@@ -53,6 +53,7 @@ struct Plan {
   size_t lds = 0;
   int nwg = 0;
   int threads = 0;
+  int R = 1;                                              // latent output: row ranges per block
   WsLayout ws{};
   kvq::MlaLayout mws{};
   int64_t total = 0;
@@ -98,7 +99,8 @@ int32_t make_mla_plan(const kvq_cache* k, const kvq_launch* l, int32_t ctx_len, 
   plan->lds = lds;
   plan->nwg = k->batch * S;
   plan->threads = 4 * H;                                 // two waves per 32-head block
-  plan->mws = kvq::mla_ws_layout(k->batch, H, S, P);
+  plan->R = kvq::mla_out_ranges(ctx_len);
+  plan->mws = kvq::mla_ws_layout(k->batch, H, S, P, plan->R);
   plan->total = plan->mws.total;
   return KVQ_OK;
 }
@@ -192,6 +194,12 @@ int32_t launch_mla(const void* q, const kvq_cache* kcache, const kvq_cache* vcac
   a.kpairs = reinterpret_cast<int32_t*>(ws + plan.mws.kpairs);
   a.kpos = reinterpret_cast<int32_t*>(ws + plan.mws.kpos);
   a.kp = reinterpret_cast<float*>(ws + plan.mws.kp);
+  a.opart = reinterpret_cast<float*>(ws + plan.mws.opart);
+  a.mpart = reinterpret_cast<float*>(ws + plan.mws.mpart);
+  a.ocnt = reinterpret_cast<uint32_t*>(ws + plan.mws.ocnt);
+  // threshold 0 keeps every row: the output contraction is split over row
+  // ranges; a positive threshold keeps few rows, one range per block
+  a.R = threshold == 0.0f ? plan.R : 1;
   a.B = kcache->batch;
   a.Hq = l->q_heads;
   a.ctx = ctx_len;
@@ -210,7 +218,7 @@ int32_t launch_mla(const void* q, const kvq_cache* kcache, const kvq_cache* vcac
   (void)hipGetDevice(&dev);
   if (int64_t(per_cu) * device_info(dev).cus < plan.nwg) return KVQ_ERR_UNSUPPORTED;
   hipError_t e = launch(ks, plan.nwg, plan.threads, &a, plan.lds, l);
-  if (e == hipSuccess) e = launch(kvq::mla_out_kernel(), kcache->batch * (plan.G / 32) * 4, 256, &a, 0, l);
+  if (e == hipSuccess) e = launch(kvq::mla_out_kernel(), kcache->batch * (plan.G / 32) * 4 * a.R, 256, &a, 0, l);
   if (e != hipSuccess) {
     (void)hipGetLastError();
     return KVQ_ERR_LAUNCH;

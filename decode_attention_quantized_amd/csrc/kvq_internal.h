@@ -104,6 +104,10 @@ struct MlaArgs {
   int32_t* kpairs;                // [B][S] kept (head, position) pairs per split
   int32_t* kpos;                  // [B][S][P] positions of kept rows
   float* kp;                      // [B][S][P][H] weights of kept rows (0 where a head skips)
+  float* opart;                   // [B][H/32][4][R][32][128] output partials of row ranges
+  float* mpart;                   // [B][H/32][R][32] kept-mass partials of row ranges
+  uint32_t* ocnt;                 // [B][H/32][4] row ranges finished (0 between calls)
+  int32_t R;                      // row ranges per output block launched
   int32_t B, Hq, ctx, cap;
   int32_t S, P;
   float sigma_log2e;
@@ -112,11 +116,11 @@ struct MlaArgs {
 };
 
 struct MlaLayout {
-  int64_t kept_mass, bgstat, split_ml, kcount, kpairs, kpos, kp, total;
+  int64_t kept_mass, bgstat, split_ml, kcount, kpairs, kpos, kp, opart, mpart, ocnt, total;
 };
 
 // The first two regions match ws_layout() so kvq_stats reads both families alike.
-inline MlaLayout mla_ws_layout(int B, int H, int S, int P) {
+inline MlaLayout mla_ws_layout(int B, int H, int S, int P, int R) {
   MlaLayout w;
   int64_t off = 256;
   w.kept_mass = off; off = align256(off + int64_t(B) * H * 4);
@@ -126,11 +130,23 @@ inline MlaLayout mla_ws_layout(int B, int H, int S, int P) {
   w.kpairs = off;    off = align256(off + int64_t(B) * S * 4);
   w.kpos = off;      off = align256(off + int64_t(B) * S * P * 4);
   w.kp = off;        off = align256(off + int64_t(B) * S * P * int64_t(H) * 4);
+  w.opart = off;     off = align256(off + int64_t(B) * (H / 32) * 4 * R * 32 * 128 * 4);
+  w.mpart = off;     off = align256(off + int64_t(B) * (H / 32) * R * 32 * 4);
+  w.ocnt = off;      off = align256(off + int64_t(B) * (H / 32) * 4 * 4);
   w.total = off;
   return w;
 }
 
 constexpr int kStamps = 10;       // phase stamps per workgroup (7..9 split the V pass)
+
+// Latent output contraction: row ranges launched per (sequence, 32 heads,
+// 128 value dims) block, from the context length (ranges of at least
+// kOutMinRows kept rows are used; the rest exit at once).
+constexpr int kOutMinRows = 2048;
+inline int mla_out_ranges(int ctx) {
+  const int r = (ctx + 4 * kOutMinRows - 1) / (4 * kOutMinRows);
+  return r < 1 ? 1 : r > 8 ? 8 : r;
+}
 
 // Floats of the first LDS region of the grouped kernel: scores [G][P], the
 // cross-wave reduction [kWaves][G][128], and the merge's slice partials

@@ -668,16 +668,23 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
 }
 
 // ----------------------------------------------------------------------------- out
-// One workgroup per (sequence, 32 heads, 128-dim value group g): the output
-// block out[h][d] = sum over the sequence's kept rows r of p[h][r] * v[r][d],
-// a contraction over rows on v_mfma_f32_32x32x16_bf16 (M = heads, N = dims,
-// K = rows; wave w owns dims 32w..32w+31 of the group). Exact operands: v is
-// the e4m3 code converted to bf16 (exact) and the row's fp32 group scale
-// goes to the weight side, p * scale (one fp32 rounding) split into three
-// bf16 terms that add up to it exactly (8 + 8 + 8 significant bits); each
-// term is a separate MFMA into the same fp32 accumulator. Rows are taken in
-// split order and, within a split, in position order, 64 at a time; both
-// operands are staged transposed in LDS (rows contiguous per head / dim).
+// Output block (sequence b, 32 heads hb, 128-dim value group g): out[h][d] =
+// sum over the sequence's kept rows r of p[h][r] * v[r][d], a contraction over
+// rows on v_mfma_f32_32x32x16_bf16 (M = heads, N = dims, K = rows; wave w owns
+// dims 32w..32w+31 of the group). Exact operands: v is the e4m3 code converted
+// to bf16 (exact) and the row's fp32 group scale goes to the weight side,
+// p * scale (one fp32 rounding) split into three bf16 terms that add up to it
+// exactly (8 + 8 + 8 significant bits); each term is a separate MFMA into the
+// same fp32 accumulator. Rows are taken in split order and, within a split, in
+// position order, 64 at a time; both operands are staged transposed in LDS
+// (rows contiguous per head / dim), and the next 64 rows are loaded while the
+// current ones are multiplied.
+//
+// R workgroups share a block, each taking one range of the kept rows; with N
+// kept rows, min(R, ceil(N / kOutMinRows)) ranges are used. One range writes
+// the block directly. Several write their partial sums to the workspace and
+// count themselves done; the last to finish (after a device-scope fence)
+// adds the partials in range order, so the result does not depend on timing.
 constexpr int OUT_CHUNK = 64;                   // rows per LDS stage (4 MFMA k-steps)
 constexpr int OUT_PITCH = OUT_CHUNK + 8;        // bf16 per staged head / dim line (bank spread)
 constexpr int OUT_MAX_S = 1024;                 // splits per sequence the prefix table holds
@@ -688,18 +695,32 @@ __device__ inline uint16_t bf16_bits_rne(float x) {  // exact-to-nearest-even fp
 }
 __device__ inline float bf16_value(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
+// One staged row of an output chunk: 32 value dims of the group (quarter sq
+// of the group's 128), the group scale, and the weights of 8 heads.
+struct OutRow {
+  uint4 v0, v1;
+  float sc;
+  float pw[8];
+};
+
 __global__ __launch_bounds__(256) void mla_out(MlaArgs a) {
   __shared__ __align__(16) uint16_t vt[128 * OUT_PITCH];            // [dim][row] bf16 values
   __shared__ __align__(16) uint16_t pt[3 * 32 * OUT_PITCH];         // [term][head][row] bf16 weight terms
   __shared__ int pre[OUT_MAX_S + 1];                                // exclusive prefix of kept rows per split
   __shared__ float mpart[256][8];                                   // kept-mass partials [thread][head slot]
   __shared__ long long cnt[4];
+  __shared__ int last;
 
   const int H = a.Hq;
   const int nhb = H / 32;
-  const int b = blockIdx.x / (nhb * 4);
-  const int rem = blockIdx.x - b * nhb * 4;
-  const int hb = rem >> 2, g = rem & 3;
+  const int R = a.R;
+  int blk = blockIdx.x;
+  const int rg = blk % R;
+  blk /= R;
+  const int g = blk & 3;
+  blk >>= 2;
+  const int hb = blk % nhb, b = blk / nhb;
+  const int obk = (b * nhb + hb) * 4 + g;          // output block index
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = a.S;
   const int64_t row0 = int64_t(b) * a.cap;
@@ -745,42 +766,60 @@ __global__ __launch_bounds__(256) void mla_out(MlaArgs a) {
     __syncthreads();
   }
   const int N = pre[OUT_MAX_S];
+  int nr = (N + kOutMinRows - 1) / kOutMinRows;    // row ranges in use (uniform over the block's workgroups)
+  nr = nr < 1 ? 1 : nr > R ? R : nr;
+  const bool active = rg < nr;
+  const int rbeg = active ? int(int64_t(N) * rg / nr) : 0;
+  const int rend = active ? int(int64_t(N) * (rg + 1) / nr) : 0;
 
   floatx16 acc = {};
   float mass[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) mass[j] = 0.f;
   const int col = lane & 31, kh = lane >> 5;
-  // staging roles: row r = tid / 4 of the chunk, quarter q = tid % 4
+  // staging roles: row sr of the chunk, quarter sq of the group's dims and
+  // heads 8sq..8sq+7; a thread's rows advance in order, so its split index
+  // only moves forward
   const int sr = tid >> 2, sq = tid & 3;
-  for (int c0 = 0; c0 < N; c0 += OUT_CHUNK) {
-    const int r = c0 + sr;
-    uint4 v0 = make_uint4(0u, 0u, 0u, 0u), v1 = v0;
-    float pw[8], sc = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) pw[j] = 0.f;
-    if (r < N) {
-      // split of global row r: the last split whose prefix is <= r (binary search)
+  int sp = 0;
+  {
+    const int r = rbeg + sr;                       // last split whose prefix is <= r (binary search)
+    if (r < rend) {
       int lo = 0, hi = S - 1;
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (pre[mid] <= r) lo = mid; else hi = mid - 1;
       }
-      const int64_t kb = int64_t(b) * S + lo;
-      const int64_t idx = kb * a.P + (r - pre[lo]);
+      sp = lo;
+    }
+  }
+  auto fetch = [&](int r, OutRow& o) {
+    o.v0 = make_uint4(0u, 0u, 0u, 0u);
+    o.v1 = o.v0;
+    o.sc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o.pw[j] = 0.f;
+    if (r < rend) {
+      while (sp + 1 < S && pre[sp + 1] <= r) ++sp;
+      const int64_t kb = int64_t(b) * S + sp;
+      const int64_t idx = kb * a.P + (r - pre[sp]);
       const int pos = a.kpos[idx];
       const uint8_t* vrow = a.kc + (row0 + pos) * D + 128 * g + 32 * sq;
-      v0 = *reinterpret_cast<const uint4*>(vrow);
-      v1 = *reinterpret_cast<const uint4*>(vrow + 16);
-      sc = reinterpret_cast<const float*>(a.ks + (row0 + pos) * (4 * NGROUPS))[g];
+      o.v0 = *reinterpret_cast<const uint4*>(vrow);
+      o.v1 = *reinterpret_cast<const uint4*>(vrow + 16);
+      o.sc = reinterpret_cast<const float*>(a.ks + (row0 + pos) * (4 * NGROUPS))[g];
       const float4 p0 = *reinterpret_cast<const float4*>(a.kp + idx * H + 32 * hb + 8 * sq);
       const float4 p1 = *reinterpret_cast<const float4*>(a.kp + idx * H + 32 * hb + 8 * sq + 4);
-      pw[0] = p0.x; pw[1] = p0.y; pw[2] = p0.z; pw[3] = p0.w;
-      pw[4] = p1.x; pw[5] = p1.y; pw[6] = p1.z; pw[7] = p1.w;
+      o.pw[0] = p0.x; o.pw[1] = p0.y; o.pw[2] = p0.z; o.pw[3] = p0.w;
+      o.pw[4] = p1.x; o.pw[5] = p1.y; o.pw[6] = p1.z; o.pw[7] = p1.w;
     }
+  };
+  OutRow cur, nxt;
+  fetch(rbeg + sr, cur);
+  for (int c0 = rbeg; c0 < rend; c0 += OUT_CHUNK) {
     // values: 32 dims of row sr -> bf16, transposed into vt[dim][row]
     {
-      const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      const uint32_t w[8] = {cur.v0.x, cur.v0.y, cur.v0.z, cur.v0.w, cur.v1.x, cur.v1.y, cur.v1.z, cur.v1.w};
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const uint32_t lo2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[k], 1.0f, false));
@@ -795,8 +834,8 @@ __global__ __launch_bounds__(256) void mla_out(MlaArgs a) {
     // weights: p * scale as three bf16 terms, transposed into pt[term][head][row]
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      mass[j] += pw[j];
-      const float x = pw[j] * sc;
+      mass[j] += cur.pw[j];
+      const float x = cur.pw[j] * cur.sc;
       const uint16_t t0 = bf16_bits_rne(x);
       const float r1 = x - bf16_value(t0);
       const uint16_t t1 = bf16_bits_rne(r1);
@@ -806,6 +845,7 @@ __global__ __launch_bounds__(256) void mla_out(MlaArgs a) {
       pt[(1 * 32 + h) * OUT_PITCH + sr] = t1;
       pt[(2 * 32 + h) * OUT_PITCH + sr] = t2;
     }
+    fetch(c0 + OUT_CHUNK + sr, nxt);                 // the next rows load during the products
     __syncthreads();
 #pragma unroll
     for (int ks = 0; ks < OUT_CHUNK / 16; ++ks) {
@@ -818,16 +858,24 @@ __global__ __launch_bounds__(256) void mla_out(MlaArgs a) {
       }
     }
     __syncthreads();                                 // the next chunk reuses vt / pt
+    cur = nxt;
   }
   // accumulator 4i+j of the lane: head 8i + 4kh + j, dim 32*wave + col of the group
-  float* ob = a.out + (int64_t(b) * H + 32 * hb) * DV + 128 * g + 32 * wave + col;
+  const int64_t ob_off = (int64_t(b) * H + 32 * hb) * DV + 128 * g + 32 * wave + col;
+  float* part = a.opart + (int64_t(obk) * R + rg) * 32 * 128 + 32 * wave + col;   // [32 heads][128 dims]
+  if (active) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ob[int64_t(8 * i + 4 * kh + j) * DV] = acc[4 * i + j];
-  if (g == 0) {
-    // kept mass of the 32 heads: thread t summed the rows t/4 (mod 64) of
-    // heads 8*(t%4)..+7; the 64 threads of a head are added in thread order
+      for (int j = 0; j < 4; ++j) {
+        const int h = 8 * i + 4 * kh + j;
+        if (nr == 1) a.out[ob_off + int64_t(h) * DV] = acc[4 * i + j];
+        else part[h * 128] = acc[4 * i + j];
+      }
+  }
+  // kept mass of the 32 heads (g == 0): thread t summed the rows t/4 (mod 64)
+  // of heads 8*(t%4)..+7; the 64 threads of a head are added in thread order
+  if (g == 0 && active) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) mpart[tid][j] = mass[j];
     __syncthreads();
@@ -835,10 +883,33 @@ __global__ __launch_bounds__(256) void mla_out(MlaArgs a) {
       const int q = tid >> 3, j = tid & 7;
       float m = 0.f;
       for (int t = q; t < 256; t += 4) m += mpart[t][j];
-      a.kept_mass[int64_t(b) * H + 32 * hb + 8 * q + j] = m;
+      if (nr == 1) a.kept_mass[int64_t(b) * H + 32 * hb + 8 * q + j] = m;
+      else a.mpart[(int64_t(b * nhb + hb) * R + rg) * 32 + 8 * q + j] = m;
     }
   }
-  if (hb == 0 && g == 0 && tid == 0) {
+  if (nr > 1 && active) {
+    // the last range of the block to finish adds the partials in range order
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) last = atomicAdd(&a.ocnt[obk], 1u) == uint32_t(nr - 1);
+    __syncthreads();
+    if (last) {
+      __threadfence();
+      const float* p0 = a.opart + int64_t(obk) * R * 32 * 128;
+      for (int e = tid; e < 32 * 128; e += 256) {
+        float v = 0.f;
+        for (int k = 0; k < nr; ++k) v += p0[int64_t(k) * 32 * 128 + e];
+        a.out[(int64_t(b) * H + 32 * hb + (e >> 7)) * DV + 128 * g + (e & 127)] = v;
+      }
+      if (g == 0 && tid < 32) {
+        float m = 0.f;
+        for (int k = 0; k < nr; ++k) m += a.mpart[(int64_t(b * nhb + hb) * R + k) * 32 + tid];
+        a.kept_mass[int64_t(b) * H + 32 * hb + tid] = m;
+      }
+      if (tid == 0) a.ocnt[obk] = 0u;                // ready for the next call
+    }
+  }
+  if (hb == 0 && g == 0 && rg == 0 && tid == 0) {
     a.bgstat[2 * b] = (unsigned long long)(cnt[0] + cnt[1] + cnt[2] + cnt[3]);
     a.bgstat[2 * b + 1] = (unsigned long long)N;
   }

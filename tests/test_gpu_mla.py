@@ -43,6 +43,21 @@ def test_mla_ragged(ctx):
     compare(inp, tau, g, r, po, mask=False)
 
 
+def test_mla_dense_row_ranges():
+    """Threshold 0 at ctx 20000: every row is kept, so each output block is
+    summed by three workgroups over unequal row ranges and the last one to
+    finish adds the partials; repeated calls must give the same bits (the
+    range counters reset themselves)."""
+    say("case mla dense row ranges: batch 2, 128 heads, ctx 20000, tau 0, 3 calls")
+    inp, tau = _case(0.0, batch=2, ctx=20000, hot=8)
+    g = run_gpu(inp, tau, q_bf16=True, repeat=3)
+    for o in g["outs"][1:]:
+        assert np.array_equal(o, g["outs"][0])
+    r, po = oracle_for(inp, tau)
+    compare(inp, tau, g, r, po, mask=False)
+    assert g["stats"]["rows_fetched"] == 2 * 20000
+
+
 def test_mla_every_fp8_code():
     say("case mla latent rows covering every non-NaN e4m3 code")
     inp, tau = _case(batch=1, ctx=256, hot=0, threshold=0.0)
