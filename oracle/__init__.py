@@ -25,7 +25,8 @@ Sources (cited by page title and section; the pages are the only authority):
 Modules: ``formats`` (fp64 pack/unpack of q8_0, q4_0, LUT3, FP8-B128),
 ``lloyd_max`` (the 8-level Lloyd-Max quantizer of N(0,1) that fills the LUT),
 ``attend`` (dequantize-then-attend with the skip rule, masks and statistics),
-``mp`` (an mpmath brute force for tiny contexts).
+``mp`` (an mpmath brute force for tiny contexts), ``kskip`` (how many key rows
+a provable score bound could leave out: the FAQ's future-work K-side skip).
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 (closed forms, invariants, a library routine or a textbook table). The pages
