@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -19,6 +20,8 @@ const void* gqa_kernel(int fmt, int G, bool run);
 size_t mla_lds_bytes(int H, int P, int S);
 const void* mla_scores_kernel(int H);
 const void* mla_out_kernel();
+size_t mla_out_dense_lds(int H);
+const void* mla_out_dense_kernel(int H);
 }  // namespace kvq
 
 namespace {
@@ -99,7 +102,10 @@ int32_t make_mla_plan(const kvq_cache* k, const kvq_launch* l, int32_t ctx_len, 
   plan->lds = lds;
   plan->nwg = k->batch * S;
   plan->threads = 4 * H;                                 // two waves per 32-head block
-  plan->R = kvq::mla_out_ranges(ctx_len);
+  // row ranges of the every-row-kept output: one workgroup per CU over the
+  // batch and its 64-head sets, at least 64 rows each
+  plan->R = int(std::max<int64_t>(
+      1, std::min<int64_t>({64, di.cus / (int64_t(k->batch) * std::max(1, H / 64)), (ctx_len + 63) / 64})));
   plan->mws = kvq::mla_ws_layout(k->batch, H, S, P, plan->R);
   plan->total = plan->mws.total;
   return KVQ_OK;
@@ -197,8 +203,11 @@ int32_t launch_mla(const void* q, const kvq_cache* kcache, const kvq_cache* vcac
   a.opart = reinterpret_cast<float*>(ws + plan.mws.opart);
   a.mpart = reinterpret_cast<float*>(ws + plan.mws.mpart);
   a.ocnt = reinterpret_cast<uint32_t*>(ws + plan.mws.ocnt);
+  a.done = reinterpret_cast<unsigned long long*>(ws + plan.mws.done);
   // threshold 0 keeps every row: the output contraction is split over row
-  // ranges; a positive threshold keeps few rows, one range per block
+  // ranges (mla_out_dense when all its workgroups fit on the GPU at once,
+  // else mla_out's per-block ranges); a positive threshold keeps few rows,
+  // one range per mla_out block
   a.R = threshold == 0.0f ? plan.R : 1;
   a.B = kcache->batch;
   a.Hq = l->q_heads;
@@ -218,7 +227,21 @@ int32_t launch_mla(const void* q, const kvq_cache* kcache, const kvq_cache* vcac
   (void)hipGetDevice(&dev);
   if (int64_t(per_cu) * device_info(dev).cus < plan.nwg) return KVQ_ERR_UNSUPPORTED;
   hipError_t e = launch(ks, plan.nwg, plan.threads, &a, plan.lds, l);
-  if (e == hipSuccess) e = launch(kvq::mla_out_kernel(), kcache->batch * (plan.G / 32) * 4 * a.R, 256, &a, 0, l);
+  if (e == hipSuccess) {
+    bool dense = false;
+    if (threshold == 0.0f) {
+      const void* kd = kvq::mla_out_dense_kernel(plan.G);
+      const size_t dl = kvq::mla_out_dense_lds(plan.G);
+      int pd = 0;
+      if (kd && dl <= size_t(device_info(dev).max_lds) &&
+          hipOccupancyMaxActiveBlocksPerMultiprocessor(&pd, kd, 256, dl) == hipSuccess &&
+          int64_t(pd) * device_info(dev).cus >= int64_t(kcache->batch) * (plan.G / 64) * a.R) {
+        e = launch(kd, kcache->batch * (plan.G / 64) * a.R, 256, &a, dl, l);
+        dense = true;
+      }
+    }
+    if (!dense) e = launch(kvq::mla_out_kernel(), kcache->batch * (plan.G / 32) * 4 * a.R, 256, &a, 0, l);
+  }
   if (e != hipSuccess) {
     (void)hipGetLastError();
     return KVQ_ERR_LAUNCH;

@@ -107,7 +107,8 @@ struct MlaArgs {
   float* opart;                   // [B][H/32][4][R][32][128] output partials of row ranges
   float* mpart;                   // [B][H/32][R][32] kept-mass partials of row ranges
   uint32_t* ocnt;                 // [B][H/32][4] row ranges finished (0 between calls)
-  int32_t R;                      // row ranges per output block launched
+  unsigned long long* done;       // tagged [B][H/64][R]: every-row-kept ranges that wrote their partials
+  int32_t R;                      // row ranges launched (per output block, or per sequence at threshold 0)
   int32_t B, Hq, ctx, cap;
   int32_t S, P;
   float sigma_log2e;
@@ -116,7 +117,7 @@ struct MlaArgs {
 };
 
 struct MlaLayout {
-  int64_t kept_mass, bgstat, split_ml, kcount, kpairs, kpos, kp, opart, mpart, ocnt, total;
+  int64_t kept_mass, bgstat, split_ml, kcount, kpairs, kpos, kp, opart, mpart, ocnt, done, total;
 };
 
 // The first two regions match ws_layout() so kvq_stats reads both families alike.
@@ -133,20 +134,16 @@ inline MlaLayout mla_ws_layout(int B, int H, int S, int P, int R) {
   w.opart = off;     off = align256(off + int64_t(B) * (H / 32) * 4 * R * 32 * 128 * 4);
   w.mpart = off;     off = align256(off + int64_t(B) * (H / 32) * R * 32 * 4);
   w.ocnt = off;      off = align256(off + int64_t(B) * (H / 32) * 4 * 4);
+  w.done = off;      off = align256(off + int64_t(B) * (H >= 64 ? H / 64 : 1) * R * 8);
   w.total = off;
   return w;
 }
 
 constexpr int kStamps = 10;       // phase stamps per workgroup (7..9 split the V pass)
 
-// Latent output contraction: row ranges launched per (sequence, 32 heads,
-// 128 value dims) block, from the context length (ranges of at least
-// kOutMinRows kept rows are used; the rest exit at once).
+// Latent output contraction at threshold 0: mla_out's per-block row ranges
+// hold at least kOutMinRows rows (the rest of the launched ranges exit at once).
 constexpr int kOutMinRows = 2048;
-inline int mla_out_ranges(int ctx) {
-  const int r = (ctx + 4 * kOutMinRows - 1) / (4 * kOutMinRows);
-  return r < 1 ? 1 : r > 8 ? 8 : r;
-}
 
 // Floats of the first LDS region of the grouped kernel: scores [G][P], the
 // cross-wave reduction [kWaves][G][128], and the merge's slice partials

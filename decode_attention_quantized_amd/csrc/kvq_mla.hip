@@ -924,6 +924,258 @@ __global__ __launch_bounds__(256) void mla_out(MlaArgs a) {
   }
 }
 
+// ----------------------------------------------------------------------------- out, every row kept
+// Threshold 0 keeps every row, and the blocks of mla_out would each convert
+// the same value rows and split the same weights. Here one workgroup takes a
+// range of rows of a sequence for 64 of its heads and all 512 value dims:
+// wave w owns heads 32(w/2)..+31 of the 64 and value dims 256(w%2)..+255 (8
+// MFMA column tiles of 32 dims, two value groups; one wave per SIMD, whose
+// registers hold its 128 fp32 accumulators and the next chunk's loads). A
+// 64-row chunk is staged once: values converted to bf16 (exact) and
+// transposed [dim][row], weights transposed [head][row] in fp32, group
+// scales [row][group]. Each wave forms its A operand from its heads' weights
+// times its group's scale, split into two bf16 terms: the product rounded to
+// nearest, then its remainder (exact in fp32) rounded to nearest, so the pair
+// carries it within 2^-17 relative (mla_out keeps a third term; here the
+// conversions, not the products, bound the chunk time).
+// The R ranges of a sequence write fp32 partial sums, mark themselves done
+// with a tagged word (after a device-scope fence), wait for the other ranges
+// and then each adds, in range order, one slice of the sequence's outputs
+// (all R workgroups of a sequence are resident: the plan launches at most one
+// per CU).
+constexpr int DN_CHUNK = 64;                     // rows per stage
+constexpr int DN_VP = DN_CHUNK + 8;              // bf16 per staged dim line
+constexpr int DN_SEG = 2048;                     // rows whose (slot, position) are looked up at once
+constexpr int DN_PP = DN_CHUNK + 4;              // floats per staged head line (16-byte rows, 4-way banks)
+
+size_t mla_out_dense_lds(int) {
+  return size_t(DV) * DN_VP * 2 + size_t(64) * DN_PP * 4 + size_t(DN_CHUNK) * 4 * 4 + size_t(OUT_MAX_S + 4) * 4 +
+         size_t(DN_SEG) * 8;
+}
+
+constexpr int DN_HW = 64;                        // heads per workgroup
+
+__global__ __launch_bounds__(256) void mla_out_dense(MlaArgs a) {
+  constexpr int HW = DN_HW, NT = 256;
+  constexpr int NPV = DN_CHUNK * 32 / NT;          // 16-byte value pieces per thread and chunk
+  constexpr int NPW = DN_CHUNK * (HW / 8) / NT;    // 8-head weight pieces per thread and chunk
+  static_assert(NPV * NT == DN_CHUNK * 32 && NPW * NT == DN_CHUNK * (HW / 8), "staging roles");
+  extern __shared__ __align__(16) unsigned char dsm[];
+  uint16_t* vt = reinterpret_cast<uint16_t*>(dsm);                                   // [512][DN_VP] bf16 values
+  float* pf = reinterpret_cast<float*>(dsm + size_t(DV) * DN_VP * 2);               // [HW][DN_PP] weights
+  float* gsc = pf + HW * DN_PP;                                                      // [DN_CHUNK][4] group scales
+  int* pre = reinterpret_cast<int*>(gsc + DN_CHUNK * 4);                             // [OUT_MAX_S + 4]
+  int2* rowtab = reinterpret_cast<int2*>(pre + OUT_MAX_S + 4);                       // [DN_SEG] (slot, position)
+
+  const int R = a.R, H = a.Hq, NHH = H / HW;      // head halves (or the one 64-head set) per sequence
+  const int rg = blockIdx.x % R, bh = blockIdx.x / R, hh = bh % NHH, b = bh / NHH;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hb = wave >> 1, half = wave & 1;
+  const int S = a.S;
+  const int64_t row0 = int64_t(b) * a.cap;
+  const uint32_t epoch = __hip_atomic_load(&a.hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+
+  // kept rows per split (every row here, counted the same way) -> exclusive prefix
+  {
+    int c[4] = {0, 0, 0, 0};
+    if (tid < OUT_MAX_S / 4)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int sp = 4 * tid + k;
+        c[k] = sp < S ? a.kcount[int64_t(b) * S + sp] : 0;
+      }
+    const int local = c[0] + c[1] + c[2] + c[3];
+    int incl = local;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63 && wave < 4) pre[OUT_MAX_S + wave] = incl;    // totals of the four counting waves
+    __syncthreads();
+    if (tid < OUT_MAX_S / 4) {
+      int run = incl - local;
+      for (int w = 0; w < wave; ++w) run += pre[OUT_MAX_S + w];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        pre[4 * tid + k] = run;
+        run += c[k];
+      }
+    }
+    __syncthreads();
+  }
+  const int N = pre[OUT_MAX_S] + pre[OUT_MAX_S + 1] + pre[OUT_MAX_S + 2] + pre[OUT_MAX_S + 3];
+  const int rbeg = int(int64_t(N) * rg / R), rend = int(int64_t(N) * (rg + 1) / R);
+
+  floatx16 acc[8] = {};
+  float msum = 0.f;                                   // weights of head 32hb + (lane & 31), this lane's rows (half 0)
+  const int col = lane & 31, kh = lane >> 5;
+  // staged data of one chunk, loaded a chunk ahead: value pieces (row pv&63,
+  // bytes 16*(pv>>6)..), 8-head weight pieces (row pw&63, heads 8*(pw>>6)..)
+  // and, for wave 0, the row's four value-group scales; consecutive lanes take
+  // consecutive rows, so the transposed LDS writes of a wave are contiguous
+  struct Stage { uint4 v[NPV]; float4 w[2 * NPW]; float4 sc; };
+  const int wr = tid & (DN_CHUNK - 1);             // row of this thread's weight pieces and scales
+  auto load_stage = [&](int c0, int seg0, int segn, Stage& st) {
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      const int pv = tid + i * NT, rr = pv & (DN_CHUNK - 1), q16 = pv / DN_CHUNK;
+      const int rs = c0 + rr - seg0;                 // row within the segment
+      st.v[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (rs < segn) st.v[i] = *reinterpret_cast<const uint4*>(a.kc + (row0 + rowtab[rs].y) * D + 16 * q16);
+    }
+    const int rs = c0 + wr - seg0;
+    st.sc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < NPW; ++i) {
+      const int h8 = (tid + i * NT) / DN_CHUNK;
+      st.w[2 * i] = st.w[2 * i + 1] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (rs < segn) {
+        const int64_t idx = int64_t(rowtab[rs].x);
+        st.w[2 * i] = *reinterpret_cast<const float4*>(a.kp + idx * H + HW * hh + 8 * h8);
+        st.w[2 * i + 1] = *reinterpret_cast<const float4*>(a.kp + idx * H + HW * hh + 8 * h8 + 4);
+      }
+    }
+    if (tid < DN_CHUNK && rs < segn)
+      st.sc = *reinterpret_cast<const float4*>(a.ks + (row0 + rowtab[rs].y) * (4 * NGROUPS));
+  };
+  auto write_stage = [&](const Stage& st) {
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      const int pv = tid + i * NT, rr = pv & (DN_CHUNK - 1), q16 = pv / DN_CHUNK;
+      const uint32_t w[4] = {st.v[i].x, st.v[i].y, st.v[i].z, st.v[i].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t lo2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[k], 1.0f, false));
+        const uint32_t hi2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[k], 1.0f, true));
+        const int d = 16 * q16 + 4 * k;
+        vt[(d + 0) * DN_VP + rr] = uint16_t(lo2);
+        vt[(d + 1) * DN_VP + rr] = uint16_t(lo2 >> 16);
+        vt[(d + 2) * DN_VP + rr] = uint16_t(hi2);
+        vt[(d + 3) * DN_VP + rr] = uint16_t(hi2 >> 16);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NPW; ++i) {
+      const int h8 = (tid + i * NT) / DN_CHUNK;
+      const float4 u = st.w[2 * i], v = st.w[2 * i + 1];
+      const float pv8[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pf[(8 * h8 + j) * DN_PP + wr] = pv8[j];
+    }
+    if (tid < DN_CHUNK) *reinterpret_cast<float4*>(gsc + wr * 4) = st.sc;
+  };
+
+  for (int seg0 = rbeg; seg0 < rend; seg0 += DN_SEG) {
+    const int segn = min(DN_SEG, rend - seg0);
+    // (slot in the split's published rows, position) of every row of the segment
+    __syncthreads();                                   // the previous segment's table is no longer read
+    for (int rs = tid; rs < segn; rs += NT) {
+      const int r = seg0 + rs;
+      int lo = 0, hi = S - 1;                          // the last split whose prefix is <= r
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pre[mid] <= r) lo = mid; else hi = mid - 1;
+      }
+      const int idx = (b * S + lo) * a.P + (r - pre[lo]);
+      rowtab[rs] = make_int2(idx, a.kpos[idx]);
+    }
+    __syncthreads();
+    Stage st;                                          // one set of registers: written to LDS, then refilled
+    load_stage(seg0, seg0, segn, st);
+    for (int c0 = seg0; c0 < seg0 + segn; c0 += DN_CHUNK) {
+      write_stage(st);
+      if (c0 + DN_CHUNK < seg0 + segn) load_stage(c0 + DN_CHUNK, seg0, segn, st);
+      __syncthreads();
+      // products: 4 k-steps of 16 rows; lane (col, kh) takes head 32hb + col
+      // and rows 16ks + 8kh .. + 7 of the chunk (not unrolled: the 128
+      // accumulators leave little room for operands of several steps)
+#pragma unroll 1
+      for (int ks = 0; ks < DN_CHUNK / 16; ++ks) {
+        const int k0 = 16 * ks + 8 * kh;
+        const float* ph = pf + (32 * hb + col) * DN_PP + k0;
+        const float4 pa = *reinterpret_cast<const float4*>(ph), pb = *reinterpret_cast<const float4*>(ph + 4);
+        const float pw[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+        if (half == 0)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) msum += pw[i];
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg) {             // the wave's two value groups
+          const int g = 2 * half + gg;
+          bf16x8 ah, al;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float x = pw[i] * gsc[(k0 + i) * 4 + g];
+            const __bf16 h = __bf16(x);                // v_cvt_pk_bf16_f32: round to nearest even
+            ah[i] = h;
+            al[i] = __bf16(x - float(h));
+          }
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&vt[(128 * g + 32 * t + col) * DN_VP + k0]);
+            acc[4 * gg + t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bv, acc[4 * gg + t], 0, 0, 0);
+            acc[4 * gg + t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bv, acc[4 * gg + t], 0, 0, 0);
+          }
+        }
+      }
+      __syncthreads();                                 // the next chunk reuses the staging
+    }
+  }
+  // partial of this range: accumulator 4i+j of tile t -> head HW*hh + 32hb + 8i + 4kh + j, dim 256half + 32t + col
+  float* part = a.opart + (int64_t(b) * R + rg) * H * DV + int64_t(HW * hh) * DV;
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        part[(32 * hb + 8 * i + 4 * kh + j) * DV + 256 * half + 32 * t + col] = acc[t][4 * i + j];
+  if (half == 0) {                                     // head 32hb + col: the two lane halves' rows
+    const float other = __shfl_xor(msum, 32);
+    if (kh == 0) a.mpart[(int64_t(b) * R + rg) * H + HW * hh + 32 * hb + col] = msum + other;
+  }
+  __threadfence();
+  __syncthreads();
+  u64* done = a.done + int64_t(bh) * R;
+  if (tid == 0) put_tagged_f(done + rg, epoch, 1.f);
+  // wait for the other ranges of these heads, then add one slice of their outputs
+  for (int k = tid; k < R; k += NT) settle_f(peek(done + k), done + k, epoch, a.hdr);
+  __syncthreads();
+  __threadfence();
+  const float* p0 = a.opart + int64_t(b) * R * H * DV + int64_t(HW * hh) * DV;
+  const int e0 = int(int64_t(HW) * DV * rg / R), e1 = int(int64_t(HW) * DV * (rg + 1) / R);
+  for (int e = e0 + tid; e < e1; e += NT) {
+    float v = 0.f;
+    for (int k = 0; k < R; ++k) v += p0[int64_t(k) * H * DV + e];
+    a.out[(int64_t(b) * H + HW * hh) * DV + e] = v;
+  }
+  if (rg == 0 && tid < HW) {
+    float m = 0.f;
+    for (int k = 0; k < R; ++k) m += a.mpart[(int64_t(b) * R + k) * H + HW * hh + tid];
+    a.kept_mass[int64_t(b) * H + HW * hh + tid] = m;
+  }
+  if (rg == 0 && hh == 0 && tid == 0) {
+    long long pairs = 0;
+    for (int sp = 0; sp < S; ++sp) pairs += a.kpairs[int64_t(b) * S + sp];
+    a.bgstat[2 * b] = (unsigned long long)pairs;
+    a.bgstat[2 * b + 1] = (unsigned long long)N;
+  }
+  // the last workgroup advances the epoch for the next call
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(&a.hdr->groups_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev == gridDim.x - 1) {
+      __hip_atomic_store(&a.hdr->groups_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.hdr->epoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// 32 heads have no dense variant; they use mla_out's ranges.
+const void* mla_out_dense_kernel(int H) {
+  return (H == 64 || H == 128) ? reinterpret_cast<const void*>(&mla_out_dense) : nullptr;
+}
+
 // LDS bytes of mla_scores (every region is a multiple of 16 bytes).
 size_t mla_lds_bytes(int H, int P, int S) {
   const int NLT = P / LTILE;
