@@ -932,9 +932,16 @@ __global__ __launch_bounds__(256) void mla_out(MlaArgs a) {
 // MFMA column tiles of 32 dims, two value groups; one wave per SIMD, whose
 // registers hold its 128 fp32 accumulators and the next chunk's loads). A
 // 64-row chunk is staged once: values converted to bf16 (exact) and
-// transposed [dim][row], weights transposed [head][row] in fp32, group
-// scales [row][group]. Each wave forms its A operand from its heads' weights
-// times its group's scale, split into two bf16 terms: the product rounded to
+// transposed [dim][slot], weights transposed [head][slot] in fp32, group
+// scales [slot][group]. Loads are coalesced (32 lanes read one 512-byte value
+// row, 16 lanes one row's 64 weights). The chunk's rows take the MFMA k
+// order slot 8b + m <- row b + 8m: a thread loads rows b, b+8, .., b+56 of
+// 16 dims, so each of its LDS writes is one 16-byte unit (8 slots of one
+// dim). Unit (dim d, block b) sits at 8 * (d ^ ((d >> 4) & 1)) +
+// ((b + (d >> 1) + (d >> 5)) & 7): the 16 lanes of a read (consecutive dims,
+// one block) and of a write (dims 16 apart, one block) fall in 16 different
+// bank groups. Each wave forms its A operand from its heads' weights times
+// its group's scale, split into two bf16 terms: the product rounded to
 // nearest, then its remainder (exact in fp32) rounded to nearest, so the pair
 // carries it within 2^-17 relative (mla_out keeps a third term; here the
 // conversions, not the products, bound the chunk time).
@@ -944,25 +951,29 @@ __global__ __launch_bounds__(256) void mla_out(MlaArgs a) {
 // (all R workgroups of a sequence are resident: the plan launches at most one
 // per CU).
 constexpr int DN_CHUNK = 64;                     // rows per stage
-constexpr int DN_VP = DN_CHUNK + 8;              // bf16 per staged dim line
 constexpr int DN_SEG = 2048;                     // rows whose (slot, position) are looked up at once
-constexpr int DN_PP = DN_CHUNK + 4;              // floats per staged head line (16-byte rows, 4-way banks)
+constexpr int DN_PP = DN_CHUNK + 4;              // floats per staged head line (16-byte rows)
 
 size_t mla_out_dense_lds(int) {
-  return size_t(DV) * DN_VP * 2 + size_t(64) * DN_PP * 4 + size_t(DN_CHUNK) * 4 * 4 + size_t(OUT_MAX_S + 4) * 4 +
+  return size_t(DV) * DN_CHUNK * 2 + size_t(64) * DN_PP * 4 + size_t(DN_CHUNK) * 4 * 4 + size_t(OUT_MAX_S + 4) * 4 +
          size_t(DN_SEG) * 8;
 }
 
 constexpr int DN_HW = 64;                        // heads per workgroup
 
+__device__ inline int dn_unit(int d, int b) {    // 16-byte unit of (value dim d, block b)
+  return 8 * (d ^ ((d >> 4) & 1)) + ((b + (d >> 1) + (d >> 5)) & 7);
+}
+__device__ inline int dn_slot(int r) { return 8 * (r & 7) + (r >> 3); }   // chunk row -> MFMA k slot
+
 __global__ __launch_bounds__(256) void mla_out_dense(MlaArgs a) {
   constexpr int HW = DN_HW, NT = 256;
   constexpr int NPV = DN_CHUNK * 32 / NT;          // 16-byte value pieces per thread and chunk
-  constexpr int NPW = DN_CHUNK * (HW / 8) / NT;    // 8-head weight pieces per thread and chunk
-  static_assert(NPV * NT == DN_CHUNK * 32 && NPW * NT == DN_CHUNK * (HW / 8), "staging roles");
+  constexpr int NPW = DN_CHUNK * (HW / 4) / NT;    // 4-head weight pieces per thread and chunk
+  static_assert(NPV == 8 && NPW * NT == DN_CHUNK * (HW / 4), "staging roles");
   extern __shared__ __align__(16) unsigned char dsm[];
-  uint16_t* vt = reinterpret_cast<uint16_t*>(dsm);                                   // [512][DN_VP] bf16 values
-  float* pf = reinterpret_cast<float*>(dsm + size_t(DV) * DN_VP * 2);               // [HW][DN_PP] weights
+  uint4* vt = reinterpret_cast<uint4*>(dsm);                                         // [512 x 8] units of 8 bf16
+  float* pf = reinterpret_cast<float*>(dsm + size_t(DV) * DN_CHUNK * 2);            // [HW][DN_PP] weights
   float* gsc = pf + HW * DN_PP;                                                      // [DN_CHUNK][4] group scales
   int* pre = reinterpret_cast<int*>(gsc + DN_CHUNK * 4);                             // [OUT_MAX_S + 4]
   int2* rowtab = reinterpret_cast<int2*>(pre + OUT_MAX_S + 4);                       // [DN_SEG] (slot, position)
@@ -1010,75 +1021,87 @@ __global__ __launch_bounds__(256) void mla_out_dense(MlaArgs a) {
   floatx16 acc[8] = {};
   float msum = 0.f;                                   // weights of head 32hb + (lane & 31), this lane's rows (half 0)
   const int col = lane & 31, kh = lane >> 5;
-  // staged data of one chunk, loaded a chunk ahead: value pieces (row pv&63,
-  // bytes 16*(pv>>6)..), 8-head weight pieces (row pw&63, heads 8*(pw>>6)..)
-  // and, for wave 0, the row's four value-group scales; consecutive lanes take
-  // consecutive rows, so the transposed LDS writes of a wave are contiguous
-  struct Stage { uint4 v[NPV]; float4 w[2 * NPW]; float4 sc; };
-  const int wr = tid & (DN_CHUNK - 1);             // row of this thread's weight pieces and scales
+  // staged data of one chunk, loaded a chunk ahead: value pieces (row
+  // tid/32 + 8i, bytes 16 * (tid % 32)..), 4-head weight pieces (row
+  // (tid + 256i) / 16, heads 4 * (tid % 16)..) and, for the first 64 threads,
+  // the four value-group scales of row tid
+  struct Stage { uint4 v[NPV]; float4 w[NPW]; float4 sc; };
+  const int vb = tid >> 5, vq = tid & 31;          // value block (row within 8) and 16-dim piece
   auto load_stage = [&](int c0, int seg0, int segn, Stage& st) {
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
-      const int pv = tid + i * NT, rr = pv & (DN_CHUNK - 1), q16 = pv / DN_CHUNK;
-      const int rs = c0 + rr - seg0;                 // row within the segment
+      const int rs = c0 + vb + 8 * i - seg0;         // row within the segment
       st.v[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (rs < segn) st.v[i] = *reinterpret_cast<const uint4*>(a.kc + (row0 + rowtab[rs].y) * D + 16 * q16);
+      if (rs < segn) st.v[i] = *reinterpret_cast<const uint4*>(a.kc + (row0 + rowtab[rs].y) * D + 16 * vq);
     }
-    const int rs = c0 + wr - seg0;
-    st.sc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int i = 0; i < NPW; ++i) {
-      const int h8 = (tid + i * NT) / DN_CHUNK;
-      st.w[2 * i] = st.w[2 * i + 1] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (rs < segn) {
-        const int64_t idx = int64_t(rowtab[rs].x);
-        st.w[2 * i] = *reinterpret_cast<const float4*>(a.kp + idx * H + HW * hh + 8 * h8);
-        st.w[2 * i + 1] = *reinterpret_cast<const float4*>(a.kp + idx * H + HW * hh + 8 * h8 + 4);
-      }
+      const int pw = tid + i * NT, rs = c0 + (pw >> 4) - seg0;
+      st.w[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (rs < segn)
+        st.w[i] = *reinterpret_cast<const float4*>(a.kp + int64_t(rowtab[rs].x) * H + HW * hh + 4 * (pw & 15));
     }
+    const int rs = c0 + tid - seg0;
+    st.sc = make_float4(0.f, 0.f, 0.f, 0.f);
     if (tid < DN_CHUNK && rs < segn)
       st.sc = *reinterpret_cast<const float4*>(a.ks + (row0 + rowtab[rs].y) * (4 * NGROUPS));
   };
   auto write_stage = [&](const Stage& st) {
+    // rows vb + 8i of dims 16vq + 2j, +1: pack the two dims' bf16 over the 8 rows
 #pragma unroll
-    for (int i = 0; i < NPV; ++i) {
-      const int pv = tid + i * NT, rr = pv & (DN_CHUNK - 1), q16 = pv / DN_CHUNK;
-      const uint32_t w[4] = {st.v[i].x, st.v[i].y, st.v[i].z, st.v[i].w};
+    for (int j = 0; j < 8; ++j) {
+      uint32_t pr[8];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t lo2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[k], 1.0f, false));
-        const uint32_t hi2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[k], 1.0f, true));
-        const int d = 16 * q16 + 4 * k;
-        vt[(d + 0) * DN_VP + rr] = uint16_t(lo2);
-        vt[(d + 1) * DN_VP + rr] = uint16_t(lo2 >> 16);
-        vt[(d + 2) * DN_VP + rr] = uint16_t(hi2);
-        vt[(d + 3) * DN_VP + rr] = uint16_t(hi2 >> 16);
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t w = j < 2 ? st.v[i].x : j < 4 ? st.v[i].y : j < 6 ? st.v[i].z : st.v[i].w;
+        pr[i] = __builtin_bit_cast(uint32_t, (j & 1) ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                                                     : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
       }
+      uint4 lo, hi;                                   // dim 16vq + 2j (low halves), + 1 (high halves)
+      lo.x = __builtin_amdgcn_perm(pr[1], pr[0], 0x05040100u);
+      lo.y = __builtin_amdgcn_perm(pr[3], pr[2], 0x05040100u);
+      lo.z = __builtin_amdgcn_perm(pr[5], pr[4], 0x05040100u);
+      lo.w = __builtin_amdgcn_perm(pr[7], pr[6], 0x05040100u);
+      hi.x = __builtin_amdgcn_perm(pr[1], pr[0], 0x07060302u);
+      hi.y = __builtin_amdgcn_perm(pr[3], pr[2], 0x07060302u);
+      hi.z = __builtin_amdgcn_perm(pr[5], pr[4], 0x07060302u);
+      hi.w = __builtin_amdgcn_perm(pr[7], pr[6], 0x07060302u);
+      const int d = 16 * vq + 2 * j;
+      vt[dn_unit(d, vb)] = lo;
+      vt[dn_unit(d + 1, vb)] = hi;
     }
 #pragma unroll
     for (int i = 0; i < NPW; ++i) {
-      const int h8 = (tid + i * NT) / DN_CHUNK;
-      const float4 u = st.w[2 * i], v = st.w[2 * i + 1];
-      const float pv8[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) pf[(8 * h8 + j) * DN_PP + wr] = pv8[j];
+      const int pw = tid + i * NT, sl = dn_slot(pw >> 4), h4 = pw & 15;
+      pf[(4 * h4 + 0) * DN_PP + sl] = st.w[i].x;
+      pf[(4 * h4 + 1) * DN_PP + sl] = st.w[i].y;
+      pf[(4 * h4 + 2) * DN_PP + sl] = st.w[i].z;
+      pf[(4 * h4 + 3) * DN_PP + sl] = st.w[i].w;
     }
-    if (tid < DN_CHUNK) *reinterpret_cast<float4*>(gsc + wr * 4) = st.sc;
+    if (tid < DN_CHUNK) *reinterpret_cast<float4*>(gsc + dn_slot(tid) * 4) = st.sc;
   };
 
   for (int seg0 = rbeg; seg0 < rend; seg0 += DN_SEG) {
     const int segn = min(DN_SEG, rend - seg0);
     // (slot in the split's published rows, position) of every row of the segment
     __syncthreads();                                   // the previous segment's table is no longer read
-    for (int rs = tid; rs < segn; rs += NT) {
-      const int r = seg0 + rs;
-      int lo = 0, hi = S - 1;                          // the last split whose prefix is <= r
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (pre[mid] <= r) lo = mid; else hi = mid - 1;
+    {
+      int idx[DN_SEG / NT], pos[DN_SEG / NT];
+#pragma unroll
+      for (int i = 0; i < DN_SEG / NT; ++i) {
+        const int r = seg0 + min(tid + i * NT, segn - 1);
+        int lo = 0, hi = S - 1;                        // the last split whose prefix is <= r
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (pre[mid] <= r) lo = mid; else hi = mid - 1;
+        }
+        idx[i] = (b * S + lo) * a.P + (r - pre[lo]);
       }
-      const int idx = (b * S + lo) * a.P + (r - pre[lo]);
-      rowtab[rs] = make_int2(idx, a.kpos[idx]);
+#pragma unroll
+      for (int i = 0; i < DN_SEG / NT; ++i) pos[i] = a.kpos[idx[i]];     // one batch of loads
+#pragma unroll
+      for (int i = 0; i < DN_SEG / NT; ++i)
+        if (tid + i * NT < segn) rowtab[tid + i * NT] = make_int2(idx[i], pos[i]);
     }
     __syncthreads();
     Stage st;                                          // one set of registers: written to LDS, then refilled
@@ -1087,8 +1110,8 @@ __global__ __launch_bounds__(256) void mla_out_dense(MlaArgs a) {
       write_stage(st);
       if (c0 + DN_CHUNK < seg0 + segn) load_stage(c0 + DN_CHUNK, seg0, segn, st);
       __syncthreads();
-      // products: 4 k-steps of 16 rows; lane (col, kh) takes head 32hb + col
-      // and rows 16ks + 8kh .. + 7 of the chunk (not unrolled: the 128
+      // products: 4 k-steps of 16 slots; lane (col, kh) takes head 32hb + col
+      // and slots 16ks + 8kh .. + 7 of the chunk (not unrolled: the 128
       // accumulators leave little room for operands of several steps)
 #pragma unroll 1
       for (int ks = 0; ks < DN_CHUNK / 16; ++ks) {
@@ -1112,7 +1135,7 @@ __global__ __launch_bounds__(256) void mla_out_dense(MlaArgs a) {
           }
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&vt[(128 * g + 32 * t + col) * DN_VP + k0]);
+            const bf16x8 bv = __builtin_bit_cast(bf16x8, vt[dn_unit(128 * g + 32 * t + col, 2 * ks + kh)]);
             acc[4 * gg + t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bv, acc[4 * gg + t], 0, 0, 0);
             acc[4 * gg + t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bv, acc[4 * gg + t], 0, 0, 0);
           }
@@ -1142,23 +1165,50 @@ __global__ __launch_bounds__(256) void mla_out_dense(MlaArgs a) {
   for (int k = tid; k < R; k += NT) settle_f(peek(done + k), done + k, epoch, a.hdr);
   __syncthreads();
   __threadfence();
-  const float* p0 = a.opart + int64_t(b) * R * H * DV + int64_t(HW * hh) * DV;
-  const int e0 = int(int64_t(HW) * DV * rg / R), e1 = int(int64_t(HW) * DV * (rg + 1) / R);
+  // slices in float4 units; the R partials of an element are loaded eight at
+  // a time and added in range order (the loads of a batch are in flight together)
+  const float4* p0 = reinterpret_cast<const float4*>(a.opart + int64_t(b) * R * H * DV + int64_t(HW * hh) * DV);
+  const int64_t pstride = int64_t(H) * DV / 4;
+  const int e0 = int(int64_t(HW) * DV / 4 * rg / R), e1 = int(int64_t(HW) * DV / 4 * (rg + 1) / R);
   for (int e = e0 + tid; e < e1; e += NT) {
-    float v = 0.f;
-    for (int k = 0; k < R; ++k) v += p0[int64_t(k) * H * DV + e];
-    a.out[(int64_t(b) * H + HW * hh) * DV + e] = v;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    int k = 0;
+    for (; k + 8 <= R; k += 8) {
+      float4 t[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t[u] = p0[(k + u) * pstride + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) { v.x += t[u].x; v.y += t[u].y; v.z += t[u].z; v.w += t[u].w; }
+    }
+    for (; k < R; ++k) {
+      const float4 t = p0[k * pstride + e];
+      v.x += t.x; v.y += t.y; v.z += t.z; v.w += t.w;
+    }
+    reinterpret_cast<float4*>(a.out + (int64_t(b) * H + HW * hh) * DV)[e] = v;
   }
-  if (rg == 0 && tid < HW) {
+  if (rg == 0 && tid < HW) {                          // kept mass of head HW*hh + tid, ranges in order
+    const float* mp = a.mpart + int64_t(b) * R * H + HW * hh + tid;
     float m = 0.f;
-    for (int k = 0; k < R; ++k) m += a.mpart[(int64_t(b) * R + k) * H + HW * hh + tid];
+    int k = 0;
+    for (; k + 8 <= R; k += 8) {
+      float t[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t[u] = mp[int64_t(k + u) * H];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) m += t[u];
+    }
+    for (; k < R; ++k) m += mp[int64_t(k) * H];
     a.kept_mass[int64_t(b) * H + HW * hh + tid] = m;
   }
-  if (rg == 0 && hh == 0 && tid == 0) {
+  if (rg == 0 && hh == 0 && wave == 0) {              // kept pairs of the sequence (integer sum: any order)
     long long pairs = 0;
-    for (int sp = 0; sp < S; ++sp) pairs += a.kpairs[int64_t(b) * S + sp];
-    a.bgstat[2 * b] = (unsigned long long)pairs;
-    a.bgstat[2 * b + 1] = (unsigned long long)N;
+    for (int sp = lane; sp < S; sp += 64) pairs += a.kpairs[int64_t(b) * S + sp];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) pairs += __shfl_xor(pairs, o);
+    if (lane == 0) {
+      a.bgstat[2 * b] = (unsigned long long)pairs;
+      a.bgstat[2 * b + 1] = (unsigned long long)N;
+    }
   }
   // the last workgroup advances the epoch for the next call
   __syncthreads();
