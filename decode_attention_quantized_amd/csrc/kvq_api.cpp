@@ -234,9 +234,9 @@ int32_t launch_mla(const void* q, const kvq_cache* kcache, const kvq_cache* vcac
       const size_t dl = kvq::mla_out_dense_lds(plan.G);
       int pd = 0;
       if (kd && dl <= size_t(device_info(dev).max_lds) &&
-          hipOccupancyMaxActiveBlocksPerMultiprocessor(&pd, kd, 256, dl) == hipSuccess &&
+          hipOccupancyMaxActiveBlocksPerMultiprocessor(&pd, kd, kvq::kDenseOutThreads, dl) == hipSuccess &&
           int64_t(pd) * device_info(dev).cus >= int64_t(kcache->batch) * (plan.G / 64) * a.R) {
-        e = launch(kd, kcache->batch * (plan.G / 64) * a.R, 256, &a, dl, l);
+        e = launch(kd, kcache->batch * (plan.G / 64) * a.R, kvq::kDenseOutThreads, &a, dl, l);
         dense = true;
       }
     }

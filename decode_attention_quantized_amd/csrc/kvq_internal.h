@@ -144,6 +144,7 @@ constexpr int kStamps = 10;       // phase stamps per workgroup (7..9 split the 
 // Latent output contraction at threshold 0: mla_out's per-block row ranges
 // hold at least kOutMinRows rows (the rest of the launched ranges exit at once).
 constexpr int kOutMinRows = 2048;
+constexpr int kDenseOutThreads = 512;       // workgroup size of the latent output kernel at threshold 0
 
 // Floats of the first LDS region of the grouped kernel: scores [G][P], the
 // cross-wave reduction [kWaves][G][128], and the merge's slice partials

@@ -928,23 +928,22 @@ __global__ __launch_bounds__(256) void mla_out(MlaArgs a) {
 // Threshold 0 keeps every row, and the blocks of mla_out would each convert
 // the same value rows and split the same weights. Here one workgroup takes a
 // range of rows of a sequence for 64 of its heads and all 512 value dims:
-// wave w owns heads 32(w/2)..+31 of the 64 and value dims 256(w%2)..+255 (8
-// MFMA column tiles of 32 dims, two value groups; one wave per SIMD, whose
-// registers hold its 128 fp32 accumulators and the next chunk's loads). A
-// 64-row chunk is staged once: values converted to bf16 (exact) and
-// transposed [dim][slot], weights transposed [head][slot] in fp32, group
-// scales [slot][group]. Loads are coalesced (32 lanes read one 512-byte value
-// row, 16 lanes one row's 64 weights). The chunk's rows take the MFMA k
-// order slot 8b + m <- row b + 8m: a thread loads rows b, b+8, .., b+56 of
-// 16 dims, so each of its LDS writes is one 16-byte unit (8 slots of one
-// dim). Unit (dim d, block b) sits at 8 * (d ^ ((d >> 4) & 1)) +
-// ((b + (d >> 1) + (d >> 5)) & 7): the 16 lanes of a read (consecutive dims,
-// one block) and of a write (dims 16 apart, one block) fall in 16 different
-// bank groups. Each wave forms its A operand from its heads' weights times
-// its group's scale, split into two bf16 terms: the product rounded to
-// nearest, then its remainder (exact in fp32) rounded to nearest, so the pair
-// carries it within 2^-17 relative (mla_out keeps a third term; here the
-// conversions, not the products, bound the chunk time).
+// eight waves, two per SIMD (one's vector work and waits overlap the other's
+// MFMAs); wave w owns heads 32(w/4)..+31 of the 64 and value group w%4 (four
+// MFMA column tiles of 32 dims). A 64-row chunk is staged once: values
+// converted to bf16 (exact) and transposed [dim][slot], weights transposed
+// [head][slot] in fp32, group scales [group][slot]. Loads are coalesced (32
+// lanes read one 512-byte value row, 16 lanes one row's 64 weights). The
+// chunk's rows take the MFMA k order slot 8b + m <- row b + 8m: a thread
+// loads rows b + 8m, m = 4s..4s+3, of 16 dims, so each of its LDS writes is
+// 8 bytes (4 slots of one dim). Unit (dim d, block b) of 16 bytes sits at
+// 8 * (d ^ ((d >> 4) & 1)) + ((b + (d >> 1) + (d >> 5)) & 7): the 16 lanes of
+// an operand read (consecutive dims, one block) fall in 16 different bank
+// groups, and so do dims 16 apart (the writes). Each wave forms its A
+// operand from its heads' weights times its group's scale, split into two
+// bf16 terms: the product rounded to nearest, then its remainder (exact in
+// fp32) rounded to nearest, so the pair carries it within 2^-17 relative
+// (mla_out keeps a third term; here the conversions bound the chunk time).
 // The R ranges of a sequence write fp32 partial sums, mark themselves done
 // with a tagged word (after a device-scope fence), wait for the other ranges
 // and then each adds, in range order, one slice of the sequence's outputs
@@ -953,6 +952,7 @@ __global__ __launch_bounds__(256) void mla_out(MlaArgs a) {
 constexpr int DN_CHUNK = 64;                     // rows per stage
 constexpr int DN_SEG = 2048;                     // rows whose (slot, position) are looked up at once
 constexpr int DN_PP = DN_CHUNK + 4;              // floats per staged head line (16-byte rows)
+constexpr int DN_NT = kDenseOutThreads;          // threads per workgroup
 
 size_t mla_out_dense_lds(int) {
   return size_t(DV) * DN_CHUNK * 2 + size_t(64) * DN_PP * 4 + size_t(DN_CHUNK) * 4 * 4 + size_t(OUT_MAX_S + 4) * 4 +
@@ -966,22 +966,22 @@ __device__ inline int dn_unit(int d, int b) {    // 16-byte unit of (value dim d
 }
 __device__ inline int dn_slot(int r) { return 8 * (r & 7) + (r >> 3); }   // chunk row -> MFMA k slot
 
-__global__ __launch_bounds__(256) void mla_out_dense(MlaArgs a) {
-  constexpr int HW = DN_HW, NT = 256;
+__global__ __launch_bounds__(DN_NT) void mla_out_dense(MlaArgs a) {
+  constexpr int HW = DN_HW, NT = DN_NT;
   constexpr int NPV = DN_CHUNK * 32 / NT;          // 16-byte value pieces per thread and chunk
   constexpr int NPW = DN_CHUNK * (HW / 4) / NT;    // 4-head weight pieces per thread and chunk
-  static_assert(NPV == 8 && NPW * NT == DN_CHUNK * (HW / 4), "staging roles");
+  static_assert(NPV == 4 && NPW * NT == DN_CHUNK * (HW / 4), "staging roles");
   extern __shared__ __align__(16) unsigned char dsm[];
   uint4* vt = reinterpret_cast<uint4*>(dsm);                                         // [512 x 8] units of 8 bf16
   float* pf = reinterpret_cast<float*>(dsm + size_t(DV) * DN_CHUNK * 2);            // [HW][DN_PP] weights
-  float* gsc = pf + HW * DN_PP;                                                      // [DN_CHUNK][4] group scales
+  float* gsc = pf + HW * DN_PP;                                                      // [4][DN_CHUNK] group scales
   int* pre = reinterpret_cast<int*>(gsc + DN_CHUNK * 4);                             // [OUT_MAX_S + 4]
   int2* rowtab = reinterpret_cast<int2*>(pre + OUT_MAX_S + 4);                       // [DN_SEG] (slot, position)
 
   const int R = a.R, H = a.Hq, NHH = H / HW;      // head halves (or the one 64-head set) per sequence
   const int rg = blockIdx.x % R, bh = blockIdx.x / R, hh = bh % NHH, b = bh / NHH;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hb = wave >> 1, half = wave & 1;
+  const int hb = wave >> 2, g = wave & 3;
   const int S = a.S;
   const int64_t row0 = int64_t(b) * a.cap;
   const uint32_t epoch = __hip_atomic_load(&a.hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
@@ -1018,19 +1018,19 @@ __global__ __launch_bounds__(256) void mla_out_dense(MlaArgs a) {
   const int N = pre[OUT_MAX_S] + pre[OUT_MAX_S + 1] + pre[OUT_MAX_S + 2] + pre[OUT_MAX_S + 3];
   const int rbeg = int(int64_t(N) * rg / R), rend = int(int64_t(N) * (rg + 1) / R);
 
-  floatx16 acc[8] = {};
-  float msum = 0.f;                                   // weights of head 32hb + (lane & 31), this lane's rows (half 0)
+  floatx16 acc[4] = {};
+  float msum = 0.f;                                   // weights of head 32hb + (lane & 31), this lane's slots
   const int col = lane & 31, kh = lane >> 5;
-  // staged data of one chunk, loaded a chunk ahead: value pieces (row
-  // tid/32 + 8i, bytes 16 * (tid % 32)..), 4-head weight pieces (row
-  // (tid + 256i) / 16, heads 4 * (tid % 16)..) and, for the first 64 threads,
-  // the four value-group scales of row tid
+  // staged data of one chunk, loaded a chunk ahead: value pieces (rows
+  // vb + 8(4vs + i), bytes 16vq..), 4-head weight pieces (row (tid + 512i) / 16,
+  // heads 4 * (tid % 16)..) and, for the first 64 threads, the four value-group
+  // scales of row tid
   struct Stage { uint4 v[NPV]; float4 w[NPW]; float4 sc; };
-  const int vb = tid >> 5, vq = tid & 31;          // value block (row within 8) and 16-dim piece
+  const int vq = tid & 31, vb = (tid >> 5) & 7, vs = tid >> 8;
   auto load_stage = [&](int c0, int seg0, int segn, Stage& st) {
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
-      const int rs = c0 + vb + 8 * i - seg0;         // row within the segment
+      const int rs = c0 + vb + 8 * (4 * vs + i) - seg0;      // row within the segment
       st.v[i] = make_uint4(0u, 0u, 0u, 0u);
       if (rs < segn) st.v[i] = *reinterpret_cast<const uint4*>(a.kc + (row0 + rowtab[rs].y) * D + 16 * vq);
     }
@@ -1047,28 +1047,24 @@ __global__ __launch_bounds__(256) void mla_out_dense(MlaArgs a) {
       st.sc = *reinterpret_cast<const float4*>(a.ks + (row0 + rowtab[rs].y) * (4 * NGROUPS));
   };
   auto write_stage = [&](const Stage& st) {
-    // rows vb + 8i of dims 16vq + 2j, +1: pack the two dims' bf16 over the 8 rows
+    // slots 8vb + 4vs .. + 3 of dims 16vq + 2j, + 1: pack the two dims' bf16 over the 4 rows
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      uint32_t pr[8];
+      uint32_t pr[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < 4; ++i) {
         const uint32_t w = j < 2 ? st.v[i].x : j < 4 ? st.v[i].y : j < 6 ? st.v[i].z : st.v[i].w;
         pr[i] = __builtin_bit_cast(uint32_t, (j & 1) ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
                                                      : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
       }
-      uint4 lo, hi;                                   // dim 16vq + 2j (low halves), + 1 (high halves)
+      uint2 lo, hi;                                   // dim 16vq + 2j (low halves), + 1 (high halves)
       lo.x = __builtin_amdgcn_perm(pr[1], pr[0], 0x05040100u);
       lo.y = __builtin_amdgcn_perm(pr[3], pr[2], 0x05040100u);
-      lo.z = __builtin_amdgcn_perm(pr[5], pr[4], 0x05040100u);
-      lo.w = __builtin_amdgcn_perm(pr[7], pr[6], 0x05040100u);
       hi.x = __builtin_amdgcn_perm(pr[1], pr[0], 0x07060302u);
       hi.y = __builtin_amdgcn_perm(pr[3], pr[2], 0x07060302u);
-      hi.z = __builtin_amdgcn_perm(pr[5], pr[4], 0x07060302u);
-      hi.w = __builtin_amdgcn_perm(pr[7], pr[6], 0x07060302u);
       const int d = 16 * vq + 2 * j;
-      vt[dn_unit(d, vb)] = lo;
-      vt[dn_unit(d + 1, vb)] = hi;
+      reinterpret_cast<uint2*>(vt + dn_unit(d, vb))[vs] = lo;
+      reinterpret_cast<uint2*>(vt + dn_unit(d + 1, vb))[vs] = hi;
     }
 #pragma unroll
     for (int i = 0; i < NPW; ++i) {
@@ -1078,7 +1074,13 @@ __global__ __launch_bounds__(256) void mla_out_dense(MlaArgs a) {
       pf[(4 * h4 + 2) * DN_PP + sl] = st.w[i].z;
       pf[(4 * h4 + 3) * DN_PP + sl] = st.w[i].w;
     }
-    if (tid < DN_CHUNK) *reinterpret_cast<float4*>(gsc + dn_slot(tid) * 4) = st.sc;
+    if (tid < DN_CHUNK) {
+      const int sl = dn_slot(tid);
+      gsc[0 * DN_CHUNK + sl] = st.sc.x;
+      gsc[1 * DN_CHUNK + sl] = st.sc.y;
+      gsc[2 * DN_CHUNK + sl] = st.sc.z;
+      gsc[3 * DN_CHUNK + sl] = st.sc.w;
+    }
   };
 
   for (int seg0 = rbeg; seg0 < rend; seg0 += DN_SEG) {
@@ -1111,49 +1113,57 @@ __global__ __launch_bounds__(256) void mla_out_dense(MlaArgs a) {
       if (c0 + DN_CHUNK < seg0 + segn) load_stage(c0 + DN_CHUNK, seg0, segn, st);
       __syncthreads();
       // products: 4 k-steps of 16 slots; lane (col, kh) takes head 32hb + col
-      // and slots 16ks + 8kh .. + 7 of the chunk (not unrolled: the 128
-      // accumulators leave little room for operands of several steps)
-#pragma unroll 1
-      for (int ks = 0; ks < DN_CHUNK / 16; ++ks) {
+      // and slots 16ks + 8kh .. + 7 of the chunk; the LDS operands of step
+      // ks + 1 are read while the MFMAs of step ks run
+      float pw[2][8], gs[2][8];
+      bf16x8 bv[2][4], ah[2], al[2];
+      auto read_ops = [&](int ks, float (&w)[8], float (&s8)[8], bf16x8 (&bq)[4]) {
         const int k0 = 16 * ks + 8 * kh;
         const float* ph = pf + (32 * hb + col) * DN_PP + k0;
         const float4 pa = *reinterpret_cast<const float4*>(ph), pb = *reinterpret_cast<const float4*>(ph + 4);
-        const float pw[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
-        if (half == 0)
+        const float4 sa = *reinterpret_cast<const float4*>(gsc + g * DN_CHUNK + k0);
+        const float4 sb = *reinterpret_cast<const float4*>(gsc + g * DN_CHUNK + k0 + 4);
+        w[0] = pa.x; w[1] = pa.y; w[2] = pa.z; w[3] = pa.w; w[4] = pb.x; w[5] = pb.y; w[6] = pb.z; w[7] = pb.w;
+        s8[0] = sa.x; s8[1] = sa.y; s8[2] = sa.z; s8[3] = sa.w; s8[4] = sb.x; s8[5] = sb.y; s8[6] = sb.z; s8[7] = sb.w;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) msum += pw[i];
+        for (int t = 0; t < 4; ++t)
+          bq[t] = __builtin_bit_cast(bf16x8, vt[dn_unit(128 * g + 32 * t + col, 2 * ks + kh)]);
+      };
+      auto make_a = [&](const float (&w)[8], const float (&s8)[8], bf16x8& hv, bf16x8& lv) {
 #pragma unroll
-        for (int gg = 0; gg < 2; ++gg) {             // the wave's two value groups
-          const int g = 2 * half + gg;
-          bf16x8 ah, al;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float x = pw[i] * gsc[(k0 + i) * 4 + g];
-            const __bf16 h = __bf16(x);                // v_cvt_pk_bf16_f32: round to nearest even
-            ah[i] = h;
-            al[i] = __bf16(x - float(h));
-          }
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const bf16x8 bv = __builtin_bit_cast(bf16x8, vt[dn_unit(128 * g + 32 * t + col, 2 * ks + kh)]);
-            acc[4 * gg + t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bv, acc[4 * gg + t], 0, 0, 0);
-            acc[4 * gg + t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bv, acc[4 * gg + t], 0, 0, 0);
-          }
+        for (int i = 0; i < 8; ++i) {
+          msum += w[i];
+          const float x = w[i] * s8[i];
+          const __bf16 h = __bf16(x);                  // v_cvt_pk_bf16_f32: round to nearest even
+          hv[i] = h;
+          lv[i] = __bf16(x - float(h));
         }
+      };
+      read_ops(0, pw[0], gs[0], bv[0]);
+      make_a(pw[0], gs[0], ah[0], al[0]);
+#pragma unroll
+      for (int ks = 0; ks < DN_CHUNK / 16; ++ks) {
+        const int c = ks & 1, n = c ^ 1;
+        if (ks + 1 < DN_CHUNK / 16) read_ops(ks + 1, pw[n], gs[n], bv[n]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[c], bv[c][t], acc[t], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[c], bv[c][t], acc[t], 0, 0, 0);
+        if (ks + 1 < DN_CHUNK / 16) make_a(pw[n], gs[n], ah[n], al[n]);
       }
       __syncthreads();                                 // the next chunk reuses the staging
     }
   }
-  // partial of this range: accumulator 4i+j of tile t -> head HW*hh + 32hb + 8i + 4kh + j, dim 256half + 32t + col
+  // partial of this range: accumulator 4i+j of tile t -> head HW*hh + 32hb + 8i + 4kh + j, dim 128g + 32t + col
   float* part = a.opart + (int64_t(b) * R + rg) * H * DV + int64_t(HW * hh) * DV;
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
+  for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        part[(32 * hb + 8 * i + 4 * kh + j) * DV + 256 * half + 32 * t + col] = acc[t][4 * i + j];
-  if (half == 0) {                                     // head 32hb + col: the two lane halves' rows
+        part[(32 * hb + 8 * i + 4 * kh + j) * DV + 128 * g + 32 * t + col] = acc[t][4 * i + j];
+  if (g == 0) {                                        // head 32hb + col: the two lane halves' slots
     const float other = __shfl_xor(msum, 32);
     if (kh == 0) a.mpart[(int64_t(b) * R + rg) * H + HW * hh + 32 * hb + col] = msum + other;
   }
