@@ -159,9 +159,11 @@ def test_lut3_ragged(ctx, threshold, name):
 
 
 @pytest.mark.parametrize("name", ["lut3", "lut3_wht"])
-def test_lut3_full_size(name):
-    say("case", name, "batch 8, 32/4 heads, ctx 32768, 8..64 hot per sequence")
-    inp, tau = _case(name)
+@pytest.mark.parametrize("threshold", [None, 0.0])
+def test_lut3_full_size(name, threshold):
+    say("case", name, "batch 8, 32/4 heads, ctx 32768, 8..64 hot per sequence, threshold",
+        "of the workload" if threshold is None else threshold)
+    inp, tau = _case(name, threshold)
     g = run_gpu(inp, tau)
     r, po = oracle_for(inp, tau)
     compare(inp, tau, g, r, po)

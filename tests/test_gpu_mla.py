@@ -76,11 +76,14 @@ def test_mla_every_fp8_code():
     compare(inp, tau, g, r, po, mask=False)
 
 
-def test_mla_full_size_sampled():
-    """Full workload (batch 8, 128 heads, ctx 65536) on the GPU; the oracle
-    recomputes sequences 0 and 7 one by one."""
-    say("case mla full size: batch 8, 128 heads, ctx 65536 (oracle on sequences 0 and 7)")
-    inp, tau = _case()
+@pytest.mark.parametrize("threshold", [None, 0.0])
+def test_mla_full_size_sampled(threshold):
+    """Full workload (batch 8, 128 heads, ctx 65536) on the GPU, with the
+    workload's threshold and with every row kept (the dense output kernel,
+    as timed); the oracle recomputes sequences 0 and 7 one by one."""
+    say("case mla full size: batch 8, 128 heads, ctx 65536 (oracle on sequences 0 and 7), threshold",
+        "1e-6" if threshold is None else threshold)
+    inp, tau = _case(threshold)
     g = run_gpu(inp, tau, q_bf16=True)
     for b in (0, 7):
         sub = synth.Inputs(synth.resized(inp.w, batch=1), inp.q[b:b + 1], inp.k[b:b + 1], None,
@@ -94,5 +97,9 @@ def test_mla_full_size_sampled():
         assert np.allclose(g["stats"]["kept_mass"][b], r.kept_mass[0], atol=1e-5)
     st = g["stats"]
     assert st["status"] == 0
-    # every sequence keeps exactly its 96 planted rows (the boost puts them far above the rest)
-    assert st["rows_fetched"] == 8 * 96, st
+    if tau > 0:
+        # every sequence keeps exactly its 96 planted rows (the boost puts them far above the rest)
+        assert st["rows_fetched"] == 8 * 96, st
+    else:
+        assert st["rows_fetched"] == 8 * 65536, st
+        assert np.allclose(g["stats"]["kept_mass"], 1.0, atol=1e-5)
