@@ -104,9 +104,10 @@ int32_t make_mla_plan(const kvq_cache* k, const kvq_launch* l, int32_t ctx_len, 
   plan->threads = 4 * H;                                 // two waves per 32-head block
   // row ranges of the every-row-kept output: one workgroup per CU over the
   // batch and its 64-head sets, at least 64 rows each
-  plan->R = int(std::max<int64_t>(
-      1, std::min<int64_t>({64, di.cus / (int64_t(k->batch) * std::max(1, H / 64)), (ctx_len + 63) / 64})));
-  plan->mws = kvq::mla_ws_layout(k->batch, H, S, P, plan->R);
+  plan->R = int(std::max<int64_t>(1, std::min<int64_t>({kvq::kMaxRanges,
+                                                          di.cus / (int64_t(k->batch) * std::max(1, H / 64)),
+                                                          (ctx_len + 63) / 64})));
+  plan->mws = kvq::mla_ws_layout(k->batch, H, S, int64_t(S) * P, plan->R);
   plan->total = plan->mws.total;
   return KVQ_OK;
 }
@@ -272,7 +273,31 @@ extern "C" int32_t kvq_workspace_bytes(int32_t fmt, const kvq_cache* kcache, con
   Plan plan;
   const int32_t rc = make_plan(fmt, kcache, l, ctx_len, &plan);
   if (rc) return rc;
-  *bytes = plan.total;
+  // Size for every context length up to ctx_len: rounding P up to whole
+  // 64-position chunks makes the split count of a plan fall and rise again
+  // as the context grows (4096 positions over 64 splits of 64, 4097 over 33
+  // of 128), so a decode loop's later, shorter or longer, calls may need more
+  // than the plan of ctx_len. Every plan for ctx' <= ctx_len has
+  //   S' <= s0 = the requested splits, else min(CUs / sequences, ceil(ctx_len / 64)),
+  //   S' * P' < ctx' + P' <= ctx_len + ceil(ctx_len / s_cap) + 126,
+  //   R' <= R of ctx_len,
+  // and every region of a layout grows with these.
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return KVQ_ERR_LAUNCH;
+  const int64_t cus = device_info(dev).cus;
+  const int64_t chunks = (int64_t(ctx_len) + 63) / 64;
+  if (plan.mla) {
+    const int64_t cap = l->splits > 0 ? l->splits : std::max<int64_t>(1, cus / kcache->batch);
+    const int64_t s_up = std::min(cap, chunks);
+    const int64_t sp_up = int64_t(ctx_len) + (int64_t(ctx_len) + cap - 1) / cap + 126;
+    const kvq::MlaLayout w = kvq::mla_ws_layout(kcache->batch, plan.G, int(s_up), sp_up, plan.R);
+    *bytes = std::max(plan.total, w.total);
+  } else {
+    const int64_t bg = int64_t(kcache->batch) * kcache->heads;
+    const int64_t s_up = l->splits > 0 ? l->splits : std::min(std::max<int64_t>(1, cus / bg), chunks);
+    const kvq::WsLayout w = kvq::ws_layout(kcache->batch, kcache->heads, l->q_heads, int(s_up), plan.Dv);
+    *bytes = std::max(plan.total, w.total);
+  }
   return KVQ_OK;
 }
 

@@ -120,21 +120,27 @@ struct MlaLayout {
   int64_t kept_mass, bgstat, split_ml, kcount, kpairs, kpos, kp, opart, mpart, ocnt, done, total;
 };
 
-// The first two regions match ws_layout() so kvq_stats reads both families alike.
-inline MlaLayout mla_ws_layout(int B, int H, int S, int P, int R) {
+// The first two regions match ws_layout() so kvq_stats reads both families
+// alike. The range counters (which must hold 0 between calls) and the done
+// words come next, sized for the most ranges a plan uses, so their offsets
+// depend on the batch and head count only: calls with different context
+// lengths on one workspace find them where the previous call left them.
+// SP: positions published per sequence over all splits (S * P).
+constexpr int kMaxRanges = 64;
+inline MlaLayout mla_ws_layout(int B, int H, int S, int64_t SP, int R) {
   MlaLayout w;
   int64_t off = 256;
   w.kept_mass = off; off = align256(off + int64_t(B) * H * 4);
   w.bgstat = off;    off = align256(off + int64_t(B) * 16);
+  w.ocnt = off;      off = align256(off + int64_t(B) * (H / 32) * 4 * 4);
+  w.done = off;      off = align256(off + int64_t(B) * (H >= 64 ? H / 64 : 1) * kMaxRanges * 8);
   w.split_ml = off;  off = align256(off + int64_t(B) * S * H * 16);
   w.kcount = off;    off = align256(off + int64_t(B) * S * 4);
   w.kpairs = off;    off = align256(off + int64_t(B) * S * 4);
-  w.kpos = off;      off = align256(off + int64_t(B) * S * P * 4);
-  w.kp = off;        off = align256(off + int64_t(B) * S * P * int64_t(H) * 4);
+  w.kpos = off;      off = align256(off + int64_t(B) * SP * 4);
+  w.kp = off;        off = align256(off + int64_t(B) * SP * int64_t(H) * 4);
   w.opart = off;     off = align256(off + int64_t(B) * (H / 32) * 4 * R * 32 * 128 * 4);
   w.mpart = off;     off = align256(off + int64_t(B) * (H / 32) * R * 32 * 4);
-  w.ocnt = off;      off = align256(off + int64_t(B) * (H / 32) * 4 * 4);
-  w.done = off;      off = align256(off + int64_t(B) * (H >= 64 ? H / 64 : 1) * R * 8);
   w.total = off;
   return w;
 }

@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_helpers import compare, oracle_for, run_gpu, say
+from gpu_helpers import MAX_ABS, MAX_REL_L2, compare, oracle_for, run_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -167,3 +167,46 @@ def test_lut3_full_size(name, threshold):
     g = run_gpu(inp, tau)
     r, po = oracle_for(inp, tau)
     compare(inp, tau, g, r, po)
+
+
+@pytest.mark.parametrize("name,heads,threshold", [("long", None, 1e-6), ("long", None, 0.0), ("mla", 32, 0.0),
+                                                  ("mla", 128, 0.0), ("mla", 64, 1e-6)])
+def test_one_workspace_for_shorter_contexts(name, heads, threshold):
+    """A workspace sized for ctx_len serves every shorter call, although the
+    rounding of positions per split makes the plan of ctx 4096 (64 splits of
+    64 positions for the long shape) larger than the plan of 4097 (33 of
+    128); the calls alternate so each finds the previous one's words in
+    another layout (the latent range counters must not move)."""
+    import torch
+
+    import decode_attention_quantized_amd as kvq
+    from decode_attention_quantized_amd.runtime import DecodeAttention, PackedCache
+    kw = dict(ctx=4097)
+    if name == "mla":
+        kw.update(batch=2, q_heads=heads)
+    w = synth.resized(synth.workload(name), **kw)
+    inp = synth.generate(w)
+    say("case one workspace:", name, "heads", w.q_heads, "threshold", threshold, "contexts 4097 4096 3000 4097 64")
+    kc, ks = kvq.kvq_pack(w.fmt, inp.k)
+    K = PackedCache.from_host(kc, ks, w.fmt, w.dim)
+    V = None
+    if inp.v is not None:
+        vc, vs = kvq.kvq_pack(w.fmt, inp.v)
+        V = PackedCache.from_host(vc, vs, w.fmt, w.v_dim)
+    latent = V is None
+    att = DecodeAttention(K, V, w.q_heads, ctx_len=w.ctx, softmax_scale=w.sigma,
+                          q_dtype=kvq.KVQ_Q_BF16 if latent else kvq.KVQ_Q_F32, v_dim=w.v_dim if latent else 0)
+    q = torch.from_numpy(inp.q).cuda()
+    if latent:
+        q = q.to(torch.bfloat16)
+    splits = set()
+    for n in (4097, 4096, 3000, 4097, 64):
+        out = att(q, n, threshold).cpu().numpy()
+        st = att.stats()
+        assert st["status"] == 0, (n, st)
+        splits.add(st["splits"])
+        r, _ = oracle_for(inp, threshold, ctx_len=n)
+        err = float(np.abs(out - r.out64).max())
+        rel = float(np.linalg.norm(out - r.out64) / max(np.linalg.norm(r.out64), 1e-30))
+        assert err <= MAX_ABS and rel <= MAX_REL_L2, (n, err, rel)
+    assert len(splits) > 1, splits
