@@ -206,7 +206,10 @@ typedef struct kvq_launch {
 enum { KVQ_LAUNCH_COOPERATIVE = 1, KVQ_SKIP_RUNNING = 2 };
 
 /* Device workspace bytes kvq_decode_attn needs for these shapes on the
- * current device (bytes: host out-pointer). */
+ * current device (bytes: host out-pointer), for every context length from 1
+ * to ctx_len: one workspace serves a decode loop whose context grows or
+ * shrinks within that bound, with the same format, cache shape and launch
+ * settings (splits, heads, value width). */
 int32_t kvq_workspace_bytes(int32_t fmt, const kvq_cache* kcache, const kvq_launch* l,
                             int32_t ctx_len, int64_t* bytes);
 
