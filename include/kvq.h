@@ -23,6 +23,13 @@
  *  - The library allocates no device memory and keeps no global mutable state
  *    apart from a per-device cache of the compute-unit count. Calls that share
  *    a workspace must be serialized (same stream or explicit ordering).
+ *  - kvq_decode_attn's workgroups hand data to one another inside a launch,
+ *    so all of them must be resident at once: the plan launches at most one
+ *    per compute unit, which holds when nothing else occupies the GPU's
+ *    compute units (other kernels on concurrent streams included). When that
+ *    cannot be ensured, KVQ_LAUNCH_COOPERATIVE makes the runtime check it. A
+ *    wait that does not end within about half a second sets a status bit
+ *    (kvq_stats reports KVQ_ERR_DEVICE) instead of hanging.
  *  - Multi-byte values in packed planes are little-endian.
  */
 #ifndef KVQ_H
