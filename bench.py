@@ -139,6 +139,46 @@ def time_mode(att, q, caches, ctx, tau, steps, warmup, out, stream):
                 eager_p90=per[(9 * len(per)) // 10], stats=st)
 
 
+def stream_reference(nbytes, grid, steps, warmup, stream):
+    """The plain streaming-read kernel over the same number of bytes and the
+    same grid as a decode call, from buffers rotated like the caches (every
+    launch reads cold HBM), timed like the decode call (HIP events around one
+    graph replay on the launch stream)."""
+    import torch
+
+    import decode_attention_quantized_amd as kvq
+    nbytes = nbytes // 16 * 16
+    R = max(2, math.ceil(ROTATION_BYTES / nbytes))
+    bufs = torch.zeros((R, nbytes), dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(grid, dtype=torch.int32, device="cuda")
+
+    def call(i):
+        kvq.kvq_stream_read(bufs[i % R], grid, sink, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            call(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(steps):
+            call(warmup + i)
+    with torch.cuda.stream(stream):
+        g.replay()                                              # untimed
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record()
+        g.replay()
+        e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    del g, bufs
+    return {"kernel": "kvq_stream_read (plain 16-byte loads, 1024 threads per workgroup)", "bytes": nbytes,
+            "grid": grid, "us_per_launch": round(us, 3), "gbs": round(nbytes / us / 1e3, 1),
+            "frac_hbm": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4), "rotation_sets": R}
+
+
 def cpu_baseline(inp, budget_s=12.0):
     """The fp64 oracle, as it stands, on a bounded sample: whole decode calls of
     the same workload (excluding packing), repeated until ~budget_s."""
@@ -459,6 +499,11 @@ def main():
             "extra_rows_vs_exact": sp["stats"]["rows_fetched"] - r["stats"]["rows_fetched"],
             "kept_pairs": sp["stats"]["kept_pairs"],
         }
+    # the same bytes read by a plain streaming kernel on the decode call's grid:
+    # what a read of this size and launch shape reaches on this GPU
+    sref = stream_reference(ab, int(r["stats"]["splits"]) * w.batch * w.kv_heads, args.steps, args.warmup, stream)
+    sref["decode_kernel_over_stream_read"] = round(r["kernel_mean"] * 1e6 / sref["us_per_launch"], 3)
+    line["stream_read_same_bytes"] = sref
     if not args.no_cpu_baseline:
         cb_, ref, (okc, oks) = cpu_baseline(inp)
         line["cpu_baseline"] = cb_

@@ -6,12 +6,12 @@ allocates device buffers with torch.
 """
 from .binding import (EXPORTS, FMT, KVQ_FP8_B128, KVQ_LUT3, KVQ_Q4_0, KVQ_Q8_0, KVQ_Q_BF16, KVQ_Q_F32, KVQ_SKIP_RUNNING,
                       KvqError, kvq_append, kvq_append_kv, kvq_decode_attn, kvq_lut3_levels, kvq_pack, kvq_phase_count, kvq_row_bytes, kvq_stats,
-                      kvq_strerror, kvq_unpack, kvq_workspace_bytes, lib, make_cache, make_launch)
+                      kvq_stream_read, kvq_strerror, kvq_unpack, kvq_workspace_bytes, lib, make_cache, make_launch)
 from .runtime import DecodeAttention, PackedCache
 
 __all__ = [
     "EXPORTS", "FMT", "KVQ_Q8_0", "KVQ_Q4_0", "KVQ_LUT3", "KVQ_FP8_B128", "KVQ_Q_F32", "KVQ_Q_BF16", "KVQ_SKIP_RUNNING",
     "KvqError", "kvq_append", "kvq_append_kv", "kvq_decode_attn", "kvq_lut3_levels", "kvq_pack", "kvq_phase_count", "kvq_row_bytes", "kvq_stats",
-    "kvq_strerror", "kvq_unpack", "kvq_workspace_bytes", "lib", "make_cache", "make_launch",
+    "kvq_stream_read", "kvq_strerror", "kvq_unpack", "kvq_workspace_bytes", "lib", "make_cache", "make_launch",
     "DecodeAttention", "PackedCache",
 ]

@@ -52,7 +52,7 @@ class kvq_stats_t(ctypes.Structure):
 
 EXPORTS = ["kvq_row_bytes", "kvq_pack", "kvq_unpack", "kvq_lut3_levels", "kvq_append", "kvq_append_kv",
            "kvq_workspace_bytes",
-           "kvq_decode_attn", "kvq_stats", "kvq_phase_count", "kvq_strerror"]
+           "kvq_decode_attn", "kvq_stats", "kvq_phase_count", "kvq_strerror", "kvq_stream_read"]
 
 _lib = None
 
@@ -79,6 +79,7 @@ def lib() -> ctypes.CDLL:
         L.kvq_stats.argtypes = [ctypes.POINTER(kvq_launch), ctypes.POINTER(kvq_stats_t), vp]
         L.kvq_phase_count.argtypes = [ctypes.POINTER(kvq_launch), ctypes.POINTER(i32), ctypes.POINTER(i32)]
         L.kvq_strerror.argtypes = [i32]
+        L.kvq_stream_read.argtypes = [vp, i64, i32, vp, vp]
         L.kvq_strerror.restype = ctypes.c_char_p
         for name in EXPORTS:
             if name != "kvq_strerror":
@@ -220,6 +221,19 @@ def kvq_stats(launch: kvq_launch, kept_mass: bool = True):
         d["kept_mass"] = km[: s.batch * s.q_heads].reshape(s.batch, s.q_heads)
     d["rc"] = rc if rc else rc0
     return d
+
+
+def kvq_stream_read(src, grid: int, sink, stream=None, nbytes: int | None = None):
+    """Streaming-read reference: read ``nbytes`` (default: all) bytes of the
+    device tensor ``src`` with ``grid`` 1024-thread workgroups on ``stream``
+    (a torch.cuda.Stream, or None for the default stream); each workgroup
+    XORs the 32-bit words it read into ``sink[g]`` (device int32 tensor of at
+    least ``grid`` elements)."""
+    n = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    if sink.numel() < grid:
+        raise KvqError(-1, "kvq_stream_read: sink holds fewer words than the grid")
+    st = stream.cuda_stream if stream is not None else None
+    _check(lib().kvq_stream_read(src.data_ptr(), n, int(grid), sink.data_ptr(), st), "kvq_stream_read")
 
 
 def kvq_phase_count(launch: kvq_launch):

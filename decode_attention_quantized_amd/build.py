@@ -35,6 +35,8 @@ SOURCES = [
     ("kvq_mla.hip", HIP_FLAGS + ["-ffp-contract=fast", "-fno-honor-nans"]),
     # the device packer rounds exactly as the host packer: no contraction
     ("kvq_append.hip", HIP_FLAGS + ["-ffp-contract=off", "-fno-fast-math"]),
+    # streaming-read reference used by the measurements
+    ("kvq_probe.hip", HIP_FLAGS),
 ]
 
 

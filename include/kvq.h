@@ -268,6 +268,18 @@ int32_t kvq_stats(const kvq_launch* l, kvq_stats_t* out, float* kept_mass);
  * (host out-pointers; synchronizes l->stream). */
 int32_t kvq_phase_count(const kvq_launch* l, int32_t* workgroups, int32_t* stamps);
 
+/* Measurement reference, not part of the attention path: read `bytes`
+ * bytes (a multiple of 16) of device memory at `src` (16-byte aligned) with
+ * `grid` workgroups of 1024 threads, workgroup g taking the g-th of `grid`
+ * contiguous slices with 16-byte loads, and XOR every 32-bit word a
+ * workgroup read into sink[g] (device uint32[grid], caller-owned; zero it
+ * first to read the XOR back). Timing it over the bytes and grid of a decode
+ * call gives the bandwidth a plain streaming read reaches at that size and
+ * launch shape. Asynchronous on `stream` (a hipStream_t, NULL: default).
+ * Errors: ARG (null pointer, bytes <= 0 or not a multiple of 16, grid
+ * outside 1..2^20), ALIGN, LAUNCH. */
+int32_t kvq_stream_read(const void* src, int64_t bytes, int32_t grid, uint32_t* sink, void* stream);
+
 /* Static text for an error code. */
 const char* kvq_strerror(int32_t code);
 

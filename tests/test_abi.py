@@ -103,3 +103,15 @@ def test_append_kv_argument_validation_without_gpu():
     assert L.kvq_append_kv(B.KVQ_Q4_0, k, v, 4, 128, dst, kc, ks, vc, vs + 4, 16, None, None) == -2
     assert L.kvq_append_kv(B.KVQ_Q4_0, k, v + 2, 4, 128, dst, kc, ks, vc, vs, 16, None, None) == -2
     assert L.kvq_append_kv(B.KVQ_Q4_0, k, v, 0, 128, dst, kc, ks, vc, vs, 16, None, None) == 0
+
+
+def test_stream_read_argument_validation_without_gpu():
+    L = B.lib()
+    src, sink = 0x10000, 0x20000                           # fake aligned addresses: never dereferenced
+    assert L.kvq_stream_read(None, 1024, 4, sink, None) == -1
+    assert L.kvq_stream_read(src, 1024, 4, None, None) == -1
+    assert L.kvq_stream_read(src, 0, 4, sink, None) == -1
+    assert L.kvq_stream_read(src, 1000, 4, sink, None) == -1     # not a multiple of 16
+    assert L.kvq_stream_read(src, 1024, 0, sink, None) == -1
+    assert L.kvq_stream_read(src, 1024, (1 << 20) + 1, sink, None) == -1
+    assert L.kvq_stream_read(0x10008, 1024, 4, sink, None) == -2  # ALIGN
