@@ -44,6 +44,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef unsigned long long u64;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kCoherentLoad = 16;                // buffer cache policy: sc1 (device-coherent read)
 
 constexpr int D = 576;          // latent width (scores)
 constexpr int DV = 512;         // value width
@@ -484,38 +486,59 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
 
   // ---------------------------------------------------------------- phase 2: LSE
   // Every workgroup merges the split statistics of all heads of its sequence
-  // itself (one exchange, no second round trip): four threads per head, thread
-  // q merging splits q, q + 4, ... in order, then the four results in a fixed
+  // itself (one exchange, no second round trip): thread (q, h) merges head
+  // h's splits q, q + 4, ... in order, reading each (max, sum) pair of tagged
+  // words with one coherent 16-byte load (consecutive threads on consecutive
+  // heads, so a wave reads whole lines) and re-reading the stale ones of a
+  // batch together; the four partial results of a head are merged in a fixed
   // order, so every workgroup of the sequence computes the same bits.
   {
-    const int h = tid >> 2, q = tid & 3;              // NT = 4 * H
+    const int h = tid % H, q = tid / H;               // NT = 4 * H
     float2 acc = make_float2(-INFINITY, 0.f);
     constexpr int SB = 8;                             // splits per batch of loads
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(a.split_ml + int64_t(b) * a.S * H * 2, 0, a.S * H * 16, 0x00020000);
     for (int s0 = q; s0 < a.S; s0 += 4 * SB) {
-      u64 w[2 * SB];
-      const u64* src[2 * SB];
+      u32x4 v[SB];
+      int off[SB];
+      bool use[SB];
 #pragma unroll
       for (int u = 0; u < SB; ++u) {
         const int sp = s0 + 4 * u;
-        src[2 * u] = a.split_ml + ((int64_t(b) * a.S + (sp < a.S ? sp : 0)) * H + h) * 2;
-        src[2 * u + 1] = src[2 * u] + 1;
-        w[2 * u] = sp < a.S ? peek(src[2 * u]) : 0ull;
-        w[2 * u + 1] = sp < a.S ? peek(src[2 * u + 1]) : 0ull;
+        use[u] = sp < a.S;
+        off[u] = ((use[u] ? sp : 0) * H + h) * 16;
+        v[u] = use[u] ? __builtin_amdgcn_raw_buffer_load_b128(r, off[u], 0, kCoherentLoad) : u32x4{0u, epoch, 0u, epoch};
+      }
+      for (uint32_t spins = 0;; ++spins) {
+        bool stale = false;
+#pragma unroll
+        for (int u = 0; u < SB; ++u) stale |= use[u] && (v[u][1] != epoch || v[u][3] != epoch);
+        if (!stale) break;
+        if (spins > kSpinLimit) {
+          __hip_atomic_fetch_or(&a.hdr->status, kStatusWaitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int u = 0; u < SB; ++u)
+          if (use[u] && (v[u][1] != epoch || v[u][3] != epoch))
+            v[u] = __builtin_amdgcn_raw_buffer_load_b128(r, off[u], 0, kCoherentLoad);
       }
 #pragma unroll
       for (int u = 0; u < SB; ++u) {
-        if (s0 + 4 * u >= a.S) break;
-        const float m = settle_f(w[2 * u], src[2 * u], epoch, a.hdr);
-        const float l = settle_f(w[2 * u + 1], src[2 * u + 1], epoch, a.hdr);
-        acc = lse_merge(acc, make_float2(m, l));
+        if (!use[u]) break;
+        acc = lse_merge(acc, make_float2(__uint_as_float(v[u][0]), __uint_as_float(v[u][2])));
       }
     }
-    // (q0 + q1) + (q2 + q3): lanes 4h.. of one wave
-    const float2 x1 = make_float2(__shfl_xor(acc.x, 1), __shfl_xor(acc.y, 1));
-    const float2 p = (q & 1) ? lse_merge(x1, acc) : lse_merge(acc, x1);
-    const float2 x2 = make_float2(__shfl_xor(p.x, 2), __shfl_xor(p.y, 2));
-    const float2 r = (q & 2) ? lse_merge(x2, p) : lse_merge(p, x2);
-    if (q == 0) lse[h] = r.x + log2f(r.y);
+    float2* part = reinterpret_cast<float2*>(xbuf);   // [4][H]; the hand-over slots are idle here
+    part[q * H + h] = acc;
+    __syncthreads();
+    if (q == 0) {
+      const float2 r01 = lse_merge(part[h], part[H + h]);
+      const float2 r23 = lse_merge(part[2 * H + h], part[3 * H + h]);
+      const float2 rr = lse_merge(r01, r23);
+      lse[h] = rr.x + log2f(rr.y);
+    }
     __syncthreads();
   }
   stamp_mla(a, 3);
@@ -525,23 +548,31 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
   // threshold (a small margin keeps the test conservative); only live tiles
   // are re-read and re-scored, with the same code and so the same bits.
   const float log2tau = a.tau > 0.f ? log2f(a.tau) : -INFINITY;
-  if (tid == 0) misc[0] = 0;
-  __syncthreads();
-  for (int u = tid; u < NLT; u += NT) {
-    bool lv = false;
-    if (pos0 + u * LTILE < ctx)
-      for (int h = 0; h < H && !lv; ++h) lv = tmax[h * NLT + u] >= lse[h] + log2tau - 0.01f;
-    if (lv) live[atomicAdd(&misc[0], 1)] = u;
-  }
+  // every (tile, head) pair is tested by its own thread and marks its tile
+  // (all marks store the same 1); wave 0 then compacts the marked tile ids in
+  // position order, 64 at a time, in place (a chunk's marks are read before
+  // any id lands at or below them)
+  for (int u = tid; u < NLT; u += NT) live[u] = 0;
   if (tid < 2 * TILE) keepmask[tid] = 0u;
   if (tid == 0) misc[2] = 0;                           // kept pairs
   __syncthreads();
-  const int nlive = misc[0];
-  // sort the (few) live tile ids so the published rows come out in position order
-  if (tid == 0)
-    for (int i = 1; i < nlive; ++i)
-      for (int j = i; j > 0 && live[j - 1] > live[j]; --j) { const int x = live[j]; live[j] = live[j - 1]; live[j - 1] = x; }
+  for (int i = tid; i < NLT * H; i += NT) {
+    const int u = i % NLT, h = i / NLT;
+    if (pos0 + u * LTILE < ctx && tmax[h * NLT + u] >= lse[h] + log2tau - 0.01f) live[u] = 1;
+  }
   __syncthreads();
+  if (wave == 0) {
+    int nl = 0;
+    for (int u0 = 0; u0 < NLT; u0 += 64) {
+      const bool mk = u0 + lane < NLT && live[u0 + lane] != 0;
+      const unsigned long long bal = __ballot(mk);
+      if (mk) live[nl + __popcll(bal & ((1ull << lane) - 1ull))] = u0 + lane;
+      nl += __popcll(bal);
+    }
+    if (lane == 0) misc[0] = nl;
+  }
+  __syncthreads();
+  const int nlive = misc[0];
 
   // Register staging of 32-position tiles into ring buffers 0 and 1, two
   // register sets, so two tiles are in flight while one is scored.
