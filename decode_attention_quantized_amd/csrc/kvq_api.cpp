@@ -17,7 +17,7 @@
 namespace kvq {
 size_t gqa_lds_bytes(int fmt, int G, int P, int S);
 const void* gqa_kernel(int fmt, int G, bool run);
-size_t mla_lds_bytes(int H, int P, int S);
+size_t mla_lds_bytes(int H, int P, int S, int tpe);
 const void* mla_scores_kernel(int H);
 const void* mla_out_kernel();
 size_t mla_out_dense_lds(int H);
@@ -57,6 +57,7 @@ struct Plan {
   int nwg = 0;
   int threads = 0;
   int R = 1;                                              // latent output: row ranges per block
+  int tpe = 2;                                            // latent scores: 32-position tiles per tile maximum
   WsLayout ws{};
   kvq::MlaLayout mws{};
   int64_t total = 0;
@@ -92,8 +93,15 @@ int32_t make_mla_plan(const kvq_cache* k, const kvq_launch* l, int32_t ctx_len, 
   P = (P + 63) / 64 * 64;
   S = (ctx_len + P - 1) / P;
   if (S > 1024) return KVQ_ERR_UNSUPPORTED;
-  const size_t lds = kvq::mla_lds_bytes(H, P, S);
+  // one tile maximum per 32-position tile when the table fits, else one per 64
+  int tpe = 1;
+  size_t lds = kvq::mla_lds_bytes(H, P, S, 1);
+  if (lds > size_t(di.max_lds)) {
+    tpe = 2;
+    lds = kvq::mla_lds_bytes(H, P, S, 2);
+  }
   if (lds > size_t(di.max_lds)) return KVQ_ERR_UNSUPPORTED;
+  plan->tpe = tpe;
   plan->mla = true;
   plan->S = S;
   plan->P = P;
@@ -210,6 +218,7 @@ int32_t launch_mla(const void* q, const kvq_cache* kcache, const kvq_cache* vcac
   // else mla_out's per-block ranges); a positive threshold keeps few rows,
   // one range per mla_out block
   a.R = threshold == 0.0f ? plan.R : 1;
+  a.tpe = plan.tpe;
   a.B = kcache->batch;
   a.Hq = l->q_heads;
   a.ctx = ctx_len;

@@ -109,6 +109,7 @@ struct MlaArgs {
   uint32_t* ocnt;                 // [B][H/32][4] row ranges finished (0 between calls)
   unsigned long long* done;       // tagged [B][H/64][R]: every-row-kept ranges that wrote their partials
   int32_t R;                      // row ranges launched (per output block, or per sequence at threshold 0)
+  int32_t tpe;                    // 32-position tiles per tile-maximum entry of the scores kernel (1 or 2)
   int32_t B, Hq, ctx, cap;
   int32_t S, P;
   float sigma_log2e;

@@ -55,7 +55,6 @@ constexpr int NGROUPS = 5;      // scale groups: 4 x 128 + 1 x 64
 constexpr int ROW_LDS = 592;    // LDS pitch of a staged latent row: 37 x 16 bytes (odd), so the 16-byte
                                 // reads of 8 consecutive rows hit distinct bank groups
 constexpr int TILE = 32;        // positions per MFMA tile
-constexpr int LTILE = 64;       // positions per liveness tile
 constexpr uint32_t kSpinLimit = 1u << 23;
 
 // LDS ring of staged tiles. A buffer holds 32 latent rows at ROW_LDS pitch
@@ -282,27 +281,44 @@ __device__ inline void hand_over(const float (&send)[8], float4* __restrict__ xw
   xw[64] = make_float4(send[4], send[5], send[6], send[7]);
 }
 
+// Maximum over the 32 columns of a wave half of each of the 8 rows in v,
+// ending with row e = col & 7 in every lane (the four lanes of a row hold
+// equal bits). Each of the first three steps halves the rows a lane carries:
+// bit 0, 1, 2 of col picks the half it keeps, and it sends the other half to
+// the partner lane that keeps it (col ^ 1, col ^ 2, then col -+ 4 in the
+// 16-lane row, which flips bit 2 and keeps bits 0 and 1); two more steps
+// combine lanes that carry the same row (col -+ 8, then the other 16 lanes).
+__device__ __attribute__((always_inline)) inline float max32_row(const float (&v)[8], int col) {
+  const bool c0 = col & 1, c1 = (col >> 1) & 1, c2 = (col >> 2) & 1;
+  float w[4], y[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = fmaxf(c0 ? v[2 * i + 1] : v[2 * i], dpp<0xB1>(c0 ? v[2 * i] : v[2 * i + 1]));
+#pragma unroll
+  for (int j = 0; j < 2; ++j) y[j] = fmaxf(c1 ? w[2 * j + 1] : w[2 * j], dpp<0x4E>(c1 ? w[2 * j] : w[2 * j + 1]));
+  float z = fmaxf(c2 ? y[1] : y[0], dpp<0x124>(c2 ? y[0] : y[1]));   // row_ror:4
+  z = fmaxf(z, dpp<0x128>(z));                                           // row_ror:8
+  const float2 r = rows16(z);
+  return fmaxf(r.x, r.y);
+}
+
 // Split statistics of the finished tiles 2u and 2u + 1 (8 head rows of this
-// lane x its column each), which form 64-position liveness tile u: its
-// maximum per head, reduced over the 32 columns, goes to the tile-maximum
-// table (lane col writes row e = col mod 8 of its half; lanes with equal e
-// hold equal values) and becomes the running reference m; every lane adds
-// exp2(s - m) of its own two scores to a lane-local sum l (rescaled when m
-// grows). No branch: lanes select their table value arithmetically.
+// lane x its column each): each tile's maximum per head, reduced over the 32
+// columns, goes to the tile-maximum table (one entry per 32-position tile
+// when it fits in LDS, else one per pair: fine = false), lane col writing row
+// e = col mod 8 of its half (lanes with equal e hold equal values); every lane
+// keeps a running maximum m of its own scores and adds exp2(s - m) of its two
+// scores to its sum l (rescaled when m grows); the lanes are merged once, at
+// the end of the pass. No branch: the table index and value are selected.
 __device__ __attribute__((always_inline)) inline void tile_stats(int u, const float (&s0)[8], const float (&s1)[8],
-                                                                 float* __restrict__ tslot, int nlt, int esel,
+                                                                 float* __restrict__ tslot, bool fine, int col,
                                                                  float (&m)[8], float (&l)[8]) {
-  float tm[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) tm[e] = fmaxf(s0[e], s1[e]);
-  reduce32<true, 8>(tm);
-  float tv = tm[0];
-#pragma unroll
-  for (int e = 1; e < 8; ++e) tv = esel == e ? tm[e] : tv;
-  tslot[u] = tv;
+  const float t0 = max32_row(s0, col), t1 = max32_row(s1, col);
+  const float tb = fmaxf(t0, t1);
+  tslot[fine ? 2 * u : u] = fine ? t0 : tb;
+  tslot[fine ? 2 * u + 1 : u] = fine ? t1 : tb;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float mn = fmaxf(m[e], tm[e]);
+    const float mn = fmaxf(m[e], fmaxf(s0[e], s1[e]));
     const float ms = mn == -INFINITY ? 0.f : mn;  // nothing valid yet: every term is 0
     l[e] = l[e] * ex2(m[e] - ms) + ex2(s0[e] - ms) + ex2(s1[e] - ms);
     m[e] = mn;
@@ -324,7 +340,7 @@ template <int NW, bool CLOSE>
 __device__ __attribute__((always_inline)) inline void scoring_step(
     uint8_t* __restrict__ wr, const uint8_t* __restrict__ rd, const float4* __restrict__ xr,
     float4* __restrict__ xw, float* __restrict__ tslot, const TileSrc<NW>& src, int next_first, int wave, int lane,
-    int dh, int tprev, bool prev_valid, int nlt, int esel, const bf16x8 (&A)[HSTEPS], float hs, float (&own)[8],
+    int dh, int tprev, bool prev_valid, bool fine, const bf16x8 (&A)[HSTEPS], float hs, float (&own)[8],
     float (&m)[8], float (&l)[8], float (&sprev)[8]) {
   const int col = lane & 31, kh = lane >> 5;
   if (wr) issue_tile<NW>(wr, src, next_first, wave);
@@ -332,7 +348,7 @@ __device__ __attribute__((always_inline)) inline void scoring_step(
   score_half(rd, A, hs, col, kh, dh, cur, send);
   finish_scores(own, xr, prev_valid, s);
   if constexpr (CLOSE) {
-    tile_stats(tprev >> 1, sprev, s, tslot, nlt, esel, m, l);
+    tile_stats(tprev >> 1, sprev, s, tslot, fine, col, m, l);
   } else {
 #pragma unroll
     for (int e = 0; e < 8; ++e) sprev[e] = s[e];
@@ -377,7 +393,8 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
   constexpr int H = 32 * NB;          // heads
   extern __shared__ __align__(16) unsigned char smem[];
   const int P = a.P;
-  const int NLT = P / LTILE;          // liveness tiles per split
+  const bool fine = a.tpe == 1;       // tile-maximum entries per 32-position tile (else per pair)
+  const int NLT = P / (TILE * a.tpe); // tile-maximum entries per split
   uint8_t* ring = smem;                                                  // [NBUF][BUF_BYTES]
   float4* xbuf = reinterpret_cast<float4*>(ring + NBUF * BUF_BYTES);     // [2][NW][2][64] handed-over halves
   float* tmax = reinterpret_cast<float*>(xbuf + 2 * NW * 128);           // [H][NLT]
@@ -449,18 +466,18 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
   wait_tiles<NW>(min(2, T - 1), wave);
   bar_lds();
   scoring_step<NW, false>(wr_of(0), ring, xr_of(1), xw_of(0), tslot, src, pos0 + 3 * TILE, wave, lane, dh, -1, false,
-                          NLT, esel, A, hs, own, m, l, sprev);
+                          fine, A, hs, own, m, l, sprev);
   for (int t = 1; t < T; t += 2) {
     wait_tiles<NW>(min(2, T - 1 - t), wave);
     bar_lds();
     scoring_step<NW, false>(wr_of(t), ring + (t % NBUF) * BUF_BYTES, xr_of(t - 1), xw_of(t), tslot, src,
-                            pos0 + (t + 3) * TILE, wave, lane, dh, t - 1, pos0 + (t - 1) * TILE + col < ctx, NLT,
-                            esel, A, hs, own, m, l, sprev);
+                            pos0 + (t + 3) * TILE, wave, lane, dh, t - 1, pos0 + (t - 1) * TILE + col < ctx, fine,
+                            A, hs, own, m, l, sprev);
     if (t + 1 < T) {
       wait_tiles<NW>(min(2, T - 2 - t), wave);
       bar_lds();
       scoring_step<NW, true>(wr_of(t + 1), ring + ((t + 1) % NBUF) * BUF_BYTES, xr_of(t), xw_of(t + 1), tslot, src,
-                             pos0 + (t + 4) * TILE, wave, lane, dh, t, pos0 + t * TILE + col < ctx, NLT, esel, A, hs,
+                             pos0 + (t + 4) * TILE, wave, lane, dh, t, pos0 + t * TILE + col < ctx, fine, A, hs,
                              own, m, l, sprev);
     }
   }
@@ -468,11 +485,23 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
   {
     float s[8];
     finish_scores(own, xr_of(T - 1), pos0 + (T - 1) * TILE + col < ctx, s);
-    tile_stats((T - 1) >> 1, sprev, s, tslot, NLT, esel, m, l);
+    tile_stats((T - 1) >> 1, sprev, s, tslot, fine, col, m, l);
   }
   __syncthreads();
   stamp_mla(a, 2);
-  // split statistics per head: m is already common to the 32 columns; sum l
+  // split statistics per head: the lanes' running maxima differ; take the
+  // maximum over the 32 columns and rescale each lane's sum to it
+  {
+    float mm[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mm[e] = m[e];
+    reduce32<true, 8>(mm);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      l[e] = mm[e] == -INFINITY ? 0.f : l[e] * ex2(m[e] - mm[e]);
+      m[e] = mm[e];
+    }
+  }
   reduce32<false, 8>(l);
   if (col == 0) {
 #pragma unroll
@@ -558,7 +587,7 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
   __syncthreads();
   for (int i = tid; i < NLT * H; i += NT) {
     const int u = i % NLT, h = i / NLT;
-    if (pos0 + u * LTILE < ctx && tmax[h * NLT + u] >= lse[h] + log2tau - 0.01f) live[u] = 1;
+    if (pos0 + u * a.tpe * TILE < ctx && tmax[h * NLT + u] >= lse[h] + log2tau - 0.01f) live[u] = 1;
   }
   __syncthreads();
   if (wave == 0) {
@@ -648,8 +677,8 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
     }
     nkept += __popc(cm);
   };
-  const int n3 = 2 * nlive;                           // 32-position tiles to re-score
-  auto tile_at = [&](int k) { return 2 * live[k >> 1] + (k & 1); };
+  const int n3 = a.tpe * nlive;                       // 32-position tiles to re-score
+  auto tile_at = [&](int k) { return fine ? live[k] : 2 * live[k >> 1] + (k & 1); };
   // tile k is scored from buffer k % 2; even tiles are staged through st0,
   // odd ones through st1. Step k first stages tile k + 1 (loaded two steps
   // earlier) into the buffer tile k - 1 used and starts loading tile k + 3
@@ -1268,8 +1297,8 @@ const void* mla_out_dense_kernel(int H) {
 }
 
 // LDS bytes of mla_scores (every region is a multiple of 16 bytes).
-size_t mla_lds_bytes(int H, int P, int S) {
-  const int NLT = P / LTILE;
+size_t mla_lds_bytes(int H, int P, int S, int tpe) {
+  const int NLT = P / (TILE * tpe);
   const int NW = 2 * (H / 32);
   (void)S;
   return size_t(NBUF) * BUF_BYTES + size_t(2) * NW * 128 * 16 + size_t(H) * NLT * 4 + size_t(H) * 4 +
