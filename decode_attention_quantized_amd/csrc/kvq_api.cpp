@@ -213,6 +213,7 @@ int32_t launch_mla(const void* q, const kvq_cache* kcache, const kvq_cache* vcac
   a.mpart = reinterpret_cast<float*>(ws + plan.mws.mpart);
   a.ocnt = reinterpret_cast<uint32_t*>(ws + plan.mws.ocnt);
   a.done = reinterpret_cast<unsigned long long*>(ws + plan.mws.done);
+  a.lseo = reinterpret_cast<float*>(ws + plan.mws.lseo);
   // threshold 0 keeps every row: the output contraction is split over row
   // ranges (mla_out_dense when all its workgroups fit on the GPU at once,
   // else mla_out's per-block ranges); a positive threshold keeps few rows,
@@ -236,21 +237,22 @@ int32_t launch_mla(const void* q, const kvq_cache* kcache, const kvq_cache* vcac
   int dev = 0;
   (void)hipGetDevice(&dev);
   if (int64_t(per_cu) * device_info(dev).cus < plan.nwg) return KVQ_ERR_UNSUPPORTED;
+  // threshold 0 with mla_out_dense (all its workgroups resident at once): the
+  // scores kernel stores every score in its first pass and skips the re-score
+  // pass; the output kernel turns scores into weights with the LSE
+  const void* kd = threshold == 0.0f ? kvq::mla_out_dense_kernel(plan.G) : nullptr;
+  const size_t dl = kvq::mla_out_dense_lds(plan.G);
+  bool dense = false;
+  if (kd && dl <= size_t(device_info(dev).max_lds)) {
+    int pd = 0;
+    dense = hipOccupancyMaxActiveBlocksPerMultiprocessor(&pd, kd, kvq::kDenseOutThreads, dl) == hipSuccess &&
+            int64_t(pd) * device_info(dev).cus >= int64_t(kcache->batch) * (plan.G / 64) * a.R;
+  }
+  a.scores_out = dense ? 1 : 0;
   hipError_t e = launch(ks, plan.nwg, plan.threads, &a, plan.lds, l);
   if (e == hipSuccess) {
-    bool dense = false;
-    if (threshold == 0.0f) {
-      const void* kd = kvq::mla_out_dense_kernel(plan.G);
-      const size_t dl = kvq::mla_out_dense_lds(plan.G);
-      int pd = 0;
-      if (kd && dl <= size_t(device_info(dev).max_lds) &&
-          hipOccupancyMaxActiveBlocksPerMultiprocessor(&pd, kd, kvq::kDenseOutThreads, dl) == hipSuccess &&
-          int64_t(pd) * device_info(dev).cus >= int64_t(kcache->batch) * (plan.G / 64) * a.R) {
-        e = launch(kd, kcache->batch * (plan.G / 64) * a.R, kvq::kDenseOutThreads, &a, dl, l);
-        dense = true;
-      }
-    }
-    if (!dense) e = launch(kvq::mla_out_kernel(), kcache->batch * (plan.G / 32) * 4 * a.R, 256, &a, 0, l);
+    if (dense) e = launch(kd, kcache->batch * (plan.G / 64) * a.R, kvq::kDenseOutThreads, &a, dl, l);
+    else e = launch(kvq::mla_out_kernel(), kcache->batch * (plan.G / 32) * 4 * a.R, 256, &a, 0, l);
   }
   if (e != hipSuccess) {
     (void)hipGetLastError();

@@ -110,6 +110,8 @@ struct MlaArgs {
   unsigned long long* done;       // tagged [B][H/64][R]: every-row-kept ranges that wrote their partials
   int32_t R;                      // row ranges launched (per output block, or per sequence at threshold 0)
   int32_t tpe;                    // 32-position tiles per tile-maximum entry of the scores kernel (1 or 2)
+  int32_t scores_out;             // 1: kp holds every row's log2-domain scores (threshold 0, mla_out_dense)
+  float* lseo;                    // [B][H] log2-domain LSE per head (written when scores_out)
   int32_t B, Hq, ctx, cap;
   int32_t S, P;
   float sigma_log2e;
@@ -118,7 +120,7 @@ struct MlaArgs {
 };
 
 struct MlaLayout {
-  int64_t kept_mass, bgstat, split_ml, kcount, kpairs, kpos, kp, opart, mpart, ocnt, done, total;
+  int64_t kept_mass, bgstat, split_ml, kcount, kpairs, kpos, kp, opart, mpart, ocnt, done, lseo, total;
 };
 
 // The first two regions match ws_layout() so kvq_stats reads both families
@@ -135,6 +137,7 @@ inline MlaLayout mla_ws_layout(int B, int H, int S, int64_t SP, int R) {
   w.bgstat = off;    off = align256(off + int64_t(B) * 16);
   w.ocnt = off;      off = align256(off + int64_t(B) * (H / 32) * 4 * 4);
   w.done = off;      off = align256(off + int64_t(B) * (H >= 64 ? H / 64 : 1) * kMaxRanges * 8);
+  w.lseo = off;      off = align256(off + int64_t(B) * H * 4);
   w.split_ml = off;  off = align256(off + int64_t(B) * S * H * 16);
   w.kcount = off;    off = align256(off + int64_t(B) * S * 4);
   w.kpairs = off;    off = align256(off + int64_t(B) * S * 4);

@@ -325,6 +325,17 @@ __device__ __attribute__((always_inline)) inline void tile_stats(int u, const fl
   }
 }
 
+// Every score of a finished tile (threshold 0 with the dense output kernel):
+// dkp points at this lane's heads (hrow) in row 0 of the split's block of kp;
+// rows 8i+4kh+j of the lane are heads hrow + 8 (e >> 2) + (e & 3), column col
+// is position t * 32 + col of the split.
+__device__ __attribute__((always_inline)) inline void store_scores(float* __restrict__ dkp, int t, int col, int H,
+                                                                   const float (&s)[8]) {
+  float* d = dkp + (int64_t(t) * TILE + col) * H;
+  *reinterpret_cast<float4*>(d) = make_float4(s[0], s[1], s[2], s[3]);
+  *reinterpret_cast<float4*>(d + 8) = make_float4(s[4], s[5], s[6], s[7]);
+}
+
 // One tile of the scoring pass: start the direct loads of a later tile into
 // `wr` (when given), score this wave's half of the tile staged in `rd`, finish
 // the previous tile with the half the other wave handed over through `xr`,
@@ -341,12 +352,13 @@ __device__ __attribute__((always_inline)) inline void scoring_step(
     uint8_t* __restrict__ wr, const uint8_t* __restrict__ rd, const float4* __restrict__ xr,
     float4* __restrict__ xw, float* __restrict__ tslot, const TileSrc<NW>& src, int next_first, int wave, int lane,
     int dh, int tprev, bool prev_valid, bool fine, const bf16x8 (&A)[HSTEPS], float hs, float (&own)[8],
-    float (&m)[8], float (&l)[8], float (&sprev)[8]) {
+    float (&m)[8], float (&l)[8], float (&sprev)[8], float* __restrict__ dkp, int H) {
   const int col = lane & 31, kh = lane >> 5;
   if (wr) issue_tile<NW>(wr, src, next_first, wave);
   float cur[8], send[8], s[8];
   score_half(rd, A, hs, col, kh, dh, cur, send);
   finish_scores(own, xr, prev_valid, s);
+  if (dkp && tprev >= 0) store_scores(dkp, tprev, col, H, s);
   if constexpr (CLOSE) {
     tile_stats(tprev >> 1, sprev, s, tslot, fine, col, m, l);
   } else {
@@ -463,28 +475,31 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
   // Before each step: this wave's loads of tile t have landed (wait_tiles),
   // then everyone's have and tile t - 1's halves are handed over (barrier),
   // and buffer (t + 3) mod NBUF is free.
+  // threshold 0 with the dense output kernel: every finished tile's scores go to kp
+  float* dkp = a.scores_out ? a.kp + (int64_t(b) * a.S + split) * P * H + hrow : nullptr;
   wait_tiles<NW>(min(2, T - 1), wave);
   bar_lds();
   scoring_step<NW, false>(wr_of(0), ring, xr_of(1), xw_of(0), tslot, src, pos0 + 3 * TILE, wave, lane, dh, -1, false,
-                          fine, A, hs, own, m, l, sprev);
+                          fine, A, hs, own, m, l, sprev, dkp, H);
   for (int t = 1; t < T; t += 2) {
     wait_tiles<NW>(min(2, T - 1 - t), wave);
     bar_lds();
     scoring_step<NW, false>(wr_of(t), ring + (t % NBUF) * BUF_BYTES, xr_of(t - 1), xw_of(t), tslot, src,
                             pos0 + (t + 3) * TILE, wave, lane, dh, t - 1, pos0 + (t - 1) * TILE + col < ctx, fine,
-                            A, hs, own, m, l, sprev);
+                            A, hs, own, m, l, sprev, dkp, H);
     if (t + 1 < T) {
       wait_tiles<NW>(min(2, T - 2 - t), wave);
       bar_lds();
       scoring_step<NW, true>(wr_of(t + 1), ring + ((t + 1) % NBUF) * BUF_BYTES, xr_of(t), xw_of(t + 1), tslot, src,
                              pos0 + (t + 4) * TILE, wave, lane, dh, t, pos0 + t * TILE + col < ctx, fine, A, hs,
-                             own, m, l, sprev);
+                             own, m, l, sprev, dkp, H);
     }
   }
   bar_lds();
   {
     float s[8];
     finish_scores(own, xr_of(T - 1), pos0 + (T - 1) * TILE + col < ctx, s);
+    if (dkp) store_scores(dkp, T - 1, col, H, s);
     tile_stats((T - 1) >> 1, sprev, s, tslot, fine, col, m, l);
   }
   __syncthreads();
@@ -567,10 +582,23 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
       const float2 r23 = lse_merge(part[2 * H + h], part[3 * H + h]);
       const float2 rr = lse_merge(r01, r23);
       lse[h] = rr.x + log2f(rr.y);
+      if (a.scores_out && split == 0) a.lseo[int64_t(b) * H + h] = lse[h];
     }
     __syncthreads();
   }
   stamp_mla(a, 3);
+  if (a.scores_out) {
+    // every row is kept and its scores are stored: publish the positions only
+    const int nv = min(P, ctx - pos0);
+    const int64_t kb = int64_t(b) * a.S + split;
+    for (int i = tid; i < nv; i += NT) a.kpos[kb * P + i] = pos0 + i;
+    if (tid == 0) {
+      a.kcount[kb] = nv;
+      a.kpairs[kb] = nv * H;
+    }
+    stamp_mla(a, 4);
+    return;
+  }
 
   // ---------------------------------------------------------------- phase 3: live tiles
   // A 64-position tile is live when some head's tile maximum can reach the
@@ -1087,6 +1115,12 @@ __global__ __launch_bounds__(DN_NT) void mla_out_dense(MlaArgs a) {
   // scales of row tid
   struct Stage { uint4 v[NPV]; float4 w[NPW]; float4 sc; };
   const int vq = tid & 31, vb = (tid >> 5) & 7, vs = tid >> 8;
+  // kp holds the scores (log2 domain) of every row; this thread's weight
+  // pieces are always heads HW*hh + 4 (tid % 16) .. + 3, whose weight is
+  // exp2(score - LSE), as the scores kernel computes kept weights
+  float lsv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) lsv[j] = a.lseo[int64_t(b) * H + HW * hh + 4 * (tid & 15) + j];
   auto load_stage = [&](int c0, int seg0, int segn, Stage& st) {
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
@@ -1097,7 +1131,7 @@ __global__ __launch_bounds__(DN_NT) void mla_out_dense(MlaArgs a) {
 #pragma unroll
     for (int i = 0; i < NPW; ++i) {
       const int pw = tid + i * NT, rs = c0 + (pw >> 4) - seg0;
-      st.w[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      st.w[i] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);   // weight 0
       if (rs < segn)
         st.w[i] = *reinterpret_cast<const float4*>(a.kp + int64_t(rowtab[rs].x) * H + HW * hh + 4 * (pw & 15));
     }
@@ -1129,10 +1163,10 @@ __global__ __launch_bounds__(DN_NT) void mla_out_dense(MlaArgs a) {
 #pragma unroll
     for (int i = 0; i < NPW; ++i) {
       const int pw = tid + i * NT, sl = dn_slot(pw >> 4), h4 = pw & 15;
-      pf[(4 * h4 + 0) * DN_PP + sl] = st.w[i].x;
-      pf[(4 * h4 + 1) * DN_PP + sl] = st.w[i].y;
-      pf[(4 * h4 + 2) * DN_PP + sl] = st.w[i].z;
-      pf[(4 * h4 + 3) * DN_PP + sl] = st.w[i].w;
+      pf[(4 * h4 + 0) * DN_PP + sl] = exp2f(st.w[i].x - lsv[0]);
+      pf[(4 * h4 + 1) * DN_PP + sl] = exp2f(st.w[i].y - lsv[1]);
+      pf[(4 * h4 + 2) * DN_PP + sl] = exp2f(st.w[i].z - lsv[2]);
+      pf[(4 * h4 + 3) * DN_PP + sl] = exp2f(st.w[i].w - lsv[3]);
     }
     if (tid < DN_CHUNK) {
       const int sl = dn_slot(tid);
