@@ -1020,8 +1020,10 @@ __global__ __launch_bounds__(256) void mla_out(MlaArgs a) {
 // MFMAs); wave w owns heads 32(w/4)..+31 of the 64 and value group w%4 (four
 // MFMA column tiles of 32 dims). A 64-row chunk is staged once: values
 // converted to bf16 (exact) and transposed [dim][slot], weights transposed
-// [head][slot] in fp32, group scales [group][slot]. Loads are coalesced (32
-// lanes read one 512-byte value row, 16 lanes one row's 64 weights). The
+// [head][slot] in fp32 (the scores kernel stored every row's log2-domain
+// scores; the weight exp2(score - LSE) is formed here, as that kernel forms
+// kept weights), group scales [group][slot]. Loads are coalesced (32 lanes
+// read one 512-byte value row, 16 lanes one row's 64 scores). The
 // chunk's rows take the MFMA k order slot 8b + m <- row b + 8m: a thread
 // loads rows b + 8m, m = 4s..4s+3, of 16 dims, so each of its LDS writes is
 // 8 bytes (4 slots of one dim). Unit (dim d, block b) of 16 bytes sits at
