@@ -19,13 +19,15 @@
 //       converter, exact), applies the per-group fp32 scales to the fp32
 //       accumulators and hands the rows the other wave finishes over through
 //       LDS; the finished scores feed per-head (max, sum exp2) and a
-//       per-(head, 64-position tile) maximum, one tile behind the MFMAs;
-//    2. the group's split statistics are merged into per-head log-sum-exps
-//       (head h by split h mod S) and exchanged as epoch-tagged words;
-//    3. re-scores only the 64-position tiles whose maximum can reach the
-//       threshold (identical code, identical bits), computes the normalized
-//       weights and publishes, per kept row, its position and the weights of
-//       all heads (0 where a head skips it).
+//       per-(head, 32-position tile) maximum, one tile behind the MFMAs (at
+//       threshold 0 with mla_out_dense they are also stored, every row);
+//    2. every workgroup merges the split statistics of its sequence into
+//       per-head log-sum-exps (one exchange of epoch-tagged words);
+//    3. re-scores only the tiles whose maximum can reach the threshold
+//       (identical code, identical bits), computes the normalized weights
+//       and publishes, per kept row, its position and the weights of all
+//       heads (0 where a head skips it); at threshold 0 with the stored
+//       scores it publishes the positions only.
 //  mla_out     (one workgroup per (sequence, 32 heads, 128 value dims))
 //    sums p * v over the published rows of the sequence in split order and
 //    row order (deterministic), reading only the kept latent rows.
@@ -340,7 +342,7 @@ __device__ __attribute__((always_inline)) inline void store_scores(float* __rest
 // `wr` (when given), score this wave's half of the tile staged in `rd`, finish
 // the previous tile with the half the other wave handed over through `xr`,
 // and hand over this tile's other half through `xw`. CLOSE: the previous tile
-// closes a liveness tile (fold the pair into the statistics), else it opens
+// closes a pair of tiles (fold the pair into the statistics), else it opens
 // one (keep its scores in sprev). The restrict qualifiers state that the
 // buffer being filled, the buffer being read, the exchange slots and the
 // tile-maximum table are disjoint, so the compiler adds no wait for the
@@ -470,7 +472,7 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
   auto xr_of = [&](int t) { return xbuf + ((t & 1) * NW + partner) * 128 + lane; };
   auto xw_of = [&](int t) { return xbuf + ((t & 1) * NW + wave) * 128 + lane; };
   auto wr_of = [&](int t) { return t + 3 < T ? ring + ((t + 3) % NBUF) * BUF_BYTES : nullptr; };
-  // Step t scores tile t and finishes tile t - 1; a liveness tile closes at
+  // Step t scores tile t and finishes tile t - 1; a pair of tiles closes at
   // even t >= 2. Step 0 finishes nothing (its "previous" scores are dropped).
   // Before each step: this wave's loads of tile t have landed (wait_tiles),
   // then everyone's have and tile t - 1's halves are handed over (barrier),
@@ -601,9 +603,10 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
   }
 
   // ---------------------------------------------------------------- phase 3: live tiles
-  // A 64-position tile is live when some head's tile maximum can reach the
-  // threshold (a small margin keeps the test conservative); only live tiles
-  // are re-read and re-scored, with the same code and so the same bits.
+  // A table entry (a 32-position tile, or a pair of them when the finer table
+  // does not fit) is live when some head's maximum can reach the threshold
+  // (a small margin keeps the test conservative); only the tiles of live
+  // entries are re-read and re-scored, with the same code and so the same bits.
   const float log2tau = a.tau > 0.f ? log2f(a.tau) : -INFINITY;
   // every (tile, head) pair is tested by its own thread and marks its tile
   // (all marks store the same 1); wave 0 then compacts the marked tile ids in
