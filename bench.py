@@ -200,7 +200,7 @@ def cpu_baseline(inp, budget_s=12.0):
                        sigma=w.sigma, threshold=w.threshold)
         calls += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or calls >= 50:
+        if el >= budget_s or calls >= 400:
             break
     return dict(value=calls * w.batch / el, unit="tokens/s", cores=int(threads), kind="oracle",
                 sample=f"{calls} whole calls of the timed workload (B={w.batch}, ctx={w.ctx}, "
