@@ -26,18 +26,22 @@ def test_mla_small(threshold):
 
 
 @pytest.mark.parametrize("heads", [32, 64])
-def test_mla_head_counts(heads):
-    say("case mla heads", heads)
-    inp, tau = _case(batch=1, q_heads=heads, ctx=3000, hot=6)
+@pytest.mark.parametrize("threshold", [None, 0.0])
+def test_mla_head_counts(heads, threshold):
+    """32 heads (no dense output kernel: row ranges of the per-block kernel
+    at threshold 0) and 64 heads (one 64-head set per sequence)."""
+    say("case mla heads", heads, "threshold", "of the workload" if threshold is None else threshold)
+    inp, tau = _case(threshold, batch=1, q_heads=heads, ctx=3000, hot=6)
     g = run_gpu(inp, tau, q_bf16=True)
     r, po = oracle_for(inp, tau)
     compare(inp, tau, g, r, po, mask=False)
 
 
 @pytest.mark.parametrize("ctx", [1, 100, 3001])
-def test_mla_ragged(ctx):
-    say("case mla ragged ctx", ctx)
-    inp, tau = _case(batch=1, ctx=ctx, hot=min(4, ctx))
+@pytest.mark.parametrize("threshold", [None, 0.0])
+def test_mla_ragged(ctx, threshold):
+    say("case mla ragged ctx", ctx, "threshold", "of the workload" if threshold is None else threshold)
+    inp, tau = _case(threshold, batch=1, ctx=ctx, hot=min(4, ctx))
     g = run_gpu(inp, tau, q_bf16=True)
     r, po = oracle_for(inp, tau)
     compare(inp, tau, g, r, po, mask=False)
