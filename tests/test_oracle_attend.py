@@ -172,3 +172,29 @@ def test_workloads_match_the_pages_regime():
     r, _ = A.attend_inputs(inp)
     assert r.kept_pairs / r.mask.size < 0.10
     assert 1.0 - r.kept_mass.min() < 5e-3
+
+
+def test_band_is_relative_to_the_float32_threshold():
+    """The mask band (weights within 1e-3 relative of the threshold, measured
+    on the float32 value the kernels receive) against constructed weights:
+    just inside / just outside the relative band on both sides, the threshold
+    itself, a band that an absolute 1e-3 or a factor of 1e-2 would get wrong,
+    and no band at threshold 0."""
+    for tau in (1e-6, 3e-5, 0.01, 0.25):
+        t32 = float(np.float32(tau))
+        p = np.array([t32, t32 * (1 + 0.999e-3), t32 * (1 - 0.999e-3), t32 * (1 + 1.001e-3), t32 * (1 - 1.001e-3),
+                      t32 * 1.005, t32 * 0.995, t32 * 2, t32 / 2, 0.0, 1.0])
+        want = np.array([True, True, True, False, False, False, False, False, False, False, False])
+        assert np.array_equal(A.band(p, tau), want), tau
+    # relative, not absolute: at tau = 0.01 an absolute band of 1e-3 would take
+    # 0.0105, which is 5% away
+    assert not A.band(np.array([0.0105, 0.0095]), 0.01).any()
+    # the float64 threshold 1e-6 is not the float32 one the kernels use; the
+    # band is taken around the float32 value
+    t32 = float(np.float32(1e-6))
+    assert t32 != 1e-6
+    p = np.array([t32 * (1 + 0.9995e-3)])
+    assert A.band(p, 1e-6).all()
+    assert not A.band(np.array([0.5, 1e-6, 1e-30]), 0.0).any()
+    # shape is kept (per (batch, head, position) weights)
+    assert A.band(np.full((2, 3, 4), 1e-6), 1e-6).shape == (2, 3, 4)
