@@ -31,7 +31,12 @@ sys.path.insert(0, ROOT)
 METRIC = "decode-attn tokens/s + KV GB/s (% HBM roofline) at 32K ctx, sparse-V on/off"
 HBM_PEAK_GBS = 8000.0
 ROTATION_BYTES = 640 << 20
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gqa_fused_long.json")
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")
+KERNEL_NAMES = {"long": "kvq::gqa_fused<q4_0, G=8>", "lut3": "kvq::gqa_fused<lut3, G=8>"}
+WORKLOAD_TEXT = {
+    "long": "long-ctx q4_0: batch 1, 32/4 heads, dim 128, ctx 32768",
+    "lut3": "LUT3: batch 8, 32/4 heads, dim 128, ctx 32768, 8..64 hot per kv head",
+}
 KERNEL_SRC = os.path.join(ROOT, "decode_attention_quantized_amd", "csrc", "kvq_gqa.hip")
 
 
@@ -40,11 +45,15 @@ def kernel_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def load_traffic(mode: str):
+def traffic_file(workload: str) -> str:
+    return os.path.join(TRAFFIC_DIR, f"traffic_gqa_fused_{workload}.json")
+
+
+def load_traffic(mode: str, workload: str = "long"):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current kernel source; else None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -54,7 +63,7 @@ def load_traffic(mode: str):
     return None if m is None else m.get("bytes_per_launch")
 
 
-def write_traffic(base: str) -> dict:
+def write_traffic(base: str, workload: str = "long") -> dict:
     """Turn six rocprofv3 --pmc runs under `base` (fs/ws: FETCH_SIZE and
     WRITE_SIZE at threshold 1e-6, fd/wd: the same at threshold 0, cf/cw: the
     plain device copy of --copy-calibration) into calibrated HBM bytes per
@@ -78,8 +87,8 @@ def write_traffic(base: str) -> dict:
     _, cf = per_dispatch("cf", "copyBuffer")
     _, cw = per_dispatch("cw", "copyBuffer")
     ff, wf = n / 1024 / cf, n / 1024 / cw
-    t = {"kernel": "kvq::gqa_fused<q4_0, G=8>",
-         "workload": "long-ctx q4_0: batch 1, 32/4 heads, dim 128, ctx 32768",
+    t = {"kernel": KERNEL_NAMES[workload],
+         "workload": WORKLOAD_TEXT[workload],
          "kernel_sha256_16": kernel_hash(),
          "calibration": {"copy_bytes_each_way": n, "copy_FETCH_SIZE_KiB": cf, "copy_WRITE_SIZE_KiB": cw,
                          "fetch_factor": ff, "write_factor": wf}}
@@ -88,9 +97,22 @@ def write_traffic(base: str) -> dict:
         _, wk = per_dispatch(ws, "gqa_fused")
         t[mode] = {"FETCH_SIZE_KiB": fk, "WRITE_SIZE_KiB": wk, "dispatches": nd,
                    "bytes_per_launch": int(round((fk * ff + wk * wf) * 1024))}
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(traffic_file(workload), "w") as f:
         json.dump(t, f, indent=1)
     return t
+
+
+def mode_name(tau):
+    return "sparse" if tau > 0 else "dense"
+
+
+def check_stats(st, where):
+    """Every timed call must have completed normally: a bounded wait that gave
+    up leaves a sticky status bit in the workspace (and kvq_stats returns
+    KVQ_ERR_DEVICE), and its output is not the attention result."""
+    if st["status"] != 0 or st["rc"] != 0:
+        raise SystemExit(f"bench.py: {where} reported a device fault (status {st['status']}, rc {st['rc']}); "
+                         "no measurement is valid")
 
 
 def time_mode(att, q, caches, ctx, tau, steps, warmup, out, stream):
@@ -110,6 +132,7 @@ def time_mode(att, q, caches, ctx, tau, steps, warmup, out, stream):
         for i in range(warmup):
             call(i)
     torch.cuda.synchronize()
+    check_stats(att.stats(), f"{mode_name(tau)} warm-up")
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     with torch.cuda.stream(stream):
         for i in range(steps):
@@ -134,80 +157,130 @@ def time_mode(att, q, caches, ctx, tau, steps, warmup, out, stream):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     st = att.stats()
+    check_stats(st, f"{mode_name(tau)} calls")
     return dict(wall=(t1 - t0) / steps, kernel_mean=e0.elapsed_time(e1) * 1e-3 / steps,
                 eager_median=per[len(per) // 2], eager_p10=per[len(per) // 10],
                 eager_p90=per[(9 * len(per)) // 10], stats=st)
 
 
-def stream_reference(nbytes, grid, steps, warmup, stream):
-    """The plain streaming-read kernel over the same number of bytes and the
-    same grid as a decode call, from buffers rotated like the caches (every
-    launch reads cold HBM), timed like the decode call (HIP events around one
-    graph replay on the launch stream)."""
+def stream_reference(nbytes, grid, steps, warmup, stream, sweep=True):
+    """The plain streaming-read kernel over the same number of bytes as a
+    decode call, from buffers rotated like the caches (every launch reads cold
+    HBM), timed like the decode call (HIP events around one graph replay on
+    the launch stream): on the decode call's grid, and (sweep) over grids of
+    256..4096 workgroups of 256, 512 or 1024 threads, whose fastest is the
+    floor a read of these bytes reaches on this GPU."""
     import torch
 
     import decode_attention_quantized_amd as kvq
     nbytes = nbytes // 16 * 16
     R = max(2, math.ceil(ROTATION_BYTES / nbytes))
     bufs = torch.zeros((R, nbytes), dtype=torch.uint8, device="cuda")
-    sink = torch.zeros(grid, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
 
-    def call(i):
-        kvq.kvq_stream_read(bufs[i % R], grid, sink, stream=stream)
+    def timed(gr, threads, n_steps):
+        def call(i):
+            kvq.kvq_stream_read(bufs[i % R], gr, sink, stream=stream, threads=threads)
 
-    with torch.cuda.stream(stream):
-        for i in range(warmup):
-            call(i)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        for i in range(steps):
-            call(warmup + i)
-    with torch.cuda.stream(stream):
-        g.replay()                                              # untimed
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        e0.record()
-        g.replay()
-        e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / steps
-    del g, bufs
-    return {"kernel": "kvq_stream_read (plain 16-byte loads, 1024 threads per workgroup)", "bytes": nbytes,
-            "grid": grid, "us_per_launch": round(us, 3), "gbs": round(nbytes / us / 1e3, 1),
-            "frac_hbm": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4), "rotation_sets": R}
+        with torch.cuda.stream(stream):
+            for i in range(warmup):
+                call(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(n_steps):
+                call(warmup + i)
+        with torch.cuda.stream(stream):
+            g.replay()                                          # untimed
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record()
+            g.replay()
+            e1.record()
+        torch.cuda.synchronize()
+        del g
+        return e0.elapsed_time(e1) * 1e3 / n_steps
+
+    us = timed(grid, 1024, steps)
+    res = {"kernel": "kvq_stream_read (plain 16-byte loads, up to 8 in flight per thread)", "bytes": nbytes,
+           "grid": grid, "threads": 1024, "us_per_launch": round(us, 3), "gbs": round(nbytes / us / 1e3, 1),
+           "frac_hbm": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4), "rotation_sets": R}
+    if sweep:
+        table = []
+        for threads in (256, 512, 1024):
+            for gr in (256, 512, 1024, 2048, 4096):
+                table.append((round(timed(gr, threads, min(steps, 100)), 3), gr, threads))
+        best = min(table)
+        res["sweep_us_grid_threads"] = table
+        res["floor"] = {"us_per_launch": best[0], "grid": best[1], "threads": best[2],
+                        "gbs": round(nbytes / best[0] / 1e3, 1),
+                        "frac_hbm": round(nbytes / best[0] / 1e3 / HBM_PEAK_GBS, 4)}
+    del bufs
+    return res
 
 
-def cpu_baseline(inp, budget_s=12.0):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(inp, runs=5, run_s=1.2):
     """The fp64 oracle, as it stands, on a bounded sample: whole decode calls of
-    the same workload (excluding packing), repeated until ~budget_s."""
+    the same workload (excluding packing). Each run repeats whole calls for
+    about run_s seconds; the figure is the median over `runs` runs, once with
+    the BLAS pool limited to one thread and once with its default size (the
+    host's cores). The oracle's dequantization and exponentials are
+    single-threaded numpy; only its matrix products use the BLAS pool, so the
+    process CPU time over wall time is reported as the parallelism reached."""
     import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import attend as A
     from oracle import formats as F
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
     w = inp.w
     kc, ks = F.pack(w.fmt, inp.k)
     vc, vs = F.pack(w.fmt, inp.v)
-    calls, t0 = 0, time.perf_counter()
     ref = None
-    while True:
-        ref = A.attend(inp.q, kc, ks, vc, vs, fmt=w.fmt, dim=w.dim, v_dim=w.v_dim, ctx_len=w.ctx,
-                       sigma=w.sigma, threshold=w.threshold)
-        calls += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or calls >= 400:
-            break
-    return dict(value=calls * w.batch / el, unit="tokens/s", cores=int(threads), kind="oracle",
-                sample=f"{calls} whole calls of the timed workload (B={w.batch}, ctx={w.ctx}, "
-                       f"{w.q_heads}/{w.kv_heads} heads), fp64 numpy, packing excluded, {el:.1f} s"), ref, (kc, ks)
+
+    def one_config(limit):
+        nonlocal ref
+        rates, cpu, wall, calls_total = [], 0.0, 0.0, 0
+        with threadpool_limits(limits=limit):
+            pool = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+            for _ in range(runs):
+                calls, t0, c0 = 0, time.perf_counter(), time.process_time()
+                while True:
+                    ref = A.attend(inp.q, kc, ks, vc, vs, fmt=w.fmt, dim=w.dim, v_dim=w.v_dim, ctx_len=w.ctx,
+                                   sigma=w.sigma, threshold=w.threshold)
+                    calls += 1
+                    el = time.perf_counter() - t0
+                    if el >= run_s:
+                        break
+                cpu += time.process_time() - c0
+                wall += el
+                calls_total += calls
+                rates.append(calls * w.batch / el)
+        return dict(value=float(np.median(rates)), runs=[round(r, 3) for r in rates], blas_threads=int(pool),
+                    cpu_time_over_wall=round(cpu / wall, 2), calls=calls_total, seconds=round(wall, 1))
+
+    one = one_config(1)
+    many = one_config(None)
+    res = dict(value=many["value"], unit="tokens/s", cores=many["blas_threads"], kind="oracle",
+               sample=f"median of {runs} runs of about {run_s} s, each whole calls of the timed workload "
+                      f"(B={w.batch}, ctx={w.ctx}, {w.q_heads}/{w.kv_heads} heads), fp64 numpy, packing excluded; "
+                      f"BLAS pool at its default size (cores = its threads; dequantization and exp are "
+                      f"single-threaded numpy)",
+               all_cores=many, one_thread=one, host_cpus=os.cpu_count(), cpu_model=cpu_model())
+    return res, ref, (kc, ks)
 
 
-def run_config(w, steps, warmup, splits=0):
+def run_config(w, steps, warmup, splits=0, modes=("sparse", "dense"), single_pass=True):
     """Graph-timed sparse (w.threshold) and dense (threshold 0) calls of one
     workload; returns one JSON-ready dict. Caches rotate over copies larger
     than twice the 256 MB Infinity Cache."""
@@ -241,8 +314,8 @@ def run_config(w, steps, warmup, splits=0):
                           q_dtype=kvq.KVQ_Q_BF16 if w.q_bf16 else kvq.KVQ_Q_F32,
                           v_dim=w.v_dim if latent else 0)
     res = {m: time_mode(att, q, caches, w.ctx, tau, steps, warmup, out, stream)
-           for m, tau in (("sparse", w.threshold), ("dense", 0.0))}
-    if not latent:                                   # the single-pass skip rule (grouped formats)
+           for m, tau in (("sparse", w.threshold), ("dense", 0.0)) if m in modes}
+    if not latent and single_pass:                   # the single-pass skip rule (grouped formats)
         att_run = DecodeAttention(K0, V0, w.q_heads, ctx_len=w.ctx, softmax_scale=w.sigma, splits=splits,
                                   stream=stream, q_dtype=kvq.KVQ_Q_BF16 if w.q_bf16 else kvq.KVQ_Q_F32,
                                   running=True)
@@ -265,10 +338,30 @@ def run_config(w, steps, warmup, splits=0):
             d["mfma_tflops"] = round(flops / r["kernel_mean"] / 1e12, 2)
             d["frac_mfma_bf16"] = round(flops / r["kernel_mean"] / 1e12 / 2500.0, 4)
         line[m] = d
-    line["speedup_sparse_vs_dense"] = round(res["dense"]["wall"] / res["sparse"]["wall"], 3)
+    if "dense" in res and "sparse" in res:
+        line["speedup_sparse_vs_dense"] = round(res["dense"]["wall"] / res["sparse"]["wall"], 3)
     if "single_pass" in res:
         line["single_pass"]["extra_rows_vs_exact"] = (res["single_pass"]["stats"]["rows_fetched"]
                                                       - res["sparse"]["stats"]["rows_fetched"])
+    torch.cuda.synchronize()
+    del att, caches, K0, V0, q, out
+    return line
+
+
+def lut3_object(steps, warmup):
+    """The LUT3 configuration (batch 8, 32/4 heads, ctx 32768: the larger of
+    the two 32K configurations) timed like the headline one, as a nested
+    object of the default line with its own roofline."""
+    import synth
+    w = synth.workload("lut3")
+    line = run_config(w, steps, warmup, single_pass=False)
+    sp = line["sparse"]
+    line["roofline"] = {"bound": "hbm", "achieved": sp["achieved_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": sp["frac_hbm"], "traffic": load_traffic("sparse", "lut3"),
+                        "kernel": KERNEL_NAMES["lut3"], "algorithmic_bytes_per_launch": sp["algorithmic_bytes"],
+                        "kernel_us_mean": sp["kernel_us_mean"],
+                        "timing": "HIP events around one graph replay of the timed steps, on the launch stream"}
+    line["dense"]["traffic"] = load_traffic("dense", "lut3")
     return line
 
 
@@ -350,10 +443,13 @@ def main():
                          "configuration (sweep: one per context length)")
     ap.add_argument("--write-traffic", metavar="DIR",
                     help="no GPU work: summarize rocprofv3 counter runs under DIR (fs ws fd wd cf cw) "
-                         "into the committed traffic file")
+                         "into the committed traffic file of --traffic-workload")
+    ap.add_argument("--traffic-workload", choices=["long", "lut3"], default="long")
+    ap.add_argument("--no-lut3", action="store_true",
+                    help="leave the LUT3 (batch 8, ctx 32768) object out of the default line")
     args = ap.parse_args()
     if args.write_traffic:
-        print(json.dumps(write_traffic(args.write_traffic)), flush=True)
+        print(json.dumps(write_traffic(args.write_traffic, args.traffic_workload)), flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU; multi-GPU sharding is not implemented "
@@ -383,8 +479,13 @@ def main():
         return
     if args.workload != "long":
         names = [f"sweep_{n}" for n in synth.SWEEP] if args.workload == "sweep" else [args.workload]
+        if args.profile_mode == "both":
+            modes, single = ("sparse", "dense"), True
+        else:
+            modes, single = (args.profile_mode,), args.profile_mode == "single_pass"
         for nm in names:
-            print(json.dumps(run_config(synth.workload(nm), args.steps, args.warmup, args.splits)), flush=True)
+            print(json.dumps(run_config(synth.workload(nm), args.steps, args.warmup, args.splits, modes=modes,
+                                        single_pass=single)), flush=True)
         return
 
     w = synth.workload("long")
@@ -503,7 +604,14 @@ def main():
     # what a read of this size and launch shape reaches on this GPU
     sref = stream_reference(ab, int(r["stats"]["splits"]) * w.batch * w.kv_heads, args.steps, args.warmup, stream)
     sref["decode_kernel_over_stream_read"] = round(r["kernel_mean"] * 1e6 / sref["us_per_launch"], 3)
+    sref["decode_kernel_over_floor"] = round(r["kernel_mean"] * 1e6 / sref["floor"]["us_per_launch"], 3)
     line["stream_read_same_bytes"] = sref
+    # the long workload's device buffers are released before the next workload
+    torch.cuda.synchronize()
+    del att, att_run, caches, K0, V0
+    torch.cuda.empty_cache()
+    if not args.no_lut3 and args.profile_mode == "both":
+        line["lut3_32k"] = lut3_object(args.steps, args.warmup)
     if not args.no_cpu_baseline:
         cb_, ref, (okc, oks) = cpu_baseline(inp)
         line["cpu_baseline"] = cb_
@@ -515,6 +623,12 @@ def main():
                               bool(np.array_equal(okc, kc) and np.array_equal(oks, ks)),
                               "kept_pairs": int(r["stats"]["kept_pairs"]), "oracle_kept_pairs": ref.kept_pairs}
     print(json.dumps(line), flush=True)
+    # explicit teardown: every queued launch has finished and the remaining
+    # device buffers and the side stream are released before interpreter exit
+    torch.cuda.synchronize()
+    del q, out, stream
+    torch.cuda.empty_cache()
+    torch.cuda.synchronize()
 
 
 if __name__ == "__main__":

@@ -18,6 +18,7 @@ KVQ_Q8_0, KVQ_Q4_0, KVQ_LUT3, KVQ_FP8_B128, KVQ_LUT3_WHT = 0, 1, 2, 3, 4
 KVQ_Q_F32, KVQ_Q_BF16 = 0, 1
 KVQ_LAUNCH_COOPERATIVE = 1
 KVQ_SKIP_RUNNING = 2
+KVQ_TEST_WITHHOLD = 4
 FMT = {"q8_0": KVQ_Q8_0, "q4_0": KVQ_Q4_0, "lut3": KVQ_LUT3, "fp8_b128": KVQ_FP8_B128, "lut3_wht": KVQ_LUT3_WHT}
 
 ERRORS = {0: "OK", -1: "ARG", -2: "ALIGN", -3: "RANGE", -4: "NONFINITE", -5: "WORKSPACE",
@@ -79,7 +80,7 @@ def lib() -> ctypes.CDLL:
         L.kvq_stats.argtypes = [ctypes.POINTER(kvq_launch), ctypes.POINTER(kvq_stats_t), vp]
         L.kvq_phase_count.argtypes = [ctypes.POINTER(kvq_launch), ctypes.POINTER(i32), ctypes.POINTER(i32)]
         L.kvq_strerror.argtypes = [i32]
-        L.kvq_stream_read.argtypes = [vp, i64, i32, vp, vp]
+        L.kvq_stream_read.argtypes = [vp, i64, i32, i32, vp, vp]
         L.kvq_strerror.restype = ctypes.c_char_p
         for name in EXPORTS:
             if name != "kvq_strerror":
@@ -223,17 +224,18 @@ def kvq_stats(launch: kvq_launch, kept_mass: bool = True):
     return d
 
 
-def kvq_stream_read(src, grid: int, sink, stream=None, nbytes: int | None = None):
+def kvq_stream_read(src, grid: int, sink, stream=None, nbytes: int | None = None, threads: int = 1024):
     """Streaming-read reference: read ``nbytes`` (default: all) bytes of the
-    device tensor ``src`` with ``grid`` 1024-thread workgroups on ``stream``
-    (a torch.cuda.Stream, or None for the default stream); each workgroup
-    XORs the 32-bit words it read into ``sink[g]`` (device int32 tensor of at
-    least ``grid`` elements)."""
+    device tensor ``src`` with ``grid`` workgroups of ``threads`` threads on
+    ``stream`` (a torch.cuda.Stream, or None for the default stream); each
+    workgroup XORs the 32-bit words it read into ``sink[g]`` (device int32
+    tensor of at least ``grid`` elements)."""
     n = src.numel() * src.element_size() if nbytes is None else int(nbytes)
     if sink.numel() < grid:
         raise KvqError(-1, "kvq_stream_read: sink holds fewer words than the grid")
     st = stream.cuda_stream if stream is not None else None
-    _check(lib().kvq_stream_read(src.data_ptr(), n, int(grid), sink.data_ptr(), st), "kvq_stream_read")
+    _check(lib().kvq_stream_read(src.data_ptr(), n, int(grid), int(threads), sink.data_ptr(), st),
+           "kvq_stream_read")
 
 
 def kvq_phase_count(launch: kvq_launch):

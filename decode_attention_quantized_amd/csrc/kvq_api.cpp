@@ -155,6 +155,15 @@ int32_t make_plan(int32_t fmt, const kvq_cache* k, const kvq_launch* l, int32_t 
   S = (ctx_len + P - 1) / P;                             // drop splits that would be empty
   if (P > 8192) return KVQ_ERR_UNSUPPORTED;              // per-split counts are packed in 14/18 bits
   if (S > 2048 || BG * S > (int64_t(1) << 30)) return KVQ_ERR_UNSUPPORTED;
+  // limits of the in-kernel exchanges (each thread reads at most two of the
+  // group's split statistics, one 16-byte piece of partial outputs and two
+  // kept-mass and flag words)
+  {
+    const int64_t E = kvq::gqa_merge_slice(G, S);
+    const int64_t nh = S >= G ? 1 : (G + S - 1) / S;
+    if (int64_t(S) * G > 2 * kvq::kThreads || (E / 2) * S > kvq::kThreads || nh * S > 2 * kvq::kThreads)
+      return KVQ_ERR_UNSUPPORTED;
+  }
   const size_t lds = kvq::gqa_lds_bytes(fmt, G, P, S);
   if (lds > size_t(di.max_lds)) return KVQ_ERR_UNSUPPORTED;
 
@@ -193,7 +202,7 @@ int32_t launch_mla(const void* q, const kvq_cache* kcache, const kvq_cache* vcac
   if (!aligned16(kcache->codes) || !aligned16(kcache->scales) || !aligned16(q) || !aligned16(out) ||
       (l->workspace && !aligned16(l->workspace)))
     return KVQ_ERR_ALIGN;
-  if (l->mask_out) return KVQ_ERR_UNSUPPORTED;
+  if (l->mask_out && !aligned16(l->mask_out)) return KVQ_ERR_ALIGN;
   if (!l->workspace || l->workspace_bytes < plan.total) return KVQ_ERR_WORKSPACE;
   unsigned char* ws = static_cast<unsigned char*>(l->workspace);
   kvq::MlaArgs a{};
@@ -214,6 +223,8 @@ int32_t launch_mla(const void* q, const kvq_cache* kcache, const kvq_cache* vcac
   a.ocnt = reinterpret_cast<uint32_t*>(ws + plan.mws.ocnt);
   a.done = reinterpret_cast<unsigned long long*>(ws + plan.mws.done);
   a.lseo = reinterpret_cast<float*>(ws + plan.mws.lseo);
+  a.mask_out = l->mask_out;
+  a.mask_words = (ctx_len + 31) / 32;
   // threshold 0 keeps every row: the output contraction is split over row
   // ranges (mla_out_dense when all its workgroups fit on the GPU at once,
   // else mla_out's per-block ranges); a positive threshold keeps few rows,
@@ -229,6 +240,8 @@ int32_t launch_mla(const void* q, const kvq_cache* kcache, const kvq_cache* vcac
   a.sigma_log2e = sigma_log2e_of(l, 192);                 // default scale 1/sqrt(qk_nope + rope = 192)
   a.tau = threshold;
   a.times = reinterpret_cast<unsigned long long*>(l->phase_times);
+  a.withhold = (l->flags & KVQ_TEST_WITHHOLD) != 0;
+  a.spin_limit = a.withhold ? kvq::kTestSpinLimit : kvq::kSpinLimit;
   const void* ks = kvq::mla_scores_kernel(plan.G);
   if (!ks) return KVQ_ERR_UNSUPPORTED;
   int per_cu = 0;
@@ -317,7 +330,7 @@ extern "C" int32_t kvq_decode_attn(const void* q, const kvq_cache* kcache, const
                                    const kvq_launch* l) {
   if (!q || !kcache || !out || !l) return KVQ_ERR_ARG;
   if (!(threshold >= 0.0f) || !(threshold < 1.0f)) return KVQ_ERR_RANGE;   // also rejects NaN
-  if (l->flags & ~int32_t(KVQ_LAUNCH_COOPERATIVE | KVQ_SKIP_RUNNING)) return KVQ_ERR_ARG;
+  if (l->flags & ~int32_t(KVQ_LAUNCH_COOPERATIVE | KVQ_SKIP_RUNNING | KVQ_TEST_WITHHOLD)) return KVQ_ERR_ARG;
   Plan plan;
   int32_t rc = make_plan(fmt, kcache, l, ctx_len, &plan);
   if (rc) return rc;
@@ -366,6 +379,8 @@ extern "C" int32_t kvq_decode_attn(const void* q, const kvq_cache* kcache, const
   a.sigma_log2e = sigma_log2e_of(l, kcache->dim);
   a.tau = threshold;
   a.times = reinterpret_cast<unsigned long long*>(l->phase_times);
+  a.withhold = (l->flags & KVQ_TEST_WITHHOLD) != 0;
+  a.spin_limit = a.withhold ? kvq::kTestSpinLimit : kvq::kSpinLimit;
 
   const void* kern = kvq::gqa_kernel(fmt, plan.G, (l->flags & KVQ_SKIP_RUNNING) != 0);
   if (!kern) return KVQ_ERR_UNSUPPORTED;

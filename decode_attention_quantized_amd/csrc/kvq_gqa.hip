@@ -40,8 +40,6 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 
-constexpr uint32_t kSpinLimit = 1u << 23;
-
 __device__ inline void stamp(const GqaArgs& a, int k) {
   if (a.times && threadIdx.x == 0) a.times[int64_t(blockIdx.x) * 16 + k] = wall_clock64();
 }
@@ -73,6 +71,21 @@ __device__ inline float sum_wave(float v) {
   v += dppf<0x140>(v);                                // row_mirror
   const float r1 = __shfl(v, 16), r2 = __shfl(v, 32), r3 = __shfl(v, 48);
   return (v + r1) + (r2 + r3);
+}
+
+// Maximum over the 64 lanes (rows with DPP, then the four rows with the
+// lane-swap instructions); every lane holds the result.
+__device__ inline float max_wave(float v) {
+  v = fmaxf(v, dppf<0xB1>(v));                        // quad_perm [1,0,3,2]
+  v = fmaxf(v, dppf<0x4E>(v));                        // quad_perm [2,3,0,1]
+  v = fmaxf(v, dppf<0x141>(v));                       // row_half_mirror
+  v = fmaxf(v, dppf<0x140>(v));                       // row_mirror
+  auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v),
+                                            false, false);
+  v = fmaxf(__builtin_bit_cast(float, unsigned(r[0])), __builtin_bit_cast(float, unsigned(r[1])));
+  r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v), false,
+                                       false);
+  return fmaxf(__builtin_bit_cast(float, unsigned(r[0])), __builtin_bit_cast(float, unsigned(r[1])));
 }
 
 // lse_merge over the lanes of equal lane mod C (C = 1, 2, 4 or 8): rotations
@@ -118,6 +131,17 @@ __device__ inline float2 merge_row16(float2 x) {
   return x;
 }
 
+// The defined result of a value that depended on a wait that gave up. The
+// kernels are compiled without NaN semantics (their arithmetic never makes
+// one), so the NaN pattern is passed through an empty asm statement: the
+// compiler cannot see that it is a NaN and fold the selection away.
+constexpr uint32_t kNaNBits = 0x7FC00000u;
+__device__ inline float poison_if(bool bad, float v) {
+  uint32_t nan_bits = kNaNBits;
+  asm volatile("" : "+v"(nan_bits));
+  return __uint_as_float(bad ? nan_bits : __float_as_uint(v));
+}
+
 __device__ inline float bf16_to_f32(uint16_t u) { return __uint_as_float(uint32_t(u) << 16); }
 
 __device__ inline float half_lo(uint32_t w) {
@@ -139,59 +163,9 @@ __device__ inline void put_tagged(u64* p, uint32_t epoch, uint32_t payload) {
 }
 __device__ inline void put_tagged_f(u64* p, uint32_t epoch, float v) { put_tagged(p, epoch, __float_as_uint(v)); }
 
-// Payload of *p once its tag equals epoch; a timeout sets a status bit.
-__device__ inline uint32_t get_tagged(const u64* p, uint32_t epoch, WsHeader* h) {
-  u64 w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  uint32_t spins = 0;
-  while (uint32_t(w >> 32) != epoch) {
-    __builtin_amdgcn_s_sleep(1);
-    if (++spins > kSpinLimit) {
-      __hip_atomic_fetch_or(&h->status, kStatusWaitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      break;
-    }
-    w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  return uint32_t(w);
-}
-__device__ inline float get_tagged_f(const u64* p, uint32_t epoch, WsHeader* h) {
-  return __uint_as_float(get_tagged(p, epoch, h));
-}
-
-// One relaxed load; pair with settle() so a batch of loads is in flight at once.
+// One relaxed load; pair with a settle so a batch of loads is in flight at once.
 __device__ inline u64 peek(const u64* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Payload of a peeked word, spinning on *p only if the peek was stale.
-__device__ inline float settle_f(u64 w, const u64* p, uint32_t epoch, WsHeader* h) {
-  if (uint32_t(w >> 32) == epoch) return __uint_as_float(uint32_t(w));
-  return get_tagged_f(p, epoch, h);
-}
-__device__ inline uint32_t settle_u(u64 w, const u64* p, uint32_t epoch, WsHeader* h) {
-  if (uint32_t(w >> 32) == epoch) return uint32_t(w);
-  return get_tagged(p, epoch, h);
-}
-
-// Bring every peeked word w[k] with use[k] set up to the current epoch,
-// re-reading all stale ones together (one round trip per retry rather than
-// one per word). Bounded like get_tagged.
-template <int N>
-__device__ inline void settle_all(u64 (&w)[N], const u64* const (&p)[N], const bool (&use)[N], uint32_t epoch,
-                                  WsHeader* h) {
-  uint32_t spins = 0;
-  while (true) {
-    bool stale = false;
-#pragma unroll
-    for (int k = 0; k < N; ++k) stale |= use[k] && uint32_t(w[k] >> 32) != epoch;
-    if (!stale) return;
-    __builtin_amdgcn_s_sleep(1);
-    if (++spins > kSpinLimit) {
-      __hip_atomic_fetch_or(&h->status, kStatusWaitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return;
-    }
-#pragma unroll
-    for (int k = 0; k < N; ++k)
-      if (use[k] && uint32_t(w[k] >> 32) != epoch) w[k] = peek(p[k]);
-  }
 }
 
 // Two adjacent tagged words read by one 16-byte buffer load with the same
@@ -210,12 +184,16 @@ __device__ inline u32x4 peek2(__amdgpu_buffer_rsrc_t r, int off) {
 }
 __device__ inline bool stale2(const u32x4& v, uint32_t epoch) { return v.y != epoch || v.w != epoch; }
 
-// settle_all for M peeked pairs of words (16-byte loads at byte offsets
-// off[] of r) plus N single words.
+// Bring M peeked pairs of words (16-byte loads at byte offsets off[] of r)
+// plus N single words up to the current epoch, re-reading all stale ones
+// together (one round trip per retry rather than one per word). Bounded:
+// after `limit` retries the wait gives up, sets the sticky status bit and
+// returns true (the caller then publishes and writes NaN instead of values
+// that depended on the words).
 template <int M, int N>
-__device__ inline void settle_mixed(u32x4 (&v)[M], const bool (&use_v)[M], __amdgpu_buffer_rsrc_t r,
+__device__ inline bool settle_mixed(u32x4 (&v)[M], const bool (&use_v)[M], __amdgpu_buffer_rsrc_t r,
                                     const int (&off)[M], u64 (&w)[N], const u64* const (&p)[N], const bool (&use)[N],
-                                    uint32_t epoch, WsHeader* h) {
+                                    uint32_t epoch, WsHeader* h, uint32_t limit) {
   uint32_t spins = 0;
   while (true) {
     bool stale = false;
@@ -223,11 +201,11 @@ __device__ inline void settle_mixed(u32x4 (&v)[M], const bool (&use_v)[M], __amd
     for (int k = 0; k < M; ++k) stale |= use_v[k] && stale2(v[k], epoch);
 #pragma unroll
     for (int k = 0; k < N; ++k) stale |= use[k] && uint32_t(w[k] >> 32) != epoch;
-    if (!stale) return;
+    if (!stale) return false;
     __builtin_amdgcn_s_sleep(1);
-    if (++spins > kSpinLimit) {
+    if (++spins > limit) {
       __hip_atomic_fetch_or(&h->status, kStatusWaitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return;
+      return true;
     }
 #pragma unroll
     for (int k = 0; k < M; ++k)
@@ -243,6 +221,35 @@ __device__ inline void online_add(float& m, float& l, float s) {
   if (s == -INFINITY) return;
   if (s > m) { l = l * ex2(m - s) + 1.f; m = s; }
   else l += ex2(s - m);
+}
+
+// The same update with N more scores at once and no branch: the new maximum
+// first, then the old sum rescaled to it plus the new terms (-inf scores add
+// 0; while every score so far is -inf the reference is 0 and the sum stays 0).
+template <int N>
+__device__ inline void batch_stats(float& m, float& l, const float (&s)[N]) {
+  float mx = m;
+#pragma unroll
+  for (int k = 0; k < N; ++k) mx = fmaxf(mx, s[k]);
+  const float ref = mx == -INFINITY ? 0.f : mx;
+  float acc = l * ex2(m - ref);
+#pragma unroll
+  for (int k = 0; k < N; ++k) acc += ex2(s[k] - ref);
+  m = mx;
+  l = acc;
+}
+
+// The pair table: 64 words in LDS, read with one ds_read_b32 per key (the
+// byte address is 4 * key), or held one entry per lane and read with
+// ds_bpermute.
+constexpr bool kLdsTable = true;
+struct Lut {
+  uint32_t entry;                                  // this lane's entry (ds_bpermute form)
+  const uint32_t* tab;                             // the table in LDS
+};
+__device__ inline uint32_t lut_pair(const Lut& L, uint32_t addr) {
+  if constexpr (kLdsTable) return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(L.tab) + addr);
+  else return uint32_t(__builtin_amdgcn_ds_bpermute(int(addr), int(L.entry)));
 }
 
 // ---------------------------------------------------------------- format traits
@@ -292,7 +299,7 @@ template <> struct Traits<KVQ_Q4_0> {
     return r;
   }
   // one dword = 8 nibbles -> fp16 (16 + c), vector order elements 0,4,1,5,2,6,3,7
-  __device__ static half8 deq(const Raw& r, int bb, uint32_t) {
+  __device__ static half8 deq(const Raw& r, int bb, const Lut&) {
     const uint32_t x = r.c[bb];
     uint4 u;
     u.x = ((x << 6) & 0x03C003C0u) | 0x4C004C00u;
@@ -313,7 +320,7 @@ template <> struct Traits<KVQ_Q4_0> {
     v.sc = *reinterpret_cast<const uint16_t*>(srow + 2 * (lane >> 4));
     return v;
   }
-  __device__ static void vdeq(const VRaw& r, uint32_t, float& v0, float& v1) {
+  __device__ static void vdeq(const VRaw& r, const Lut&, float& v0, float& v1) {
     const float d = float(__builtin_bit_cast(_Float16, uint16_t(r.sc)));
     v0 = float(int(r.code & 15u) - 8) * d;
     v1 = float(int(r.code >> 4) - 8) * d;
@@ -352,7 +359,7 @@ template <> struct Traits<KVQ_Q8_0> {
     r.s = s;
     return r;
   }
-  __device__ static half8 deq(const Raw& r, int bb, uint32_t) {
+  __device__ static half8 deq(const Raw& r, int bb, const Lut&) {
     const uint32_t x0 = r.c[bb].x ^ 0x80808080u, x1 = r.c[bb].y ^ 0x80808080u;
     uint4 u;
     u.x = __builtin_amdgcn_perm(0x64646464u, x0, 0x04010400u);
@@ -372,7 +379,7 @@ template <> struct Traits<KVQ_Q8_0> {
     v.sc = *reinterpret_cast<const uint16_t*>(srow + 2 * (lane >> 4));
     return v;
   }
-  __device__ static void vdeq(const VRaw& r, uint32_t, float& v0, float& v1) {
+  __device__ static void vdeq(const VRaw& r, const Lut&, float& v0, float& v1) {
     const float d = float(__builtin_bit_cast(_Float16, uint16_t(r.sc)));
     v0 = float(int(int8_t(r.code & 0xFFu))) * d;
     v1 = float(int(int8_t(r.code >> 8))) * d;
@@ -392,10 +399,11 @@ constexpr uint16_t kLut3Bits[4] = {0x33D8, 0x3A0C, 0x3D60, 0x404E};
 __device__ inline uint32_t lut3_code_bits(uint32_t c) {
   return ((c & 4u) << 13) | kLut3Bits[c & 3u];
 }
-// this lane's entry of the pair table: key = c0 | c1 << 3 -> (value c0, value c1)
-__device__ inline uint32_t lut3_pair_entry(int lane) {
-  return lut3_code_bits(uint32_t(lane) & 7u) | (lut3_code_bits(uint32_t(lane) >> 3) << 16);
+// entry k of the pair table: key k = c0 | c1 << 3 -> (value c0, value c1)
+__device__ inline uint32_t lut3_pair_entry(int k) {
+  return lut3_code_bits(uint32_t(k) & 7u) | (lut3_code_bits(uint32_t(k) >> 3) << 16);
 }
+
 
 template <> struct Traits<KVQ_LUT3> {
   static constexpr int CB = 48, SB = 2;
@@ -422,12 +430,12 @@ template <> struct Traits<KVQ_LUT3> {
     const uint32_t x = (o <= 26) ? (r.c[w] >> o) : __builtin_amdgcn_alignbit(r.c[w + 1], r.c[w], o);
     return (x << 2) & 0xFCu;
   }
-  __device__ static half8 deq(const Raw& r, int bb, uint32_t table) {
+  __device__ static half8 deq(const Raw& r, int bb, const Lut& L) {
     uint4 u;
-    u.x = uint32_t(__builtin_amdgcn_ds_bpermute(int(key_addr(r, 24 * bb + 0)), int(table)));
-    u.y = uint32_t(__builtin_amdgcn_ds_bpermute(int(key_addr(r, 24 * bb + 6)), int(table)));
-    u.z = uint32_t(__builtin_amdgcn_ds_bpermute(int(key_addr(r, 24 * bb + 12)), int(table)));
-    u.w = uint32_t(__builtin_amdgcn_ds_bpermute(int(key_addr(r, 24 * bb + 18)), int(table)));
+    u.x = lut_pair(L, key_addr(r, 24 * bb + 0));
+    u.y = lut_pair(L, key_addr(r, 24 * bb + 6));
+    u.z = lut_pair(L, key_addr(r, 24 * bb + 12));
+    u.w = lut_pair(L, key_addr(r, 24 * bb + 18));
     return __builtin_bit_cast(half8, u);
   }
   __device__ static float scale(const Raw& r, int) { return half_lo(r.s); }
@@ -442,11 +450,11 @@ template <> struct Traits<KVQ_LUT3> {
     v.sc = *reinterpret_cast<const uint16_t*>(srow);
     return v;
   }
-  __device__ static void vdeq(const VRaw& r, uint32_t table, float& v0, float& v1) {
+  __device__ static void vdeq(const VRaw& r, const Lut& L, float& v0, float& v1) {
     const int lane = __lane_id();
     const int o = (6 * lane) & 31;
     const uint32_t x = __builtin_amdgcn_alignbit(r.hi, r.lo, o);
-    const uint32_t pair = uint32_t(__builtin_amdgcn_ds_bpermute(int((x << 2) & 0xFCu), int(table)));
+    const uint32_t pair = lut_pair(L, (x << 2) & 0xFCu);
     const float nu = float(__builtin_bit_cast(_Float16, uint16_t(r.sc))) * kRowMul;
     v0 = half_lo(pair) * nu;
     v1 = half_hi(pair) * nu;
@@ -474,10 +482,15 @@ __device__ inline float sum_pairs32(float v) {
 // A wave with many value rows sums p * v with v_mfma_f32_16x16x16_f16, 16
 // rows per batch: out[h][d] = sum_r (p[h][r] * s[r][d]) * c[r][d] with s the
 // row's scale for dim d and c its code value (q4_0: c - 8, exact in fp16).
-// A rows 0..7 hold the fp16 high parts of p * s for heads 0..7, rows 8..15
-// the low parts (p * s minus the high part), so the two rows of a head add
-// up to p * s within 2^-22 relative; the products with the exact codes are
-// formed and summed in fp32. Tile t (0..7) takes the dims n + 16t (n the
+// A rows 0..7 hold the fp16 high parts of x = 2^sh * p * s for heads 0..7,
+// rows 8..15 the low parts (x minus the high part); the products with the
+// exact codes are formed and summed in fp32. The power of two 2^sh puts the
+// largest x of the wave's rows so far in [2^14, 2^15), far inside the fp16
+// normal range: a term within 2^18 of that largest one is represented within
+// 2^-22 relative, a smaller one within 2^-25 of the fp16 unit of its batch
+// (weights near 1/n at long contexts would otherwise fall among fp16
+// subnormals and lose their low parts). When a batch holds a larger x than
+// any before, the accumulators are rescaled by the exact power of two. Tile t (0..7) takes the dims n + 16t (n the
 // MFMA column), all inside scale block t / 2, so each tile has one A operand.
 // A row's 64 code bytes are staged transposed as an 8 x 8 byte matrix,
 // T[8j + a] = R[8a + j], so that the lane of column n finds the nibbles of
@@ -503,7 +516,7 @@ template <> struct VMfma<KVQ_Q4_0> {
   }
   __device__ static int dim(int n, int t) { return n + 16 * t; }
   // B operands of the 8 tiles for rows 4g .. 4g + 3 of the batch (column n)
-  __device__ static void b_ops(const uint8_t* vst, int g, int n, uint32_t, half4 (&B)[8]) {
+  __device__ static void b_ops(const uint8_t* vst, int g, int n, const Lut&, half4 (&B)[8]) {
     const int sh = 4 * (n & 1);
     uint32_t lo[4], hi[4];
 #pragma unroll
@@ -544,7 +557,7 @@ template <> struct VMfma<KVQ_LUT3> {
     *reinterpret_cast<uint4*>(lrow + 16 * ch) = cv;
   }
   __device__ static int dim(int n, int t) { return 8 * n + t; }
-  __device__ static void b_ops(const uint8_t* vst, int g, int n, uint32_t table, half4 (&B)[8]) {
+  __device__ static void b_ops(const uint8_t* vst, int g, int n, const Lut& L, half4 (&B)[8]) {
     const int w = (24 * n) >> 5, o = (24 * n) & 31;
     uint32_t pr[4][4];                               // [row][dim pair] value pairs
 #pragma unroll
@@ -554,7 +567,7 @@ template <> struct VMfma<KVQ_LUT3> {
       const uint32_t bits = __builtin_amdgcn_alignbit(rw[w + 1], rw[w], o);
 #pragma unroll
       for (int tp = 0; tp < 4; ++tp)
-        pr[i][tp] = uint32_t(__builtin_amdgcn_ds_bpermute(int(((bits >> (6 * tp)) << 2) & 0xFCu), int(table)));
+        pr[i][tp] = lut_pair(L, ((bits >> (6 * tp)) << 2) & 0xFCu);
     }
 #pragma unroll
     for (int tp = 0; tp < 4; ++tp) {
@@ -623,7 +636,8 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   int* wrows = wcount + kWaves;                                   // [kWaves] rows fetched
   float* wmass = reinterpret_cast<float*>(wrows + kWaves);        // [kWaves][G]
   float2* wml = reinterpret_cast<float2*>(wmass + kWaves * G);    // [kWaves][8] per-wave (max, sum)
-  int* wproc = reinterpret_cast<int*>(wml + kWaves * 8);          // [kWaves + 4] value rows each wave summed
+  int* wproc = reinterpret_cast<int*>(wml + kWaves * 8);          // [kWaves] value rows each wave summed
+  int* wto = wproc + kWaves;                                      // [4]: [0] a wait of this workgroup gave up
   unsigned long long* umask = reinterpret_cast<unsigned long long*>(wproc + kWaves + 4);  // [P/64] union keep bits
   // per-wave lists of the kept rows a wave fetches: [kWaves][32 * ceil(P/64 / (kWaves/2))]
   uint16_t* rowlist = reinterpret_cast<uint16_t*>(umask + (P / kChunk));
@@ -651,7 +665,9 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
 
   const int n16 = lane & 15;     // MFMA column (position within a tile)
   const int kg = lane >> 4;      // lane group
-  const uint32_t table = (FMT == KVQ_LUT3 || FMT == KVQ_LUT3_WHT) ? lut3_pair_entry(lane) : 0u;
+  constexpr bool kLut3 = FMT == KVQ_LUT3 || FMT == KVQ_LUT3_WHT;
+  __shared__ uint32_t lut3_tab[kLut3 ? 64 : 1];      // LUT3 pair table (written in the set-up below)
+  const Lut table{kLut3 ? lut3_pair_entry(lane) : 0u, lut3_tab};
   // issue the first K tiles before the q set-up so their latency overlaps it
   const int ntiles = P / 16;
   constexpr int U = 4;
@@ -660,18 +676,17 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   // requested before the current one is scored) when two fit in registers
   constexpr bool kDouble = sizeof(Loaded) <= 24;
   Loaded rawA[U], rawB[kDouble ? U : 1];
+  // Every lane loads unconditionally: a position past the context (or a tile
+  // past the split) reads row ctx - 1 instead, and its score is masked to
+  // -inf. No load sits behind a branch, so the next batch's loads are issued
+  // before the current batch is waited for.
   auto load_tiles = [&](Loaded* raw, int t0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = t0 + u * kWaves;
-      const int r = pos0 + t * 16 + n16;
-      if (t < ntiles && r < ctx) {
-        const int64_t row = row0 + r;
-        if constexpr (T::kStaged) raw[u] = T::load16(a.kc + row * T::CB, a.ks + row * T::SB, kg);
-        else raw[u] = T::load(a.kc + row * T::CB, a.ks + row * T::SB, kg);
-      } else {
-        raw[u] = Loaded{};
-      }
+      const int64_t row = row0 + min(pos0 + t * 16 + n16, ctx - 1);
+      if constexpr (T::kStaged) raw[u] = T::load16(a.kc + row * T::CB, a.ks + row * T::SB, kg);
+      else raw[u] = T::load(a.kc + row * T::CB, a.ks + row * T::SB, kg);
     }
   };
   // the operand layout of a loaded tile (through this wave's LDS strip when
@@ -699,6 +714,8 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     a.hdr->v_row_bytes = T::CB + T::SB;
   }
   for (int c = tid; c < P / kChunk; c += kThreads) umask[c] = 0ull;
+  if (tid == 0) wto[0] = 0;
+  if (kLut3 && tid < 64) lut3_tab[tid] = lut3_pair_entry(tid);
   // q of this group: per-head max |q| -> power-of-two prescale, then fp16 hi/lo rows
   float qv[4];
   {
@@ -793,9 +810,13 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   stamp(a, 1);
 
   // ---------------------------------------------------------------- phase 1: scores
-  // Scores go to LDS; each lane keeps an online (max, sum exp2) of its two heads.
+  // Scores go to LDS; each lane keeps a running (max, sum exp2) of its two
+  // heads, updated once per batch of tiles without branches.
   float m0 = -INFINITY, l0 = 0.f, m1 = -INFINITY, l1 = 0.f;
   auto score_batch = [&](const Loaded* raw, int t0) {
+    float sa[U], sb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) sa[u] = sb[u] = -INFINITY;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = t0 + u * kWaves;
@@ -823,18 +844,24 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
       const bool valid = (pos0 + lp) < ctx;
       const float s0 = valid ? (acc[0] + acc[1]) * hs0 : -INFINITY;
       const float s1 = valid ? (acc[2] + acc[3]) * hs1 : -INFINITY;
-      if (j0 < G) { sc[j0 * P + lp] = s0; online_add(m0, l0, s0); }
-      if (j1 < G) { sc[j1 * P + lp] = s1; online_add(m1, l1, s1); }
+      if (j0 < G) sc[j0 * P + lp] = s0;
+      if (j1 < G) sc[j1 * P + lp] = s1;
+      sa[u] = s0;
+      sb[u] = s1;
     }
+    batch_stats<U>(m0, l0, sa);
+    batch_stats<U>(m1, l1, sb);
   };
   constexpr int STRIDE = kWaves * U;                  // tiles between a wave's batches
   if constexpr (kDouble) {
+    // the loads of the next batch are issued before the current batch is
+    // scored, unconditionally (past the split they re-read row ctx - 1, an
+    // L2 hit), so no load depends on a branch and two batches stay in flight
     for (int t0 = wave; t0 < ntiles; t0 += 2 * STRIDE) {
-      if (t0 + STRIDE < ntiles) load_tiles(rawB, t0 + STRIDE);
+      load_tiles(rawB, t0 + STRIDE);
       score_batch(rawA, t0);
-      if (t0 + STRIDE >= ntiles) break;
-      if (t0 + 2 * STRIDE < ntiles) load_tiles(rawA, t0 + 2 * STRIDE);
-      score_batch(rawB, t0 + STRIDE);
+      load_tiles(rawA, t0 + 2 * STRIDE);
+      score_batch(rawB, t0 + STRIDE);               // tiles past the split are skipped inside
     }
   } else {
     for (int t0 = wave; t0 < ntiles; t0 += STRIDE) {
@@ -857,7 +884,9 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     const int j = tid >> 4, w = tid & 15;
     float2 acc = (j < G) ? wml[w * 8 + j] : make_float2(-INFINITY, 0.f);
     acc = merge_row16(acc);
-    if (w == 0 && j < G) {
+    // (test aid: split 0 of the first group withholds its statistics, so
+    // every workgroup of that group waits in vain)
+    if (w == 0 && j < G && !(a.withhold && bg == 0 && split == 0)) {
       u64* dst = a.split_ml + ((int64_t(bg) * a.S + split) * G + j) * 2;
       put_tagged_f(dst, epoch, acc.x);
       put_tagged_f(dst + 1, epoch, acc.y);
@@ -892,7 +921,7 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     u64 none[1] = {0ull};
     const u64* const nop[1] = {a.split_ml};
     const bool nouse[1] = {false};
-    settle_mixed(v, use, r, off, none, nop, nouse, epoch, a.hdr);
+    if (settle_mixed(v, use, r, off, none, nop, nouse, epoch, a.hdr, a.spin_limit)) wto[0] = 1;
     float2 acc = make_float2(-INFINITY, 0.f);
 #pragma unroll
     for (int k = 0; k < 2; ++k)
@@ -945,54 +974,81 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
 
   // ---------------------------------------------------------------- phase 3: sparse V pass
   // Waves 2c' and 2c'+1 share the 64-position chunks c = c' (mod kWaves/2).
-  // (a) Each computes the normalized weights and keep bits of half of the
-  //     group's heads and ORs the union (a value row is fetched iff some
-  //     head keeps it) into umask[c].
+  // (a) Each decides the keep bits of half of the group's heads and ORs the
+  //     union (a value row is fetched iff some head keeps it) into umask[c].
+  //     A head keeps a position iff its normalized weight 2^(s - LSE) reaches
+  //     the threshold, decided on the score as s >= LSE + log2(threshold)
+  //     (the two differ only for weights within float32 rounding of the
+  //     threshold); weights are formed only in chunks that keep a row.
   // (b) After one barrier each takes the kept rows of its chunks of even
   //     (first wave of the pair) or odd (second) rank and fetches only those.
   constexpr int HALF = G > 1 ? G / 2 : 1;
   const int pair = wave >> 1, side = wave & 1;
   const int jb = G > 1 ? side * HALF : 0;
   const bool do_p = G > 1 || side == 0;
-  const bool tau_normal = tau >= 1.17549435e-38f;    // FLT_MIN
+  // the hardware exp flushes results below 2^-126: exact for weights that a
+  // normal threshold keeps, and for threshold 0 (such weights add < 2^-126);
+  // a subnormal threshold needs the full-range exp2f
+  const bool hw_exp = tau >= 1.17549435e-38f || tau == 0.f;
+  const float ltau = tau > 0.f ? log2f(tau) : -INFINITY;
   float o0[G], o1[G], mass[G];
 #pragma unroll
   for (int j = 0; j < G; ++j) { o0[j] = 0.f; o1[j] = 0.f; mass[j] = 0.f; }
   int kept_cnt = 0;
-  float lsej[HALF];
+  float lsej[HALF], thr[HALF];
 #pragma unroll
-  for (int jj = 0; jj < HALF; ++jj) lsej[jj] = lse[jb + jj];
+  for (int jj = 0; jj < HALF; ++jj) {
+    lsej[jj] = lse[jb + jj];
+    thr[jj] = lsej[jj] + ltau;
+  }
   const int nchunks = P / kChunk;
   if (do_p) {
+    // the scores of the wave's next chunk are read while this one is decided
+    float svn[HALF];
+#pragma unroll
+    for (int jj = 0; jj < HALF; ++jj) svn[jj] = pair < nchunks ? sc[(jb + jj) * P + pair * kChunk + lane] : 0.f;
     for (int c = pair; c < nchunks; c += kWaves / 2) {
       const int lp = c * kChunk + lane;
       const bool valid = pos0 + lp < ctx;
-      bool any = false;
+      float sv[HALF];
+#pragma unroll
+      for (int jj = 0; jj < HALF; ++jj) sv[jj] = svn[jj];
+      const int cn = c + kWaves / 2;
+#pragma unroll
+      for (int jj = 0; jj < HALF; ++jj) svn[jj] = cn < nchunks ? sc[(jb + jj) * P + cn * kChunk + lane] : 0.f;
+      unsigned long long bal[HALF], uni = 0ull;
 #pragma unroll
       for (int jj = 0; jj < HALF; ++jj) {
-        const int j = jb + jj;
-        // the hardware exp flushes results below 2^-126; any normal threshold
-        // decides above that, so it gives the same keep bits and weights
-        const float sv = sc[j * P + lp];
-        const float x = sv - (RUN ? rl[j * nch + c] : lsej[jj]);
-        const float p = valid ? (tau_normal ? ex2(x) : exp2f(x)) : 0.f;
-        const bool keep = valid && (p >= tau);
-        // kept weight replaces the score in place (single-pass rule: relative
-        // to the split's max, rescaled when the partial is published)
-        sc[j * P + lp] = keep ? (RUN ? ex2(sv - lsej[jj]) : p) : 0.f;
-        any |= keep;
-        const unsigned long long bal = __ballot(keep);
-        kept_cnt += __popcll(bal);
-        if (a.mask_out && lane < 2) {
-          const int word = (pos0 + c * kChunk) / 32 + lane;
-          if (word < a.mask_words) {
-            const int h = g * G + j;
-            a.mask_out[(int64_t(b) * a.Hq + h) * a.mask_words + word] = uint32_t(bal >> (32 * lane));
-          }
-        }
+        // single-pass rule: the reference is the running LSE of the block
+        const float th = RUN ? rl[(jb + jj) * nch + c] + ltau : thr[jj];
+        bal[jj] = __ballot(valid && sv[jj] >= th);
+        uni |= bal[jj];
+        kept_cnt += __popcll(bal[jj]);
       }
-      const unsigned long long um = __ballot(any);
-      if (lane == 0 && um) atomicOr(&umask[c], um);
+      // kept weights replace the scores in place; a head that skips a row
+      // another head keeps leaves 0 there, and so does every head in a chunk
+      // where this wave's heads keep nothing (the other half of the group may
+      // keep rows of it). Single-pass rule: relative to the split's max,
+      // rescaled when the partial is published.
+      if (uni) {                                   // uniform
+#pragma unroll
+        for (int jj = 0; jj < HALF; ++jj) {
+          const bool keep = (bal[jj] >> lane) & 1ull;
+          const float x = sv[jj] - lsej[jj];
+          sc[(jb + jj) * P + lp] = keep ? (hw_exp ? ex2(x) : exp2f(x)) : 0.f;
+        }
+        if (lane == 0) atomicOr(&umask[c], uni);
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < HALF; ++jj) sc[(jb + jj) * P + lp] = 0.f;
+      }
+      if (a.mask_out && lane < 2) {
+        const int word = (pos0 + c * kChunk) / 32 + lane;
+        if (word < a.mask_words)
+#pragma unroll
+          for (int jj = 0; jj < HALF; ++jj)
+            a.mask_out[(int64_t(b) * a.Hq + g * G + jb + jj) * a.mask_words + word] = uint32_t(bal[jj] >> (32 * lane));
+      }
     }
   }
   stamp(a, 7);
@@ -1013,6 +1069,10 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   const bool use_mfma = VM::kOn && nmine >= 8;
   floatx4 vacc[8];
   float vmass = 0.f;                                  // lanes of high-part rows: their head's weights
+  // exponent e with every x = p * s of the wave's rows so far below 2^e; the
+  // A operands hold x * 2^(15 - e) (kNoExp: no nonzero x yet)
+  constexpr int kNoExp = -100000;
+  int vexp = kNoExp;
 #pragma unroll
   for (int t = 0; t < 8; ++t) vacc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
   {
@@ -1114,14 +1174,37 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
             w[i] = (okr[i] && hj < G) ? sc[hj * P + mylist[okr[i] ? kk : k]] : 0.f;
             if (!lo_part) vmass += w[i];
           }
+          float x[VM::kBlocks][4];
+          float xm = 0.f;
+#pragma unroll
+          for (int b = 0; b < VM::kBlocks; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              x[b][i] = okr[i] ? w[i] * VM::scale(vst + (4 * g4 + i) * T::PITCH, b) : 0.f;
+              xm = fmaxf(xm, fabsf(x[b][i]));
+            }
+          // wave-uniform exponent of the batch's largest term (xm < 2^e)
+          xm = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, max_wave(xm))));
+          if (xm > 0.f) {
+            const int e = __builtin_amdgcn_frexp_expf(xm);
+            if (e > vexp) {                          // rescale the sums to the new exponent (exact)
+              const float f = vexp == kNoExp ? 0.f : __builtin_ldexpf(1.f, vexp - e);
+#pragma unroll
+              for (int t = 0; t < 8; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) vacc[t][i] *= f;
+              vexp = e;
+            }
+          }
+          const int sh = 15 - vexp;
 #pragma unroll
           for (int b = 0; b < VM::kBlocks; ++b) {
             half4 A;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const float x = okr[i] ? w[i] * VM::scale(vst + (4 * g4 + i) * T::PITCH, b) : 0.f;
-              const _Float16 h = _Float16(x);
-              A[i] = lo_part ? _Float16(x - float(h)) : h;
+              const float xs = __builtin_ldexpf(x[b][i], sh);    // |xs| < 2^15
+              const _Float16 h = _Float16(xs);
+              A[i] = lo_part ? _Float16(xs - float(h)) : h;
             }
 #pragma unroll
             for (int t = 0; t < 8; ++t)
@@ -1154,10 +1237,12 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     // and low part rows are on lanes l and l + 32
     vmass = sum_pairs16(vmass);
     vmass = sum_pairs32(vmass);
+    // undo the operand scale 2^(15 - vexp) (a power of two: exact)
+    const float unscale = vexp == kNoExp ? 0.f : __builtin_ldexpf(1.f, vexp - 15);
 #pragma unroll
     for (int t = 0; t < 8; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vacc[t][i] = sum_pairs32(vacc[t][i]);
+      for (int i = 0; i < 4; ++i) vacc[t][i] = sum_pairs32(vacc[t][i]) * unscale;
   }
   stamp(a, 9);
 
@@ -1191,9 +1276,13 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     if (tid < G) fac[tid] = exp2f(lse[tid] - fac[tid]);
     __syncthreads();
   }
+  // a wait of this workgroup gave up (its statistics and weights are not the
+  // call's): publish NaN, so every sum that uses them is NaN as well
+  const bool bad = wto[0] != 0;
   if (nact == 0) {                                    // uniform: nothing kept, publish zeros
-    for (int i = tid; i < G * 128; i += kThreads) put_tagged_f(a.partial + pbase * G * 128 + i, epoch, 0.f);
-    if (tid < G) put_tagged_f(a.pmass + pbase * G + tid, epoch, 0.f);
+    for (int i = tid; i < G * 128; i += kThreads)
+      put_tagged_f(a.partial + pbase * G * 128 + i, epoch, poison_if(bad, 0.f));
+    if (tid < G) put_tagged_f(a.pmass + pbase * G + tid, epoch, poison_if(bad, 0.f));
   } else {
     // the partials of the waves that summed rows meet in LDS and are added in
     // ascending wave order; every thread publishes one word
@@ -1232,15 +1321,15 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
       if (wave < G) {
         float v0 = rot[wave * 128 + lane], v1 = rot[wave * 128 + 64 + lane];
         wht_wave(lane, v0, v1);
-        put_tagged_f(a.partial + pbase * G * 128 + wave * 128 + lane, epoch, v0);
-        put_tagged_f(a.partial + pbase * G * 128 + wave * 128 + 64 + lane, epoch, v1);
+        put_tagged_f(a.partial + pbase * G * 128 + wave * 128 + lane, epoch, poison_if(bad, v0));
+        put_tagged_f(a.partial + pbase * G * 128 + wave * 128 + 64 + lane, epoch, poison_if(bad, v1));
       }
     } else {
       for (int i = tid; i < G * 128; i += kThreads) {
         float s = 0.f;
         for (int k = 0; k < nact; ++k) s += red[k * G * 128 + i];
         if constexpr (RUN) s *= fac[i >> 7];
-        put_tagged_f(a.partial + pbase * G * 128 + i, epoch, s);
+        put_tagged_f(a.partial + pbase * G * 128 + i, epoch, poison_if(bad, s));
       }
     }
     if (tid < G) {
@@ -1248,7 +1337,7 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
       for (int w = 0; w < kWaves; ++w)
         if ((act >> w) & 1u) s += wmass[w * G + tid];
       if constexpr (RUN) s *= fac[tid];
-      put_tagged_f(a.pmass + pbase * G + tid, epoch, s);
+      put_tagged_f(a.pmass + pbase * G + tid, epoch, poison_if(bad, s));
     }
   }
   if (tid == 0) put_tagged(a.flags + pbase, epoch, (uint32_t(wg_rows) << 18) | uint32_t(wg_kept));
@@ -1305,7 +1394,7 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     uint32_t prev = 0;
     const bool counts = master && tid == 0;
     if (counts) prev = __hip_atomic_fetch_add(&a.hdr->groups_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    settle_mixed(pw, puse, rp, poff, w, src, use, epoch, a.hdr);
+    if (settle_mixed(pw, puse, rp, poff, w, src, use, epoch, a.hdr, a.spin_limit)) wto[0] = 1;
     if (counts && prev == uint32_t(a.B * a.Hkv) - 1) {
       __hip_atomic_store(&a.hdr->groups_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&a.hdr->epoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1321,6 +1410,7 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
       if (use[2 + k]) fl[tid + k * kThreads] = uint32_t(w[2 + k]);
     }
     __syncthreads();
+    const bool mbad = wto[0] != 0;                   // a wait gave up: the slice is NaN
     // one wave per sum: lane l adds splits l, l+64, ... in order, then a
     // fixed tree over the lanes (deterministic)
     if (S <= 16) {                                   // few splits: one thread per sum, in split order
@@ -1328,6 +1418,7 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
         const float* src = job < ne ? pv + job * S : pm + (job - ne) * S;
         float v = 0.f;
         for (int sp = 0; sp < S; ++sp) v += src[sp];
+        v = poison_if(mbad, v);
         if (job < ne) a.out[int64_t(bg) * NE + e0 + job] = v;
         else a.kept_mass[int64_t(bg) * G + split + (job - ne) * S] = v;
       }
@@ -1336,7 +1427,7 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
         const float* src = job < ne ? pv + job * S : pm + (job - ne) * S;
         float v = 0.f;
         for (int sp = lane; sp < S; sp += 64) v += src[sp];
-        v = sum_wave(v);
+        v = poison_if(mbad, sum_wave(v));
         if (lane == 0) {
           if (job < ne) a.out[int64_t(bg) * NE + e0 + job] = v;
           else a.kept_mass[int64_t(bg) * G + split + (job - ne) * S] = v;

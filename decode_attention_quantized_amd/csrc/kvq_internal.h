@@ -13,6 +13,12 @@ constexpr int kChunk = 64;              // positions per wave chunk (one ballot 
 // Device fault bits reported through WsHeader::status.
 constexpr uint32_t kStatusWaitTimeout = 1u;   // a bounded wait gave up
 
+// Retries of a bounded wait before it gives up (each retry sleeps briefly and
+// re-reads: about half a second in all), and the short limit of the test aid
+// that withholds one split's statistics.
+constexpr uint32_t kSpinLimit = 1u << 23;
+constexpr uint32_t kTestSpinLimit = 1u << 12;
+
 // Workspace header. The first 256 bytes of every workspace; the rest holds the
 // per-split statistics and partial outputs of the last call.
 struct WsHeader {
@@ -88,6 +94,8 @@ struct GqaArgs {
   float sigma_log2e;              // softmax scale times log2(e)
   float tau;                      // threshold on the normalized weight
   unsigned long long* times;      // optional [nwg][16] phase stamps
+  uint32_t spin_limit;            // retries of a bounded wait
+  int32_t withhold;               // test aid: split 0 of group 0 does not publish its statistics
 };
 
 // Arguments of the two MLA kernels.
@@ -112,11 +120,15 @@ struct MlaArgs {
   int32_t tpe;                    // 32-position tiles per tile-maximum entry of the scores kernel (1 or 2)
   int32_t scores_out;             // 1: kp holds every row's log2-domain scores (threshold 0, mla_out_dense)
   float* lseo;                    // [B][H] log2-domain LSE per head (written when scores_out)
+  uint32_t* mask_out;             // optional keep bits [B][H][mask_words]
+  int32_t mask_words;             // ceil(ctx / 32)
   int32_t B, Hq, ctx, cap;
   int32_t S, P;
   float sigma_log2e;
   float tau;
   unsigned long long* times;      // optional [nwg][16] phase stamps of mla_scores
+  uint32_t spin_limit;            // retries of a bounded wait
+  int32_t withhold;               // test aid: split 0 of sequence 0 does not publish its statistics
 };
 
 struct MlaLayout {

@@ -57,7 +57,6 @@ constexpr int NGROUPS = 5;      // scale groups: 4 x 128 + 1 x 64
 constexpr int ROW_LDS = 592;    // LDS pitch of a staged latent row: 37 x 16 bytes (odd), so the 16-byte
                                 // reads of 8 consecutive rows hit distinct bank groups
 constexpr int TILE = 32;        // positions per MFMA tile
-constexpr uint32_t kSpinLimit = 1u << 23;
 
 // LDS ring of staged tiles. A buffer holds 32 latent rows at ROW_LDS pitch
 // (37 slots of 16 bytes, the last one padding) followed by the 32 x 5 scales.
@@ -75,18 +74,36 @@ __device__ inline void put_tagged_f(u64* p, uint32_t epoch, float v) {
   __hip_atomic_store(p, (u64(epoch) << 32) | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ inline u64 peek(const u64* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-__device__ inline float settle_f(u64 w, const u64* p, uint32_t epoch, WsHeader* h) {
+// Payload of a peeked tagged word once its tag is the call's epoch. Bounded:
+// after `limit` retries the wait gives up, sets the sticky status bit and
+// sets `gave_up` (the caller then writes NaN instead of what depended on it).
+__device__ inline float settle_f(u64 w, const u64* p, uint32_t epoch, WsHeader* h, uint32_t limit, bool& gave_up) {
   uint32_t spins = 0;
   while (uint32_t(w >> 32) != epoch) {
     __builtin_amdgcn_s_sleep(1);
-    if (++spins > kSpinLimit) {
+    if (++spins > limit) {
       __hip_atomic_fetch_or(&h->status, kStatusWaitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      gave_up = true;
       break;
     }
     w = peek(p);
   }
   return __uint_as_float(uint32_t(w));
 }
+
+// The defined result of a value that depended on a wait that gave up. The
+// kernels are compiled without NaN semantics (their arithmetic never makes
+// one), so the NaN pattern is passed through an empty asm statement: the
+// compiler cannot see that it is a NaN and fold the selection away.
+constexpr uint32_t kNaNBits = 0x7FC00000u;
+__device__ inline float poison_if(bool bad, float v) {
+  uint32_t nan_bits = kNaNBits;
+  asm volatile("" : "+v"(nan_bits));
+  return __uint_as_float(bad ? nan_bits : __float_as_uint(v));
+}
+// A split whose statistics wait gave up publishes its kept-row count with
+// this bit set; the output kernels then write NaN for the whole sequence.
+constexpr uint32_t kCountPoison = 0x80000000u;
 
 __device__ inline float2 lse_merge(float2 x, float2 y) {
   const float M = fmaxf(x.x, y.x);
@@ -520,7 +537,9 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
     }
   }
   reduce32<false, 8>(l);
-  if (col == 0) {
+  // (test aid: split 0 of the first sequence withholds its statistics, so
+  // every workgroup of that sequence waits in vain)
+  if (col == 0 && !(a.withhold && b == 0 && split == 0)) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int h = hrow + 8 * (e >> 2) + (e & 3);
@@ -538,9 +557,11 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
   // heads, so a wave reads whole lines) and re-reading the stale ones of a
   // batch together; the four partial results of a head are merged in a fixed
   // order, so every workgroup of the sequence computes the same bits.
+  bool sbad;                                          // a wait of this workgroup gave up
   {
     const int h = tid % H, q = tid / H;               // NT = 4 * H
     float2 acc = make_float2(-INFINITY, 0.f);
+    bool gave_up = false;
     constexpr int SB = 8;                             // splits per batch of loads
     const __amdgpu_buffer_rsrc_t r =
         __builtin_amdgcn_make_buffer_rsrc(a.split_ml + int64_t(b) * a.S * H * 2, 0, a.S * H * 16, 0x00020000);
@@ -560,8 +581,9 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
 #pragma unroll
         for (int u = 0; u < SB; ++u) stale |= use[u] && (v[u][1] != epoch || v[u][3] != epoch);
         if (!stale) break;
-        if (spins > kSpinLimit) {
+        if (spins > a.spin_limit) {
           __hip_atomic_fetch_or(&a.hdr->status, kStatusWaitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          gave_up = true;
           break;
         }
         __builtin_amdgcn_s_sleep(1);
@@ -578,12 +600,12 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
     }
     float2* part = reinterpret_cast<float2*>(xbuf);   // [4][H]; the hand-over slots are idle here
     part[q * H + h] = acc;
-    __syncthreads();
+    sbad = __syncthreads_or(gave_up) != 0;
     if (q == 0) {
       const float2 r01 = lse_merge(part[h], part[H + h]);
       const float2 r23 = lse_merge(part[2 * H + h], part[3 * H + h]);
       const float2 rr = lse_merge(r01, r23);
-      lse[h] = rr.x + log2f(rr.y);
+      lse[h] = poison_if(sbad, rr.x + log2f(rr.y));
       if (a.scores_out && split == 0) a.lseo[int64_t(b) * H + h] = lse[h];
     }
     __syncthreads();
@@ -594,6 +616,14 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
     const int nv = min(P, ctx - pos0);
     const int64_t kb = int64_t(b) * a.S + split;
     for (int i = tid; i < nv; i += NT) a.kpos[kb * P + i] = pos0 + i;
+    if (a.mask_out) {                                  // every valid position is kept by every head
+      const int nt = (nv + TILE - 1) / TILE;
+      for (int i = tid; i < H * nt; i += NT) {
+        const int h = i / nt, u = i - h * nt;
+        const int left = nv - u * TILE;
+        a.mask_out[(int64_t(b) * H + h) * a.mask_words + pos0 / TILE + u] = left >= TILE ? ~0u : (1u << left) - 1u;
+      }
+    }
     if (tid == 0) {
       a.kcount[kb] = nv;
       a.kpairs[kb] = nv * H;
@@ -621,6 +651,16 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
     if (pos0 + u * a.tpe * TILE < ctx && tmax[h * NLT + u] >= lse[h] + log2tau - 0.01f) live[u] = 1;
   }
   __syncthreads();
+  if (a.mask_out) {
+    // tiles that are not re-scored keep no position: their words are zero
+    // (the re-scored tiles' words are written as their weights are formed)
+    const int nt = min(P, ctx - pos0 + TILE - 1) / TILE;   // tiles holding a valid position
+    for (int i = tid; i < H * nt; i += NT) {
+      const int h = i / nt, u = i - h * nt;
+      if (!live[u / a.tpe]) a.mask_out[(int64_t(b) * H + h) * a.mask_words + pos0 / TILE + u] = 0u;
+    }
+    __syncthreads();                                   // live[] is compacted in place below
+  }
   if (wave == 0) {
     int nl = 0;
     for (int u0 = 0; u0 < NLT; u0 += 64) {
@@ -682,6 +722,7 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
     float s[8];
     finish_scores(own, xbuf + ((k & 1) * NW + partner) * 128 + lane, pos0 + t * TILE + col < ctx, s);
     bool any = false;
+    uint32_t word = 0u;                               // keep bits of this lane's mask word (lanes 8i + j, j < 8)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float pe = exp2f(s[e] - lse[hrow + 8 * (e >> 2) + (e & 3)]);   // denormal-exact
@@ -689,6 +730,19 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
       p[e] = keep ? pe : 0.f;
       any |= keep;
       kept_pairs += keep ? 1 : 0;
+      if (a.mask_out) {
+        // columns 0..31 of head hrow + 8(e >> 2) + (e & 3) in the low half of
+        // the ballot, those of the head 4 above (kh = 1) in the high half
+        const unsigned long long bal = __ballot(keep);
+        if ((lane & 31) == e) word = kh ? uint32_t(bal >> 32) : uint32_t(bal);
+      }
+    }
+    // (the second tile of a 64-position entry can lie past the context: no word)
+    const int widx = (pos0 + t * TILE) / TILE;
+    if (a.mask_out && (lane & 31) < 8 && widx < a.mask_words) {
+      const int e = lane & 31;
+      const int h = hrow + 8 * (e >> 2) + (e & 3);
+      a.mask_out[(int64_t(b) * H + h) * a.mask_words + widx] = word;
     }
     if (any) atomicOr(&keepmask[(k & 1) * TILE + col], 1u);
   };
@@ -752,7 +806,7 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
   if (lane == 0) atomicAdd(&misc[2], kept_pairs);
   __syncthreads();
   if (tid == 0) {
-    a.kcount[kbase] = nkept;
+    a.kcount[kbase] = int32_t(uint32_t(nkept) | (sbad ? kCountPoison : 0u));
     a.kpairs[kbase] = misc[2];
   }
   stamp_mla(a, 4);
@@ -820,12 +874,15 @@ __global__ __launch_bounds__(256) void mla_out(MlaArgs a) {
 
   // kept rows per split: one batch of loads, then an exclusive prefix sum
   long long pairs_part = 0;
+  bool obad = false;                                  // a split of the sequence gave up a wait: NaN out
   {
     int c[OUT_MAX_S / 256];
 #pragma unroll
     for (int k = 0; k < OUT_MAX_S / 256; ++k) {
       const int sp = tid * (OUT_MAX_S / 256) + k;
       c[k] = sp < S ? a.kcount[int64_t(b) * S + sp] : 0;
+      obad |= (uint32_t(c[k]) & kCountPoison) != 0u;
+      c[k] &= int(~kCountPoison);
       if (sp < S) pairs_part += a.kpairs[int64_t(b) * S + sp];
     }
     int local = 0;
@@ -839,7 +896,7 @@ __global__ __launch_bounds__(256) void mla_out(MlaArgs a) {
       if (lane >= o) incl += y;
     }
     if (lane == 63) pre[OUT_MAX_S - 4 + wave] = incl;   // wave totals parked at the table's end
-    __syncthreads();
+    obad = __syncthreads_or(obad) != 0;
     int wbase = 0;
     for (int w = 0; w < wave; ++w) wbase += pre[OUT_MAX_S - 4 + w];
     const int total = pre[OUT_MAX_S - 4] + pre[OUT_MAX_S - 3] + pre[OUT_MAX_S - 2] + pre[OUT_MAX_S - 1];
@@ -960,8 +1017,8 @@ __global__ __launch_bounds__(256) void mla_out(MlaArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int h = 8 * i + 4 * kh + j;
-        if (nr == 1) a.out[ob_off + int64_t(h) * DV] = acc[4 * i + j];
-        else part[h * 128] = acc[4 * i + j];
+        if (nr == 1) a.out[ob_off + int64_t(h) * DV] = poison_if(obad, acc[4 * i + j]);
+        else part[h * 128] = poison_if(obad, acc[4 * i + j]);
       }
   }
   // kept mass of the 32 heads (g == 0): thread t summed the rows t/4 (mod 64)
@@ -974,6 +1031,7 @@ __global__ __launch_bounds__(256) void mla_out(MlaArgs a) {
       const int q = tid >> 3, j = tid & 7;
       float m = 0.f;
       for (int t = q; t < 256; t += 4) m += mpart[t][j];
+      m = poison_if(obad, m);
       if (nr == 1) a.kept_mass[int64_t(b) * H + 32 * hb + 8 * q + j] = m;
       else a.mpart[(int64_t(b * nhb + hb) * R + rg) * 32 + 8 * q + j] = m;
     }
@@ -1271,8 +1329,9 @@ __global__ __launch_bounds__(DN_NT) void mla_out_dense(MlaArgs a) {
   u64* done = a.done + int64_t(bh) * R;
   if (tid == 0) put_tagged_f(done + rg, epoch, 1.f);
   // wait for the other ranges of these heads, then add one slice of their outputs
-  for (int k = tid; k < R; k += NT) settle_f(peek(done + k), done + k, epoch, a.hdr);
-  __syncthreads();
+  bool gave_up = false;
+  for (int k = tid; k < R; k += NT) settle_f(peek(done + k), done + k, epoch, a.hdr, a.spin_limit, gave_up);
+  const bool dbad = __syncthreads_or(gave_up) != 0;   // another range's partials are not this call's: NaN
   __threadfence();
   // slices in float4 units; the R partials of an element are loaded eight at
   // a time and added in range order (the loads of a batch are in flight together)
@@ -1293,6 +1352,7 @@ __global__ __launch_bounds__(DN_NT) void mla_out_dense(MlaArgs a) {
       const float4 t = p0[k * pstride + e];
       v.x += t.x; v.y += t.y; v.z += t.z; v.w += t.w;
     }
+    v.x = poison_if(dbad, v.x); v.y = poison_if(dbad, v.y); v.z = poison_if(dbad, v.z); v.w = poison_if(dbad, v.w);
     reinterpret_cast<float4*>(a.out + (int64_t(b) * H + HW * hh) * DV)[e] = v;
   }
   if (rg == 0 && tid < HW) {                          // kept mass of head HW*hh + tid, ranges in order
@@ -1307,7 +1367,7 @@ __global__ __launch_bounds__(DN_NT) void mla_out_dense(MlaArgs a) {
       for (int u = 0; u < 8; ++u) m += t[u];
     }
     for (; k < R; ++k) m += mp[int64_t(k) * H];
-    a.kept_mass[int64_t(b) * H + HW * hh + tid] = m;
+    a.kept_mass[int64_t(b) * H + HW * hh + tid] = poison_if(dbad, m);
   }
   if (rg == 0 && hh == 0 && wave == 0) {              // kept pairs of the sequence (integer sum: any order)
     long long pairs = 0;

@@ -209,8 +209,17 @@ typedef struct kvq_launch {
  * positions up to the end of its block reaches the threshold. That weight is
  * never smaller than the normalized weight, so the kept set contains the
  * default rule's; the output still uses the normalized weights of the kept
- * positions. Grouped formats only (UNSUPPORTED for the fp8 latent). */
-enum { KVQ_LAUNCH_COOPERATIVE = 1, KVQ_SKIP_RUNNING = 2 };
+ * positions. Grouped formats only (UNSUPPORTED for the fp8 latent).
+ *
+ * KVQ_TEST_WITHHOLD is a test aid for the give-up path of the bounded waits:
+ * context split 0 of the first (sequence, kv head) group does not publish its
+ * split statistics, and every wait gives up after about 4096 polls instead of
+ * about half a second. The call still ends normally: every wait that gives up
+ * sets the sticky status bit (kvq_stats then returns KVQ_ERR_DEVICE), and
+ * every output element and kept mass that depended on a wait that gave up is
+ * written as NaN (here: all outputs of the first group; the other groups are
+ * exact). After such a call the workspace must be zero-filled again. */
+enum { KVQ_LAUNCH_COOPERATIVE = 1, KVQ_SKIP_RUNNING = 2, KVQ_TEST_WITHHOLD = 4 };
 
 /* Device workspace bytes kvq_decode_attn needs for these shapes on the
  * current device (bytes: host out-pointer), for every context length from 1
@@ -270,15 +279,17 @@ int32_t kvq_phase_count(const kvq_launch* l, int32_t* workgroups, int32_t* stamp
 
 /* Measurement reference, not part of the attention path: read `bytes`
  * bytes (a multiple of 16) of device memory at `src` (16-byte aligned) with
- * `grid` workgroups of 1024 threads, workgroup g taking the g-th of `grid`
- * contiguous slices with 16-byte loads, and XOR every 32-bit word a
- * workgroup read into sink[g] (device uint32[grid], caller-owned; zero it
- * first to read the XOR back). Timing it over the bytes and grid of a decode
- * call gives the bandwidth a plain streaming read reaches at that size and
- * launch shape. Asynchronous on `stream` (a hipStream_t, NULL: default).
- * Errors: ARG (null pointer, bytes <= 0 or not a multiple of 16, grid
- * outside 1..2^20), ALIGN, LAUNCH. */
-int32_t kvq_stream_read(const void* src, int64_t bytes, int32_t grid, uint32_t* sink, void* stream);
+ * `grid` workgroups of `threads` threads (256, 512 or 1024), workgroup g
+ * taking the g-th of `grid` contiguous slices with 16-byte loads (each thread
+ * issues up to eight loads before it uses the first), and XOR every 32-bit
+ * word a workgroup read into sink[g] (device uint32[grid], caller-owned; zero
+ * it first to read the XOR back). Timing it over the bytes of a decode call
+ * gives the bandwidth a plain streaming read reaches at that size.
+ * Asynchronous on `stream` (a hipStream_t, NULL: default). Errors: ARG (null
+ * pointer, bytes <= 0 or not a multiple of 16, grid outside 1..2^20, another
+ * workgroup size), ALIGN, LAUNCH. */
+int32_t kvq_stream_read(const void* src, int64_t bytes, int32_t grid, int32_t threads, uint32_t* sink,
+                        void* stream);
 
 /* Static text for an error code. */
 const char* kvq_strerror(int32_t code);

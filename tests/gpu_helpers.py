@@ -46,14 +46,17 @@ def run_gpu(inp, threshold, *, ctx_len=None, splits=0, q_bf16=False, repeat=1, c
     masks = []
     stats = None
     for _ in range(repeat):
-        mask = None
-        if V is not None:                       # the latent (MLA) path reports no per-head bits
-            mask = torch.zeros((w.batch, w.q_heads, mask_words(n)), dtype=torch.int32, device="cuda")
+        # filled with a pattern no result has in every word, so a word the
+        # kernel leaves unwritten shows up as a mismatch
+        mask = torch.full((w.batch, w.q_heads, mask_words(n)), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
         out = att(q, n, threshold, mask_out=mask)
         torch.cuda.synchronize()
         stats = att.stats()
         outs.append(out.cpu().numpy())
-        masks.append(unpack_mask(mask.cpu().numpy().view(np.uint32), n) if mask is not None else None)
+        mw = mask.cpu().numpy().view(np.uint32)
+        if n % 32:                               # bits past the context in the last word are zero
+            assert not (mw[..., -1] >> np.uint32(n % 32)).any(), "mask bits set past the context"
+        masks.append(unpack_mask(mw, n))
     return dict(out=outs[0], outs=outs, mask=masks[0], masks=masks, stats=stats,
                 planes=dict(kc=kc, ks=ks, vc=vc, vs=vs), splits=att.stats()["splits"])
 

@@ -108,10 +108,11 @@ def test_append_kv_argument_validation_without_gpu():
 def test_stream_read_argument_validation_without_gpu():
     L = B.lib()
     src, sink = 0x10000, 0x20000                           # fake aligned addresses: never dereferenced
-    assert L.kvq_stream_read(None, 1024, 4, sink, None) == -1
-    assert L.kvq_stream_read(src, 1024, 4, None, None) == -1
-    assert L.kvq_stream_read(src, 0, 4, sink, None) == -1
-    assert L.kvq_stream_read(src, 1000, 4, sink, None) == -1     # not a multiple of 16
-    assert L.kvq_stream_read(src, 1024, 0, sink, None) == -1
-    assert L.kvq_stream_read(src, 1024, (1 << 20) + 1, sink, None) == -1
-    assert L.kvq_stream_read(0x10008, 1024, 4, sink, None) == -2  # ALIGN
+    assert L.kvq_stream_read(None, 1024, 4, 1024, sink, None) == -1
+    assert L.kvq_stream_read(src, 1024, 4, 1024, None, None) == -1
+    assert L.kvq_stream_read(src, 0, 4, 1024, sink, None) == -1
+    assert L.kvq_stream_read(src, 1000, 4, 1024, sink, None) == -1     # not a multiple of 16
+    assert L.kvq_stream_read(src, 1024, 0, 1024, sink, None) == -1
+    assert L.kvq_stream_read(src, 1024, (1 << 20) + 1, 1024, sink, None) == -1
+    assert L.kvq_stream_read(src, 1024, 4, 128, sink, None) == -1      # workgroup size not built
+    assert L.kvq_stream_read(0x10008, 1024, 4, 1024, sink, None) == -2  # ALIGN

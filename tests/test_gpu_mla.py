@@ -22,7 +22,7 @@ def test_mla_small(threshold):
     inp, tau = _case(threshold, batch=2, ctx=4096, hot=8)
     g = run_gpu(inp, tau, q_bf16=True)
     r, po = oracle_for(inp, tau)
-    compare(inp, tau, g, r, po, mask=False)
+    compare(inp, tau, g, r, po)
 
 
 @pytest.mark.parametrize("heads", [32, 64])
@@ -34,7 +34,7 @@ def test_mla_head_counts(heads, threshold):
     inp, tau = _case(threshold, batch=1, q_heads=heads, ctx=3000, hot=6)
     g = run_gpu(inp, tau, q_bf16=True)
     r, po = oracle_for(inp, tau)
-    compare(inp, tau, g, r, po, mask=False)
+    compare(inp, tau, g, r, po)
 
 
 @pytest.mark.parametrize("ctx", [1, 100, 3001])
@@ -44,7 +44,23 @@ def test_mla_ragged(ctx, threshold):
     inp, tau = _case(threshold, batch=1, ctx=ctx, hot=min(4, ctx))
     g = run_gpu(inp, tau, q_bf16=True)
     r, po = oracle_for(inp, tau)
-    compare(inp, tau, g, r, po, mask=False)
+    compare(inp, tau, g, r, po)
+
+
+@pytest.mark.parametrize("heads", [32, 128])
+def test_mla_scattered_weights(heads):
+    """No planted rows and latent rows of standard deviation 2: the scaled
+    logits spread over about 25 nats, so weights fall on both sides of 1e-6
+    throughout the context (many live tiles, many heads keeping different
+    positions, weights near the threshold)."""
+    say("case mla scattered weights, heads", heads)
+    inp, tau = _case(batch=2, q_heads=heads, ctx=5000, hot=0, key_std=2.0, seed=21)
+    g = run_gpu(inp, tau, q_bf16=True)
+    r, po = oracle_for(inp, tau)
+    frac = r.kept_pairs / r.mask.size
+    say(f"  kept fraction {frac:.4f}")
+    assert 0.01 < frac < 0.9
+    compare(inp, tau, g, r, po)
 
 
 def test_mla_dense_row_ranges():
@@ -58,7 +74,7 @@ def test_mla_dense_row_ranges():
     for o in g["outs"][1:]:
         assert np.array_equal(o, g["outs"][0])
     r, po = oracle_for(inp, tau)
-    compare(inp, tau, g, r, po, mask=False)
+    compare(inp, tau, g, r, po)
     assert g["stats"]["rows_fetched"] == 2 * 20000
 
 
@@ -77,30 +93,39 @@ def test_mla_every_fp8_code():
     assert len(set(codes.ravel().tolist())) == 254
     g = run_gpu(inp, tau, q_bf16=True)
     r, po = oracle_for(inp, tau)
-    compare(inp, tau, g, r, po, mask=False)
+    compare(inp, tau, g, r, po)
 
 
 @pytest.mark.parametrize("threshold", [None, 0.0])
-def test_mla_full_size_sampled(threshold):
+def test_mla_full_size(threshold):
     """Full workload (batch 8, 128 heads, ctx 65536) on the GPU, with the
     workload's threshold and with every row kept (the dense output kernel,
-    as timed); the oracle recomputes sequences 0 and 7 one by one."""
-    say("case mla full size: batch 8, 128 heads, ctx 65536 (oracle on sequences 0 and 7), threshold",
+    as timed); the oracle recomputes every sequence, one at a time, and each
+    is compared in full: packed planes, per-head keep bits outside the band,
+    output, kept mass."""
+    say("case mla full size: batch 8, 128 heads, ctx 65536, every sequence, threshold",
         "1e-6" if threshold is None else threshold)
     inp, tau = _case(threshold)
     g = run_gpu(inp, tau, q_bf16=True)
-    for b in (0, 7):
+    kept = rows = nband = 0
+    for b in range(inp.w.batch):
         sub = synth.Inputs(synth.resized(inp.w, batch=1), inp.q[b:b + 1], inp.k[b:b + 1], None,
                            [inp.hot[b]])
         r, po = oracle_for(sub, tau)
         assert np.array_equal(g["planes"]["kc"][b:b + 1], po["kc"])
         assert np.array_equal(g["planes"]["ks"][b:b + 1], po["ks"])
-        gb = dict(g, out=g["out"][b:b + 1], planes={"kc": None, "ks": None, "vc": None, "vs": None})
-        compare(sub, tau, gb, r, {"kc": None, "ks": None, "vc": None, "vs": None}, mask=False,
-                check_stats=False)
+        gb = dict(g, out=g["out"][b:b + 1], mask=g["mask"][b:b + 1],
+                  planes={"kc": None, "ks": None, "vc": None, "vs": None})
+        say("  sequence", b)
+        compare(sub, tau, gb, r, {"kc": None, "ks": None, "vc": None, "vs": None}, check_stats=False)
         assert np.allclose(g["stats"]["kept_mass"][b], r.kept_mass[0], atol=1e-5)
+        kept += r.kept_pairs
+        rows += r.rows_fetched
+        nband += int(A.band(r.p, tau).sum())
+        del r
     st = g["stats"]
     assert st["status"] == 0
+    assert abs(st["kept_pairs"] - kept) <= nband and abs(st["rows_fetched"] - rows) <= nband, (st, kept, rows)
     if tau > 0:
         # every sequence keeps exactly its 96 planted rows (the boost puts them far above the rest)
         assert st["rows_fetched"] == 8 * 96, st
