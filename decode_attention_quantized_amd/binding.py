@@ -52,8 +52,8 @@ class kvq_stats_t(ctypes.Structure):
 
 
 EXPORTS = ["kvq_row_bytes", "kvq_pack", "kvq_unpack", "kvq_lut3_levels", "kvq_append", "kvq_append_kv",
-           "kvq_workspace_bytes",
-           "kvq_decode_attn", "kvq_stats", "kvq_phase_count", "kvq_strerror", "kvq_stream_read"]
+           "kvq_workspace_bytes", "kvq_decode_attn", "kvq_decode_attn_noalloc", "kvq_stats", "kvq_phase_count",
+           "kvq_strerror", "kvq_stream_read"]
 
 _lib = None
 
@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
                                           ctypes.POINTER(i64)]
         L.kvq_decode_attn.argtypes = [vp, ctypes.POINTER(kvq_cache), ctypes.POINTER(kvq_cache), i32, i32,
                                       ctypes.c_float, vp, ctypes.POINTER(kvq_launch)]
+        L.kvq_decode_attn_noalloc.argtypes = [vp, ctypes.POINTER(kvq_cache), ctypes.POINTER(kvq_cache), i32, i32,
+                                              ctypes.c_float, vp, ctypes.POINTER(kvq_launch)]
         L.kvq_stats.argtypes = [ctypes.POINTER(kvq_launch), ctypes.POINTER(kvq_stats_t), vp]
         L.kvq_phase_count.argtypes = [ctypes.POINTER(kvq_launch), ctypes.POINTER(i32), ctypes.POINTER(i32)]
         L.kvq_strerror.argtypes = [i32]
@@ -203,6 +205,16 @@ def kvq_decode_attn(q, kcache: kvq_cache, vcache, fmt, ctx_len: int, threshold: 
     vptr = ctypes.byref(vcache) if vcache is not None else None
     _check(lib().kvq_decode_attn(q.data_ptr(), ctypes.byref(kcache), vptr, _fmt(fmt), int(ctx_len),
                                  float(threshold), out.data_ptr(), ctypes.byref(launch)), "kvq_decode_attn")
+
+
+def kvq_decode_attn_noalloc(q, kcache: kvq_cache, vcache, fmt, ctx_len: int, threshold: float, out,
+                            launch: kvq_launch):
+    """kvq_decode_attn on the library's own fixed device array instead of
+    launch.workspace (allocates nothing)."""
+    vptr = ctypes.byref(vcache) if vcache is not None else None
+    _check(lib().kvq_decode_attn_noalloc(q.data_ptr(), ctypes.byref(kcache), vptr, _fmt(fmt), int(ctx_len),
+                                         float(threshold), out.data_ptr(), ctypes.byref(launch)),
+           "kvq_decode_attn_noalloc")
 
 
 def kvq_stats(launch: kvq_launch, kept_mass: bool = True):

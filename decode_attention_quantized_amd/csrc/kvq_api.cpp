@@ -448,3 +448,51 @@ extern "C" int32_t kvq_stats(const kvq_launch* l, kvq_stats_t* out, float* kept_
   }
   return h.status ? KVQ_ERR_DEVICE : KVQ_OK;
 }
+
+// ---------------------------------------------------------------- no-allocation entry point
+// A fixed device array stands in for the caller's workspace. Each GPU holds
+// its own copy (zero at load, which is the state a fresh workspace must
+// have; the kernels keep it valid from call to call). Host code never uses
+// the array's name as an address: the device address of this device's copy
+// comes from hipGetSymbolAddress, once per device, and is kept.
+namespace {
+
+constexpr int64_t kScratchBytes = int64_t(8) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+void* scratch_address(int dev) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev < 0 || dev >= 64) return nullptr;
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
+}  // namespace
+
+extern "C" int32_t kvq_decode_attn_noalloc(const void* q, const kvq_cache* kcache, const kvq_cache* vcache,
+                                           int32_t fmt, int32_t ctx_len, float threshold, float* out,
+                                           const kvq_launch* l) {
+  if (!q || !kcache || !out || !l) return KVQ_ERR_ARG;
+  Plan plan;
+  const int32_t rc = make_plan(fmt, kcache, l, ctx_len, &plan);
+  if (rc) return rc;
+  if (plan.mla) return KVQ_ERR_UNSUPPORTED;              // the latent plans need far more than the array
+  if (plan.total > kScratchBytes) return KVQ_ERR_WORKSPACE;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return KVQ_ERR_LAUNCH;
+  void* ws = scratch_address(dev);
+  if (!ws) return KVQ_ERR_LAUNCH;
+  kvq_launch lw = *l;
+  lw.workspace = ws;
+  lw.workspace_bytes = kScratchBytes;
+  return kvq_decode_attn(q, kcache, vcache, fmt, ctx_len, threshold, out, &lw);
+}

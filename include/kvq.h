@@ -252,6 +252,26 @@ int32_t kvq_decode_attn(const void* q, const kvq_cache* kcache, const kvq_cache*
                         int32_t fmt, int32_t ctx_len, float threshold, float* out,
                         const kvq_launch* l);
 
+/* kvq_decode_attn for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same computation, kernels and arguments, except that l->workspace and
+ * l->workspace_bytes are ignored. Instead the library uses a fixed 8 MiB
+ * device array of its own (one per GPU, zero when the library is loaded and
+ * kept valid by the kernels from call to call; it is held until the process
+ * ends). The caller still passes q, the caches and out. No call allocates.
+ * Grouped-query formats only: the fp8 latent plans need far more workspace
+ * (UNSUPPORTED); a plan whose workspace exceeds 8 MiB returns
+ * KVQ_ERR_WORKSPACE (on a 256-CU GPU every grouped plan fits). Every call on
+ * one GPU uses that GPU's array: calls that overlap on one GPU (concurrent
+ * streams, or several threads) race and must be serialized by the caller.
+ * kvq_stats cannot read this array's counters; a bounded wait that gives up
+ * still shows as NaN in the outputs that depended on it.
+ * Errors: as kvq_decode_attn, plus LAUNCH if the array's address cannot be
+ * obtained. */
+int32_t kvq_decode_attn_noalloc(const void* q, const kvq_cache* kcache, const kvq_cache* vcache,
+                                int32_t fmt, int32_t ctx_len, float threshold, float* out,
+                                const kvq_launch* l);
+
 typedef struct kvq_stats_t {
   int64_t positions;       /* batch * kv_heads * ctx_len key rows scored */
   int64_t pairs;           /* batch * q_heads * ctx_len (head, position) weights */
