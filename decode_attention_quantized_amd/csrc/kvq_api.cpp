@@ -223,6 +223,8 @@ int32_t launch_mla(const void* q, const kvq_cache* kcache, const kvq_cache* vcac
   a.ocnt = reinterpret_cast<uint32_t*>(ws + plan.mws.ocnt);
   a.done = reinterpret_cast<unsigned long long*>(ws + plan.mws.done);
   a.lseo = reinterpret_cast<float*>(ws + plan.mws.lseo);
+  a.live = reinterpret_cast<int32_t*>(ws + plan.mws.live);
+  a.live_off = plan.mws.live;
   a.mask_out = l->mask_out;
   a.mask_words = (ctx_len + 31) / 32;
   // threshold 0 keeps every row: the output contraction is split over row
@@ -366,6 +368,8 @@ extern "C" int32_t kvq_decode_attn(const void* q, const kvq_cache* kcache, const
   a.flags = reinterpret_cast<unsigned long long*>(ws + plan.ws.flags);
   a.pmass = reinterpret_cast<unsigned long long*>(ws + plan.ws.pmass);
   a.partial = reinterpret_cast<unsigned long long*>(ws + plan.ws.partial);
+  a.live = reinterpret_cast<int32_t*>(ws + plan.ws.live);
+  a.live_off = plan.ws.live;
   a.B = kcache->batch;
   a.Hkv = kcache->heads;
   a.Hq = l->q_heads;
@@ -435,6 +439,13 @@ extern "C" int32_t kvq_stats(const kvq_launch* l, kvq_stats_t* out, float* kept_
       out->rows_fetched += int64_t(st[2 * i + 1]);
     }
     out->v_bytes = out->rows_fetched * h.v_row_bytes;
+  }
+  if (h.batch > 0 && h.nwg > 0 && h.live_off > 0) {
+    std::vector<int32_t> lv(size_t(h.nwg));
+    if (hipMemcpy(lv.data(), static_cast<unsigned char*>(l->workspace) + h.live_off, lv.size() * 4,
+                  hipMemcpyDeviceToHost) != hipSuccess)
+      return KVQ_ERR_LAUNCH;
+    for (int32_t v : lv) out->live_tiles += v;
   }
   out->status = int32_t(h.status);
   out->splits = h.splits;

@@ -252,6 +252,26 @@ __device__ inline uint32_t lut_pair(const Lut& L, uint32_t addr) {
   else return uint32_t(__builtin_amdgcn_ds_bpermute(int(addr), int(L.entry)));
 }
 
+// K rows are read with buffer loads: the resource covers exactly the split's
+// rows in the context, so a load past them (the pipelined loop requests
+// batches beyond the split) returns zeros without touching memory; the row
+// offset of a tile is a wave-uniform byte offset and the lane's part a
+// 32-bit offset, so no 64-bit address arithmetic is needed per tile.
+typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x3v __attribute__((ext_vector_type(3)));
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+__device__ inline __amdgpu_buffer_rsrc_t rows_rsrc(const uint8_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, bytes, 0x00020000);
+}
+__device__ inline uint4 bload16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ inline uint2 bload8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  const u32x2v v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+  return make_uint2(v.x, v.y);
+}
+
 // ---------------------------------------------------------------- format traits
 // Each lane of a 16x16x32 MFMA supplies 8 consecutive K-slots of one column.
 // For the K pass the column is a position and the 32 K-slots of one MFMA are
@@ -281,11 +301,13 @@ template <> struct Traits<KVQ_Q4_0> {
   static constexpr bool kStaged = true;
   static constexpr int NV = 1;                    // 16-byte pieces per lane and row
   static constexpr int PITCH = 80;                // staged row pitch in LDS (bytes)
+  static constexpr int kLaneOff = 16;             // byte offset of lane group kg's piece in a row
   struct Raw16 { uint4 v[NV]; uint2 s; };
-  __device__ static Raw16 load16(const uint8_t* crow, const uint8_t* srow, int kg) {
+  __device__ static Raw16 bload(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs, int vc, int vs, int sc,
+                                int ss) {
     Raw16 r;
-    r.v[0] = *reinterpret_cast<const uint4*>(crow + 16 * kg);
-    r.s = *reinterpret_cast<const uint2*>(srow);
+    r.v[0] = bload16(rc, vc, sc);
+    r.s = bload8(rs, vs, ss);
     return r;
   }
   __device__ static void stage(uint8_t* lrow, const Raw16& r, int kg) {
@@ -340,12 +362,14 @@ template <> struct Traits<KVQ_Q8_0> {
   static constexpr bool kStaged = true;
   static constexpr int NV = 2;
   static constexpr int PITCH = 144;
+  static constexpr int kLaneOff = 32;
   struct Raw16 { uint4 v[NV]; uint2 s; };
-  __device__ static Raw16 load16(const uint8_t* crow, const uint8_t* srow, int kg) {
+  __device__ static Raw16 bload(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs, int vc, int vs, int sc,
+                                int ss) {
     Raw16 r;
-    r.v[0] = *reinterpret_cast<const uint4*>(crow + 32 * kg);
-    r.v[1] = *reinterpret_cast<const uint4*>(crow + 32 * kg + 16);
-    r.s = *reinterpret_cast<const uint2*>(srow);
+    r.v[0] = bload16(rc, vc, sc);
+    r.v[1] = bload16(rc, vc + 16, sc);
+    r.s = bload8(rs, vs, ss);
     return r;
   }
   __device__ static void stage(uint8_t* lrow, const Raw16& r, int kg) {
@@ -417,11 +441,13 @@ template <> struct Traits<KVQ_LUT3> {
   // MFMA bb takes elements 32kk + 8bb + e
   __device__ static int dim_of(int bb, int kk, int e) { return 32 * kk + 8 * bb + e; }
   __device__ static void locate(int d, int& bb, int& kk, int& slot) { kk = d >> 5; bb = (d >> 3) & 3; slot = d & 7; }
-  __device__ static Raw load(const uint8_t* crow, const uint8_t* srow, int kk) {
+  static constexpr int kLaneOff = 12;             // lane group kk reads bytes 12kk .. 12kk + 11
+  __device__ static Raw bload(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs, int vc, int vs, int sc,
+                              int ss) {
     Raw r;
-    const uint32_t* p = reinterpret_cast<const uint32_t*>(crow + 12 * kk);
-    r.c[0] = p[0]; r.c[1] = p[1]; r.c[2] = p[2];
-    r.s = *reinterpret_cast<const uint16_t*>(srow);
+    const u32x3v v = __builtin_amdgcn_raw_buffer_load_b96(rc, vc, sc, 0);
+    r.c[0] = v.x; r.c[1] = v.y; r.c[2] = v.z;
+    r.s = __builtin_amdgcn_raw_buffer_load_b16(rs, vs, ss, 0);
     return r;
   }
   // byte address (4 * key) of the 6-bit key at bit b of the lane's 96 bits
@@ -627,6 +653,10 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   const int P = a.P;
   const int sc_floats = gqa_sc_floats(G, P, a.S);
   float* sc = reinterpret_cast<float*>(smem);
+  // scores (then weights) of head j at split position i: chunk-major, the G
+  // heads' 64 values of a chunk contiguous, so one chunk's heads are read
+  // from one base address with constant offsets
+  auto sidx = [](int j, int i) { return (i >> 6) * (G * kChunk) + j * kChunk + (i & (kChunk - 1)); };
   _Float16* qop = reinterpret_cast<_Float16*>(sc + sc_floats);     // [16 rows][4 blk][4 kk][8]
   float* cst = reinterpret_cast<float*>(qop + 16 * 128);          // [4 blk][16 rows]
   float* hs = cst + 64;                                           // [8] per-head score scale
@@ -674,19 +704,25 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   using Loaded = typename LoadedOf<T, T::kStaged>::type;
   // a wave's batches of U tiles are double-buffered (the next batch is
   // requested before the current one is scored) when two fit in registers
+  // (a third buffer measured slower for LUT3)
   constexpr bool kDouble = sizeof(Loaded) <= 24;
   Loaded rawA[U], rawB[kDouble ? U : 1];
-  // Every lane loads unconditionally: a position past the context (or a tile
-  // past the split) reads row ctx - 1 instead, and its score is masked to
-  // -inf. No load sits behind a branch, so the next batch's loads are issued
-  // before the current batch is waited for.
-  auto load_tiles = [&](Loaded* raw, int t0) {
+  // Every lane loads unconditionally (buffer loads over the split's rows in
+  // the context: a position past them reads zeros, its score is masked to
+  // -inf or never formed). No load sits behind a branch, so the next batch's
+  // loads are issued before the current batch is waited for. Batch kb's
+  // tile u is tile wave + (kb * U + u) * kWaves; its rows start
+  // (kb * U + u) * kWaves * 16 rows after the wave's first tile.
+  const int nvalid = min(P, ctx - pos0);
+  const __amdgpu_buffer_rsrc_t krc = rows_rsrc(a.kc + (row0 + pos0) * T::CB, nvalid * T::CB);
+  const __amdgpu_buffer_rsrc_t krs = rows_rsrc(a.ks + (row0 + pos0) * T::SB, nvalid * T::SB);
+  const int kvc = (16 * wave + n16) * T::CB + T::kLaneOff * kg;
+  const int kvs = (16 * wave + n16) * T::SB;
+  auto load_tiles = [&](Loaded* raw, int kb) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int t = t0 + u * kWaves;
-      const int64_t row = row0 + min(pos0 + t * 16 + n16, ctx - 1);
-      if constexpr (T::kStaged) raw[u] = T::load16(a.kc + row * T::CB, a.ks + row * T::SB, kg);
-      else raw[u] = T::load(a.kc + row * T::CB, a.ks + row * T::SB, kg);
+      const int m = (kb * U + u) * kWaves * 16;      // rows past the wave's first tile (uniform)
+      raw[u] = T::bload(krc, krs, kvc, kvs, m * T::CB, m * T::SB);
     }
   };
   // the operand layout of a loaded tile (through this wave's LDS strip when
@@ -700,9 +736,17 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
       return rl;
     }
   };
-  load_tiles(rawA, wave);
-  // keep these loads ahead of the q loads below (both latencies then overlap
-  // in the set-up's first barrier instead of following one another)
+  // q of this group first, then the first K tiles: loads complete in order,
+  // so the set-up below waits for q only while the K tiles are in flight
+  // (one unconditional 16-byte load per thread, whatever the element type: a
+  // bf16 row uses the first 8 bytes; the buffer bounds make the bytes past
+  // the end of q read as zeros)
+  const int jq = tid >> 5, lnq = tid & 31;          // 32 threads per head, 4 dims each
+  const int qesz = a.q_bf16 ? 2 : 4;
+  const __amdgpu_buffer_rsrc_t qrc = rows_rsrc(static_cast<const uint8_t*>(a.q), a.B * a.Hq * 128 * qesz);
+  const uint4 qraw = bload16(qrc, ((b * a.Hq + g * G + min(jq, G - 1)) * 128 + lnq * 4) * qesz, 0);
+  __asm__ volatile("" ::: "memory");
+  load_tiles(rawA, 0);
   __asm__ volatile("" ::: "memory");
 
   // ---------------------------------------------------------------- setup
@@ -712,6 +756,7 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     a.hdr->nwg = int(gridDim.x);
     a.hdr->k_row_bytes = T::CB + T::SB;
     a.hdr->v_row_bytes = T::CB + T::SB;
+    a.hdr->live_off = a.live_off;
   }
   for (int c = tid; c < P / kChunk; c += kThreads) umask[c] = 0ull;
   if (tid == 0) wto[0] = 0;
@@ -719,18 +764,15 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   // q of this group: per-head max |q| -> power-of-two prescale, then fp16 hi/lo rows
   float qv[4];
   {
-    const int j = tid >> 5, ln = tid & 31;      // 32 threads per head, 4 dims each
+    const int j = jq, ln = lnq;
     float m = 0.f;
     if (j < G) {
-      const int h = g * G + j;
-      const int64_t qoff = (int64_t(b) * a.Hq + h) * 128 + ln * 4;
-      if (a.q_bf16) {                                  // one 8-byte load
-        const uint2 r = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.q) + qoff);
-        qv[0] = __uint_as_float(r.x << 16); qv[1] = __uint_as_float(r.x & 0xFFFF0000u);
-        qv[2] = __uint_as_float(r.y << 16); qv[3] = __uint_as_float(r.y & 0xFFFF0000u);
-      } else {                                         // one 16-byte load
-        const float4 r = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.q) + qoff);
-        qv[0] = r.x; qv[1] = r.y; qv[2] = r.z; qv[3] = r.w;
+      if (a.q_bf16) {
+        qv[0] = __uint_as_float(qraw.x << 16); qv[1] = __uint_as_float(qraw.x & 0xFFFF0000u);
+        qv[2] = __uint_as_float(qraw.y << 16); qv[3] = __uint_as_float(qraw.y & 0xFFFF0000u);
+      } else {
+        qv[0] = __uint_as_float(qraw.x); qv[1] = __uint_as_float(qraw.y);
+        qv[2] = __uint_as_float(qraw.z); qv[3] = __uint_as_float(qraw.w);
       }
       if constexpr (kRot) {
         // q' = H q / sqrt(128): dims 4ln + e; stages 1 and 2 inside the
@@ -844,8 +886,8 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
       const bool valid = (pos0 + lp) < ctx;
       const float s0 = valid ? (acc[0] + acc[1]) * hs0 : -INFINITY;
       const float s1 = valid ? (acc[2] + acc[3]) * hs1 : -INFINITY;
-      if (j0 < G) sc[j0 * P + lp] = s0;
-      if (j1 < G) sc[j1 * P + lp] = s1;
+      if (j0 < G) sc[sidx(j0, lp)] = s0;
+      if (j1 < G) sc[sidx(j1, lp)] = s1;
       sa[u] = s0;
       sb[u] = s1;
     }
@@ -853,20 +895,22 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     batch_stats<U>(m1, l1, sb);
   };
   constexpr int STRIDE = kWaves * U;                  // tiles between a wave's batches
+  const int nbat = (ntiles + STRIDE - 1) / STRIDE;     // batches of the split (uniform)
   if constexpr (kDouble) {
     // the loads of the next batch are issued before the current batch is
-    // scored, unconditionally (past the split they re-read row ctx - 1, an
-    // L2 hit), so no load depends on a branch and two batches stay in flight
-    for (int t0 = wave; t0 < ntiles; t0 += 2 * STRIDE) {
-      load_tiles(rawB, t0 + STRIDE);
-      score_batch(rawA, t0);
-      load_tiles(rawA, t0 + 2 * STRIDE);
-      score_batch(rawB, t0 + STRIDE);               // tiles past the split are skipped inside
+    // scored, unconditionally (past the split they read zeros without a
+    // memory access), so no load depends on a branch and two batches stay in
+    // flight; tiles past the split are skipped inside score_batch
+    for (int kb = 0; kb < nbat; kb += 2) {
+      load_tiles(rawB, kb + 1);
+      score_batch(rawA, wave + kb * STRIDE);
+      load_tiles(rawA, kb + 2);
+      score_batch(rawB, wave + (kb + 1) * STRIDE);
     }
   } else {
-    for (int t0 = wave; t0 < ntiles; t0 += STRIDE) {
-      if (t0 != wave) load_tiles(rawA, t0);
-      score_batch(rawA, t0);
+    for (int kb = 0; kb < nbat; ++kb) {
+      if (kb > 0) load_tiles(rawA, kb);
+      score_batch(rawA, wave + kb * STRIDE);
     }
   }
   // split statistics: merge over the 16 lanes of a lane group, then over waves
@@ -952,7 +996,7 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
       const int q4 = it & 3, jc = it >> 2;
       const int j = jc / nch, c = jc - j * nch;
       float m = -INFINITY, l = 0.f;
-      const float* src = sc + j * P + c * kChunk + 16 * q4;
+      const float* src = sc + sidx(j, c * kChunk + 16 * q4);
 #pragma unroll
       for (int i = 0; i < 16; ++i) online_add(m, l, src[i]);
       float2 v = make_float2(m, l);
@@ -979,7 +1023,8 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   //     A head keeps a position iff its normalized weight 2^(s - LSE) reaches
   //     the threshold, decided on the score as s >= LSE + log2(threshold)
   //     (the two differ only for weights within float32 rounding of the
-  //     threshold); weights are formed only in chunks that keep a row.
+  //     threshold). The scores stay in place: the value pass forms the
+  //     weights of the rows it fetches (the same decision, then 2^(s - LSE)).
   // (b) After one barrier each takes the kept rows of its chunks of even
   //     (first wave of the pair) or odd (second) rank and fetches only those.
   constexpr int HALF = G > 1 ? G / 2 : 1;
@@ -1003,68 +1048,93 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   }
   const int nchunks = P / kChunk;
   if (do_p) {
-    // the scores of the wave's next chunk are read while this one is decided
-    float svn[HALF];
+    // a score past the context is -inf, below every threshold (threshold 0
+    // compares with the lowest finite value)
+    float th[HALF];
 #pragma unroll
-    for (int jj = 0; jj < HALF; ++jj) svn[jj] = pair < nchunks ? sc[(jb + jj) * P + pair * kChunk + lane] : 0.f;
-    for (int c = pair; c < nchunks; c += kWaves / 2) {
-      const int lp = c * kChunk + lane;
-      const bool valid = pos0 + lp < ctx;
-      float sv[HALF];
+    for (int jj = 0; jj < HALF; ++jj) th[jj] = fmaxf(thr[jj], -3.4028235e38f);
+    // four of the wave's chunks per step: their scores are read together,
+    // so the LDS latency is paid once per four chunks
+    constexpr int CB4 = 4, CSTEP = kWaves / 2;
+    for (int c0 = pair; c0 < nchunks; c0 += CB4 * CSTEP) {
+      float sv4[CB4][HALF];
 #pragma unroll
-      for (int jj = 0; jj < HALF; ++jj) sv[jj] = svn[jj];
-      const int cn = c + kWaves / 2;
+      for (int q = 0; q < CB4; ++q) {
+        const int c = min(c0 + q * CSTEP, nchunks - 1);
+        const float* base = sc + c * (G * kChunk) + jb * kChunk + lane;
 #pragma unroll
-      for (int jj = 0; jj < HALF; ++jj) svn[jj] = cn < nchunks ? sc[(jb + jj) * P + cn * kChunk + lane] : 0.f;
-      unsigned long long bal[HALF], uni = 0ull;
-#pragma unroll
-      for (int jj = 0; jj < HALF; ++jj) {
-        // single-pass rule: the reference is the running LSE of the block
-        const float th = RUN ? rl[(jb + jj) * nch + c] + ltau : thr[jj];
-        bal[jj] = __ballot(valid && sv[jj] >= th);
-        uni |= bal[jj];
-        kept_cnt += __popcll(bal[jj]);
+        for (int jj = 0; jj < HALF; ++jj) sv4[q][jj] = base[jj * kChunk];
       }
-      // kept weights replace the scores in place; a head that skips a row
-      // another head keeps leaves 0 there, and so does every head in a chunk
-      // where this wave's heads keep nothing (the other half of the group may
-      // keep rows of it). Single-pass rule: relative to the split's max,
-      // rescaled when the partial is published.
-      if (uni) {                                   // uniform
+#pragma unroll
+      for (int q = 0; q < CB4; ++q) {
+        const int c = c0 + q * CSTEP;
+        if (c >= nchunks) break;                      // uniform
+        float* base = sc + c * (G * kChunk) + jb * kChunk + lane;
+        const float (&sv)[HALF] = sv4[q];
+        unsigned long long bal[HALF], uni = 0ull;
 #pragma unroll
         for (int jj = 0; jj < HALF; ++jj) {
-          const bool keep = (bal[jj] >> lane) & 1ull;
-          const float x = sv[jj] - lsej[jj];
-          sc[(jb + jj) * P + lp] = keep ? (hw_exp ? ex2(x) : exp2f(x)) : 0.f;
+          // single-pass rule: the reference is the running LSE of the block
+          const float t = RUN ? fmaxf(rl[(jb + jj) * nch + c] + ltau, -3.4028235e38f) : th[jj];
+          bal[jj] = __ballot(sv[jj] >= t);
+          uni |= bal[jj];
+          kept_cnt += __popcll(bal[jj]);
         }
-        if (lane == 0) atomicOr(&umask[c], uni);
-      } else {
+        if (lane == 0 && uni) atomicOr(&umask[c], uni);
+        if constexpr (RUN) {
+          // single-pass rule: the running LSE of the blocks lives in the K
+          // staging strip, which the value pass reuses, so the weights
+          // (relative to the split's max, 0 where a head skips) replace the
+          // scores here
 #pragma unroll
-        for (int jj = 0; jj < HALF; ++jj) sc[(jb + jj) * P + lp] = 0.f;
-      }
-      if (a.mask_out && lane < 2) {
-        const int word = (pos0 + c * kChunk) / 32 + lane;
-        if (word < a.mask_words)
+          for (int jj = 0; jj < HALF; ++jj) {
+            const bool keep = (bal[jj] >> lane) & 1ull;
+            const float x = sv[jj] - lsej[jj];
+            base[jj * kChunk] = keep ? (hw_exp ? ex2(x) : exp2f(x)) : 0.f;
+          }
+        }
+        if (a.mask_out && lane < 2) {
+          const int word = (pos0 + c * kChunk) / 32 + lane;
+          if (word < a.mask_words)
 #pragma unroll
-          for (int jj = 0; jj < HALF; ++jj)
-            a.mask_out[(int64_t(b) * a.Hq + g * G + jb + jj) * a.mask_words + word] = uint32_t(bal[jj] >> (32 * lane));
+            for (int jj = 0; jj < HALF; ++jj)
+              a.mask_out[(int64_t(b) * a.Hq + g * G + jb + jj) * a.mask_words + word] = uint32_t(bal[jj] >> (32 * lane));
+        }
       }
     }
   }
   stamp(a, 7);
   __syncthreads();
   uint16_t* mylist = rowlist + wave * list_cap;
-  int nmine = 0, rows_cnt = 0;
-  for (int c = pair; c < nchunks; c += kWaves / 2) {
-    const unsigned long long um = umask[c];
-    const int n = __popcll(um);
-    if (side == 0) rows_cnt += n;
-    const int rank = __popcll(um & ((1ull << lane) - 1ull));
-    if (((um >> lane) & 1ull) && (rank & 1) == side) mylist[nmine + (rank >> 1)] = uint16_t(c * kChunk + lane);
-    nmine += (n + 1 - side) >> 1;
+  int nmine = 0, rows_cnt = 0;                       // rows_cnt: rows | live chunks << 16
+  for (int c0 = pair; c0 < nchunks; c0 += 4 * (kWaves / 2)) {
+    unsigned long long um4[4];                        // four chunks' union words read together
+#pragma unroll
+    for (int q = 0; q < 4; ++q) um4[q] = umask[min(c0 + q * (kWaves / 2), nchunks - 1)];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = c0 + q * (kWaves / 2);
+      if (c >= nchunks) break;                        // uniform
+      const unsigned long long um = um4[q];
+      const int n = __popcll(um);
+      if (side == 0) rows_cnt += n + (n ? 1 << 16 : 0);
+      const int rank = __popcll(um & ((1ull << lane) - 1ull));
+      if (((um >> lane) & 1ull) && (rank & 1) == side) mylist[nmine + (rank >> 1)] = uint16_t(c * kChunk + lane);
+      nmine += (n + 1 - side) >> 1;
+    }
   }
   stamp(a, 8);
   using VM = VMfma<FMT>;
+  // weight of head j at split position i: 2^(s - LSE) if the head keeps the
+  // position, else 0 (single-pass rule: formed in the keep-decision pass)
+  auto weight = [&](int j, int i) __attribute__((always_inline)) -> float {
+    const float sv = sc[sidx(j, i)];
+    if constexpr (RUN) return sv;                    // formed in the keep-decision pass
+    const float ref = lse[j];
+    const float th = fmaxf(ref + ltau, -3.4028235e38f);
+    const float x = sv - ref;
+    return sv >= th ? (hw_exp ? ex2(x) : exp2f(x)) : 0.f;
+  };
   // a wave with at least 8 rows sums them on MFMA (wave-uniform choice)
   const bool use_mfma = VM::kOn && nmine >= 8;
   floatx4 vacc[8];
@@ -1171,7 +1241,7 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
           for (int i = 0; i < 4; ++i) {
             const int kk = k + 4 * g4 + i;
             okr[i] = kk < nmine;
-            w[i] = (okr[i] && hj < G) ? sc[hj * P + mylist[okr[i] ? kk : k]] : 0.f;
+            w[i] = (okr[i] && hj < G) ? weight(hj, mylist[okr[i] ? kk : k]) : 0.f;
             if (!lo_part) vmass += w[i];
           }
           float x[VM::kBlocks][4];
@@ -1224,7 +1294,7 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
           const int pr = mylist[k + u];
 #pragma unroll
           for (int j = 0; j < G; ++j) {
-            const float pj = sc[j * P + pr];        // same for every lane of the wave
+            const float pj = weight(j, pr);         // same for every lane of the wave
             o0[j] = fmaf(pj, v0, o0[j]);
             o1[j] = fmaf(pj, v1, o1[j]);
             mass[j] += pj;
@@ -1258,11 +1328,12 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   }
   if (use_mfma && lane < G) wmass[wave * G + lane] = vmass;
   __syncthreads();                                   // all waves done with sc
-  int wg_rows = 0, wg_kept = 0, nact = 0;
+  int wg_rows = 0, wg_kept = 0, wg_live = 0, nact = 0;
   uint32_t act = 0;                                  // waves that summed value rows
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
-    wg_rows += wrows[w];
+    wg_rows += wrows[w] & 0xFFFF;
+    wg_live += wrows[w] >> 16;
     wg_kept += wcount[w];
     if (wproc[w] > 0) act |= 1u << w;
   }
@@ -1340,7 +1411,10 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
       put_tagged_f(a.pmass + pbase * G + tid, epoch, poison_if(bad, s));
     }
   }
-  if (tid == 0) put_tagged(a.flags + pbase, epoch, (uint32_t(wg_rows) << 18) | uint32_t(wg_kept));
+  if (tid == 0) {
+    put_tagged(a.flags + pbase, epoch, (uint32_t(wg_rows) << 18) | uint32_t(wg_kept));
+    a.live[wg] = wg_live;                            // read by the host after the call
+  }
   stamp(a, 4);
 
   // ---------------------------------------------------------------- phase 4: merge

@@ -26,7 +26,7 @@ struct WsHeader {
   uint32_t groups_done;                 // groups past their LSE exchange in the running call (returns to 0)
   uint32_t status;                      // sticky device fault bits
   uint32_t pad0;
-  unsigned long long reserved2;
+  long long live_off;                   // byte offset of the per-workgroup live-tile counts (int32 [nwg])
   unsigned long long reserved3;
   int32_t batch, q_heads, kv_heads, ctx;
   int32_t splits, positions_per_split, fmt, v_dim;
@@ -48,6 +48,7 @@ struct WsLayout {
   int64_t flags;       // tagged [B*Hkv][S]: rows fetched << 18 | kept pairs of the split
   int64_t pmass;       // tagged [B*Hkv][S][G]: per-split kept mass
   int64_t partial;     // tagged [B*Hkv][S][G][Dv]: per-split partial outputs
+  int64_t live;        // int32 [B*Hkv][S]: 64-position chunks of the split holding a kept row
   int64_t total;
 };
 
@@ -65,6 +66,7 @@ inline WsLayout ws_layout(int B, int Hkv, int Hq, int S, int Dv) {
   w.flags = off;     off = align256(off + BG * S * 8);
   w.pmass = off;     off = align256(off + BG * S * G * 8);
   w.partial = off;   off = align256(off + BG * S * G * int64_t(Dv) * 8);
+  w.live = off;      off = align256(off + BG * S * 4);
   w.total = off;
   return w;
 }
@@ -96,6 +98,8 @@ struct GqaArgs {
   unsigned long long* times;      // optional [nwg][16] phase stamps
   uint32_t spin_limit;            // retries of a bounded wait
   int32_t withhold;               // test aid: split 0 of group 0 does not publish its statistics
+  int32_t* live;                  // [nwg] live 64-position chunks per workgroup
+  long long live_off;             // its byte offset in the workspace (recorded in the header)
 };
 
 // Arguments of the two MLA kernels.
@@ -129,10 +133,12 @@ struct MlaArgs {
   unsigned long long* times;      // optional [nwg][16] phase stamps of mla_scores
   uint32_t spin_limit;            // retries of a bounded wait
   int32_t withhold;               // test aid: split 0 of sequence 0 does not publish its statistics
+  int32_t* live;                  // [B][S] 32-position tiles each scores workgroup re-scored
+  long long live_off;             // its byte offset in the workspace (recorded in the header)
 };
 
 struct MlaLayout {
-  int64_t kept_mass, bgstat, split_ml, kcount, kpairs, kpos, kp, opart, mpart, ocnt, done, lseo, total;
+  int64_t kept_mass, bgstat, split_ml, kcount, kpairs, kpos, kp, opart, mpart, ocnt, done, lseo, live, total;
 };
 
 // The first two regions match ws_layout() so kvq_stats reads both families
@@ -157,6 +163,7 @@ inline MlaLayout mla_ws_layout(int B, int H, int S, int64_t SP, int R) {
   w.kp = off;        off = align256(off + int64_t(B) * SP * int64_t(H) * 4);
   w.opart = off;     off = align256(off + int64_t(B) * (H / 32) * 4 * R * 32 * 128 * 4);
   w.mpart = off;     off = align256(off + int64_t(B) * (H / 32) * R * 32 * 4);
+  w.live = off;      off = align256(off + int64_t(B) * S * 4);
   w.total = off;
   return w;
 }

@@ -458,6 +458,7 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
     a.hdr->nwg = int(gridDim.x);
     a.hdr->k_row_bytes = D + 4 * NGROUPS;               // a whole latent row
     a.hdr->v_row_bytes = DV + 4 * (DV / 128);           // its value part
+    a.hdr->live_off = a.live_off;
   }
 
   const TileSrc<NW> src(a.kc + row0 * D, reinterpret_cast<const float*>(a.ks) + row0 * NGROUPS, ctx, wave, lane);
@@ -627,6 +628,7 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
     if (tid == 0) {
       a.kcount[kb] = nv;
       a.kpairs[kb] = nv * H;
+      a.live[kb] = (nv + TILE - 1) / TILE;             // every tile holds kept rows
     }
     stamp_mla(a, 4);
     return;
@@ -808,6 +810,7 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
   if (tid == 0) {
     a.kcount[kbase] = int32_t(uint32_t(nkept) | (sbad ? kCountPoison : 0u));
     a.kpairs[kbase] = misc[2];
+    a.live[kbase] = n3;                                // tiles re-scored (those that could keep a row)
   }
   stamp_mla(a, 4);
 }

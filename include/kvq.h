@@ -284,6 +284,10 @@ typedef struct kvq_stats_t {
   int32_t splits;          /* context splits per (batch, kv head) used */
   int32_t batch;
   int32_t q_heads;
+  int64_t live_tiles;      /* grouped formats: 64-position chunks holding a row kept by some head
+                              (the chunks whose value rows are read); fp8 latent: 32-position
+                              tiles re-scored because their score maximum could reach the
+                              threshold (a superset of the tiles holding kept rows) */
 } kvq_stats_t;
 
 /* Statistics of the last kvq_decode_attn on this workspace. Synchronizes

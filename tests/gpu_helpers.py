@@ -100,4 +100,21 @@ def compare(inp, threshold, g, r, planes_o, *, check_stats=True, mask=True):
         assert abs(st["kept_pairs"] - r.kept_pairs) <= nb, (st["kept_pairs"], r.kept_pairs)
         assert abs(st["rows_fetched"] - r.rows_fetched) <= nb, (st["rows_fetched"], r.rows_fetched)
         assert np.allclose(st["kept_mass"], r.kept_mass, rtol=0, atol=1e-5)
+        if inp.v is not None:
+            # grouped formats: the 64-position chunks holding a kept row
+            want = live_chunks(r.union, 64)
+            assert abs(st["live_tiles"] - want) <= nb, (st["live_tiles"], want)
+        else:
+            # latent: the re-scored 32-position tiles include every tile with a kept row
+            lo, hi = live_chunks(r.union, 32), live_chunks(np.ones_like(r.union), 32)
+            assert lo <= st["live_tiles"] <= hi + r.union.shape[0] * 2, (st["live_tiles"], lo, hi)
     return err, rel
+
+
+def live_chunks(union, width):
+    """Chunks of `width` positions (aligned to position 0) holding a row of the
+    union mask, summed over [B][Hkv]."""
+    B, H, n = union.shape
+    pad = (-n) % width
+    u = np.pad(union, ((0, 0), (0, 0), (0, pad)))
+    return int(u.reshape(B, H, -1, width).any(axis=-1).sum())
