@@ -366,6 +366,7 @@ extern "C" int32_t kvq_decode_attn(const void* q, const kvq_cache* kcache, const
   a.lse = reinterpret_cast<unsigned long long*>(ws + plan.ws.lse);
   a.split_ml = reinterpret_cast<unsigned long long*>(ws + plan.ws.split_ml);
   a.flags = reinterpret_cast<unsigned long long*>(ws + plan.ws.flags);
+  a.act = reinterpret_cast<unsigned long long*>(ws + plan.ws.act);
   a.pmass = reinterpret_cast<unsigned long long*>(ws + plan.ws.pmass);
   a.partial = reinterpret_cast<unsigned long long*>(ws + plan.ws.partial);
   a.live = reinterpret_cast<int32_t*>(ws + plan.ws.live);

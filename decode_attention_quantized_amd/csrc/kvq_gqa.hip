@@ -667,7 +667,8 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   float* wmass = reinterpret_cast<float*>(wrows + kWaves);        // [kWaves][G]
   float2* wml = reinterpret_cast<float2*>(wmass + kWaves * G);    // [kWaves][8] per-wave (max, sum)
   int* wproc = reinterpret_cast<int*>(wml + kWaves * 8);          // [kWaves] value rows each wave summed
-  int* wto = wproc + kWaves;                                      // [4]: [0] a wait of this workgroup gave up
+  int* wto = wproc + kWaves;                                      // [4]: [0] a wait of this workgroup gave up,
+                                                                  // [1] a head of the group keeps a row here
   unsigned long long* umask = reinterpret_cast<unsigned long long*>(wproc + kWaves + 4);  // [P/64] union keep bits
   // per-wave lists of the kept rows a wave fetches: [kWaves][32 * ceil(P/64 / (kWaves/2))]
   uint16_t* rowlist = reinterpret_cast<uint16_t*>(umask + (P / kChunk));
@@ -679,7 +680,10 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // the wave index is uniform across the wave: taken as a scalar, every
+  // tile index and loop bound derived from it stays scalar (no exec-masked
+  // branches around uniform per-tile tests)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wg = blockIdx.x;
   const int bg = wg / a.S;                  // b * Hkv + g
   const int split = wg - bg * a.S;
@@ -759,7 +763,7 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     a.hdr->live_off = a.live_off;
   }
   for (int c = tid; c < P / kChunk; c += kThreads) umask[c] = 0ull;
-  if (tid == 0) wto[0] = 0;
+  if (tid == 0) wto[0] = wto[1] = 0;
   if (kLut3 && tid < 64) lut3_tab[tid] = lut3_pair_entry(tid);
   // q of this group: per-head max |q| -> power-of-two prescale, then fp16 hi/lo rows
   float qv[4];
@@ -1080,7 +1084,10 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
           uni |= bal[jj];
           kept_cnt += __popcll(bal[jj]);
         }
-        if (lane == 0 && uni) atomicOr(&umask[c], uni);
+        if (lane == 0 && uni) {
+          atomicOr(&umask[c], uni);
+          wto[1] = 1;
+        }
         if constexpr (RUN) {
           // single-pass rule: the running LSE of the blocks lives in the K
           // staging strip, which the value pass reuses, so the weights
@@ -1105,6 +1112,14 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   }
   stamp(a, 7);
   __syncthreads();
+  // Whether this split will publish a partial output, published at once:
+  // the merge reads it with the partials and skips the partial of a split
+  // that keeps nothing (which never writes one). A split whose wait gave up
+  // publishes its NaN partial; under the single-pass rule every split
+  // publishes (its factor to the group's LSE is only known later).
+  const int64_t pbase = int64_t(bg) * a.S + split;
+  const bool publishes = RUN || wto[0] != 0 || wto[1] != 0;
+  if (tid == 0) put_tagged(a.act + pbase, epoch, publishes ? 1u : 0u);
   uint16_t* mylist = rowlist + wave * list_cap;
   int nmine = 0, rows_cnt = 0;                       // rows_cnt: rows | live chunks << 16
   for (int c0 = pair; c0 < nchunks; c0 += 4 * (kWaves / 2)) {
@@ -1338,7 +1353,6 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     if (wproc[w] > 0) act |= 1u << w;
   }
   nact = __popc(act);
-  const int64_t pbase = int64_t(bg) * a.S + split;
   float* fac = qmax;                                  // single-pass rule: per-head factor to the group LSE
   if constexpr (RUN) {
     // every workgroup takes part (the exchange also proves to the epoch
@@ -1350,9 +1364,11 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   // a wait of this workgroup gave up (its statistics and weights are not the
   // call's): publish NaN, so every sum that uses them is NaN as well
   const bool bad = wto[0] != 0;
-  if (nact == 0) {                                    // uniform: nothing kept, publish zeros
-    for (int i = tid; i < G * 128; i += kThreads)
-      put_tagged_f(a.partial + pbase * G * 128 + i, epoch, poison_if(bad, 0.f));
+  if (nact == 0) {                                    // uniform: nothing kept
+    // zeros (NaN after a wait gave up) only where the merge expects a partial
+    if (publishes)
+      for (int i = tid; i < G * 128; i += kThreads)
+        put_tagged_f(a.partial + pbase * G * 128 + i, epoch, poison_if(bad, 0.f));
     if (tid < G) put_tagged_f(a.pmass + pbase * G + tid, epoch, poison_if(bad, 0.f));
   } else {
     // the partials of the waves that summed rows meet in LDS and are added in
@@ -1419,11 +1435,12 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
 
   // ---------------------------------------------------------------- phase 4: merge
   // Workgroup `split` of the group sums the slice [split*E, split*E + E) of
-  // the group's G*128 outputs over all splits (a split without kept rows
-  // published zeros) in ascending split order, which is deterministic, and
-  // the kept mass of heads split, split+S, ... ; split 0 also sums the
-  // group's counters. All words are read in one batch and stale ones are
-  // re-read together.
+  // the group's G*128 outputs over all splits (a split that keeps no row
+  // publishes no partial and counts as zeros) in ascending split order,
+  // which is deterministic, and the kept mass of heads split, split+S, ... ;
+  // split 0 also sums the group's counters. All words are read in one batch
+  // and stale ones are re-read together; a partial piece is waited for only
+  // when its split's early word says it publishes one.
   {
     constexpr int NE = G * 128;
     const int S = a.S;
@@ -1444,9 +1461,10 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     const int sp_p = use_p ? tid / (hc > 0 ? hc : 1) : 0;
     const int k_p = use_p ? tid - sp_p * hc : 0;
     const __amdgpu_buffer_rsrc_t rp = coherent_rsrc(a.partial + gb * NE, S * NE * 8);
-    const int poff[1] = {(sp_p * NE + e0 + 2 * k_p) * 8};
-    const bool puse[1] = {use_p};
-    u32x4 pw[1] = {use_p ? peek2(rp, poff[0]) : u32x4{0u, epoch, 0u, epoch}};
+    const int poff = (sp_p * NE + e0 + 2 * k_p) * 8;
+    u32x4 pw = use_p ? peek2(rp, poff) : u32x4{0u, epoch, 0u, epoch};
+    const u64* asrc = a.act + gb + sp_p;
+    u64 aw = use_p ? peek(asrc) : (u64(epoch) << 32) | 1u;
     constexpr int NW = 2 + 2;                        // mass and flag words per thread
     u64 w[NW];
     const u64* src[NW];
@@ -1468,15 +1486,38 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     uint32_t prev = 0;
     const bool counts = master && tid == 0;
     if (counts) prev = __hip_atomic_fetch_add(&a.hdr->groups_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (settle_mixed(pw, puse, rp, poff, w, src, use, epoch, a.hdr, a.spin_limit)) wto[0] = 1;
+    {
+      // settle: the split's early word, then its piece if it publishes one,
+      // plus the mass and flag words (bounded like settle_mixed)
+      uint32_t spins = 0;
+      while (true) {
+        const bool afresh = uint32_t(aw >> 32) == epoch;
+        bool stale = !afresh || (uint32_t(aw) != 0u && stale2(pw, epoch));
+#pragma unroll
+        for (int k = 0; k < NW; ++k) stale |= use[k] && uint32_t(w[k] >> 32) != epoch;
+        if (!stale) break;
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > a.spin_limit) {
+          __hip_atomic_fetch_or(&a.hdr->status, kStatusWaitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          wto[0] = 1;
+          break;
+        }
+        if (!afresh) aw = peek(asrc);
+        else if (uint32_t(aw) != 0u && stale2(pw, epoch)) pw = peek2(rp, poff);
+#pragma unroll
+        for (int k = 0; k < NW; ++k)
+          if (use[k] && uint32_t(w[k] >> 32) != epoch) w[k] = peek(src[k]);
+      }
+      if (uint32_t(aw) == 0u) pw = u32x4{0u, epoch, 0u, epoch};   // no partial: zeros
+    }
     if (counts && prev == uint32_t(a.B * a.Hkv) - 1) {
       __hip_atomic_store(&a.hdr->groups_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&a.hdr->epoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     stamp(a, 5);
     if (use_p) {
-      pv[(2 * k_p) * S + sp_p] = __uint_as_float(pw[0].x);
-      pv[(2 * k_p + 1) * S + sp_p] = __uint_as_float(pw[0].z);
+      pv[(2 * k_p) * S + sp_p] = __uint_as_float(pw.x);
+      pv[(2 * k_p + 1) * S + sp_p] = __uint_as_float(pw.z);
     }
 #pragma unroll
     for (int k = 0; k < 2; ++k) {

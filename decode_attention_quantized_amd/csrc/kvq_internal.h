@@ -46,6 +46,7 @@ struct WsLayout {
   int64_t lse;         // tagged [B*Hkv][G]: log2-domain log-sum-exp per head
   int64_t split_ml;    // tagged [B*Hkv][S][G][2]: per-split (max, sum) in the log2 domain
   int64_t flags;       // tagged [B*Hkv][S]: rows fetched << 18 | kept pairs of the split
+  int64_t act;         // tagged [B*Hkv][S]: 1 if the split publishes a partial output (it keeps a row)
   int64_t pmass;       // tagged [B*Hkv][S][G]: per-split kept mass
   int64_t partial;     // tagged [B*Hkv][S][G][Dv]: per-split partial outputs
   int64_t live;        // int32 [B*Hkv][S]: 64-position chunks of the split holding a kept row
@@ -64,6 +65,7 @@ inline WsLayout ws_layout(int B, int Hkv, int Hq, int S, int Dv) {
   w.lse = off;       off = align256(off + BG * G * 8);
   w.split_ml = off;  off = align256(off + BG * S * G * 16);
   w.flags = off;     off = align256(off + BG * S * 8);
+  w.act = off;       off = align256(off + BG * S * 8);
   w.pmass = off;     off = align256(off + BG * S * G * 8);
   w.partial = off;   off = align256(off + BG * S * G * int64_t(Dv) * 8);
   w.live = off;      off = align256(off + BG * S * 4);
@@ -86,6 +88,7 @@ struct GqaArgs {
   unsigned long long* lse;        // tagged
   unsigned long long* split_ml;   // tagged
   unsigned long long* flags;      // tagged
+  unsigned long long* act;        // tagged
   unsigned long long* pmass;      // tagged
   unsigned long long* partial;    // tagged
   int32_t B, Hkv, Hq, ctx, cap;
