@@ -344,7 +344,7 @@ def run_config(w, steps, warmup, splits=0, modes=("sparse", "dense"), single_pas
         line["single_pass"]["extra_rows_vs_exact"] = (res["single_pass"]["stats"]["rows_fetched"]
                                                       - res["sparse"]["stats"]["rows_fetched"])
     torch.cuda.synchronize()
-    del att, caches, K0, V0, q, out
+    del att, caches, K0, V0, q, out, stream
     return line
 
 
@@ -362,6 +362,16 @@ def lut3_object(steps, warmup):
                         "kernel_us_mean": sp["kernel_us_mean"],
                         "timing": "HIP events around one graph replay of the timed steps, on the launch stream"}
     line["dense"]["traffic"] = load_traffic("dense", "lut3")
+    # the same bytes read by the plain streaming kernel, on the call's grid and
+    # swept: the floor a read of this size reaches
+    import torch
+    stream = torch.cuda.Stream()
+    sref = stream_reference(sp["algorithmic_bytes"], int(line["splits"]) * w.batch * w.kv_heads, steps, warmup,
+                            stream)
+    sref["decode_kernel_over_floor"] = round(sp["kernel_us_mean"] / sref["floor"]["us_per_launch"], 3)
+    line["stream_read_same_bytes"] = sref
+    torch.cuda.synchronize()
+    del stream
     return line
 
 
