@@ -48,7 +48,8 @@ class kvq_stats_t(ctypes.Structure):
     _fields_ = [("positions", ctypes.c_int64), ("pairs", ctypes.c_int64), ("kept_pairs", ctypes.c_int64),
                 ("rows_fetched", ctypes.c_int64), ("k_bytes", ctypes.c_int64), ("v_bytes", ctypes.c_int64),
                 ("v_bytes_dense", ctypes.c_int64), ("status", ctypes.c_int32), ("splits", ctypes.c_int32),
-                ("batch", ctypes.c_int32), ("q_heads", ctypes.c_int32), ("live_tiles", ctypes.c_int64)]
+                ("batch", ctypes.c_int32), ("q_heads", ctypes.c_int32), ("live_tiles", ctypes.c_int64),
+                ("launches", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 EXPORTS = ["kvq_row_bytes", "kvq_pack", "kvq_unpack", "kvq_lut3_levels", "kvq_append", "kvq_append_kv",

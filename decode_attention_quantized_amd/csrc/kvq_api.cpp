@@ -58,6 +58,7 @@ struct Plan {
   int threads = 0;
   int R = 1;                                              // latent output: row ranges per block
   int tpe = 2;                                            // latent scores: 32-position tiles per tile maximum
+  int gpl = 0, nsub = 1;                                  // grouped plans: groups per launch, launches
   WsLayout ws{};
   kvq::MlaLayout mws{};
   int64_t total = 0;
@@ -139,40 +140,51 @@ int32_t make_plan(int32_t fmt, const kvq_cache* k, const kvq_launch* l, int32_t 
   if (di.cus <= 0) return KVQ_ERR_LAUNCH;
 
   const int64_t BG = int64_t(k->batch) * k->heads;
-  int S;
-  if (l->splits > 0) {
-    S = l->splits;
-  } else {
-    const int64_t target = di.cus;                        // one 16-wave workgroup per CU
-    int64_t s = target / BG;
-    if (s < 1) s = 1;
-    const int64_t most = (ctx_len + kvq::kChunk - 1) / kvq::kChunk;
-    if (s > most) s = most;
-    S = int(s);
-  }
-  int P = (ctx_len + S - 1) / S;
-  P = (P + kvq::kChunk - 1) / kvq::kChunk * kvq::kChunk;
-  S = (ctx_len + P - 1) / P;                             // drop splits that would be empty
-  if (P > 8192) return KVQ_ERR_UNSUPPORTED;              // per-split counts are packed in 14/18 bits
-  if (S > 2048 || BG * S > (int64_t(1) << 30)) return KVQ_ERR_UNSUPPORTED;
-  // limits of the in-kernel exchanges (each thread reads at most two of the
-  // group's split statistics, one 16-byte piece of partial outputs and two
-  // kept-mass and flag words)
-  {
+  // All workgroups of a launch must be resident (one per CU) and a split's
+  // scores must fit in LDS. A call whose groups (sequence, kv head) do not
+  // fit one launch under both limits runs in several launches on the stream,
+  // each over an equal share of the groups with the splits refilling the CUs
+  // (fewer groups per launch: more splits, fewer positions per split).
+  int S = 0, P = 0;
+  int64_t gpl = BG;                                       // groups per launch
+  size_t lds = 0;
+  for (int64_t nsub = 1;; ++nsub) {
+    gpl = (BG + nsub - 1) / nsub;
+    if (nsub > 1 && (BG + gpl - 1) / gpl < nsub) continue;   // same share as a smaller count
+    if (l->splits > 0) {
+      S = l->splits;
+    } else {
+      int64_t s = di.cus / gpl;
+      if (s < 1) s = 1;
+      const int64_t most = (ctx_len + kvq::kChunk - 1) / kvq::kChunk;
+      if (s > most) s = most;
+      S = int(s);
+    }
+    P = (ctx_len + S - 1) / S;
+    P = (P + kvq::kChunk - 1) / kvq::kChunk * kvq::kChunk;
+    S = (ctx_len + P - 1) / P;                           // drop splits that would be empty
+    // P <= 8192: per-split counts are packed in 14/18 bits; the in-kernel
+    // exchanges read at most two of the group's split statistics, one
+    // 16-byte piece of partial outputs and two kept-mass and flag words per
+    // thread
     const int64_t E = kvq::gqa_merge_slice(G, S);
     const int64_t nh = S >= G ? 1 : (G + S - 1) / S;
-    if (int64_t(S) * G > 2 * kvq::kThreads || (E / 2) * S > kvq::kThreads || nh * S > 2 * kvq::kThreads)
-      return KVQ_ERR_UNSUPPORTED;
+    const bool fits = P <= 8192 && S <= 2048 && BG * S <= (int64_t(1) << 30) && gpl * S <= di.cus &&
+                      int64_t(S) * G <= 2 * kvq::kThreads && (E / 2) * S <= kvq::kThreads &&
+                      nh * S <= 2 * kvq::kThreads;
+    lds = fits ? kvq::gqa_lds_bytes(fmt, G, P, S) : 0;
+    if (fits && lds <= size_t(di.max_lds)) break;
+    if (gpl == 1) return KVQ_ERR_UNSUPPORTED;               // one group alone does not fit
   }
-  const size_t lds = kvq::gqa_lds_bytes(fmt, G, P, S);
-  if (lds > size_t(di.max_lds)) return KVQ_ERR_UNSUPPORTED;
 
   plan->S = S;
   plan->P = P;
   plan->G = G;
   plan->Dv = 128;
   plan->lds = lds;
-  plan->nwg = int(BG * S);
+  plan->gpl = int(gpl);
+  plan->nsub = int((BG + gpl - 1) / gpl);
+  plan->nwg = int(gpl * S);                               // workgroups of a (full) launch
   plan->threads = kvq::kThreads;
   plan->ws = kvq::ws_layout(k->batch, k->heads, l->q_heads, S, plan->Dv);
   plan->total = plan->ws.total;
@@ -319,8 +331,9 @@ extern "C" int32_t kvq_workspace_bytes(int32_t fmt, const kvq_cache* kcache, con
     const kvq::MlaLayout w = kvq::mla_ws_layout(kcache->batch, plan.G, int(s_up), sp_up, plan.R);
     *bytes = std::max(plan.total, w.total);
   } else {
-    const int64_t bg = int64_t(kcache->batch) * kcache->heads;
-    const int64_t s_up = l->splits > 0 ? l->splits : std::min(std::max<int64_t>(1, cus / bg), chunks);
+    // a shorter context needs at most as many launches, so at least as many
+    // groups per launch and at most as many splits
+    const int64_t s_up = l->splits > 0 ? l->splits : std::min(std::max<int64_t>(1, cus / plan.gpl), chunks);
     const kvq::WsLayout w = kvq::ws_layout(kcache->batch, kcache->heads, l->q_heads, int(s_up), plan.Dv);
     *bytes = std::max(plan.total, w.total);
   }
@@ -395,10 +408,18 @@ extern "C" int32_t kvq_decode_attn(const void* q, const kvq_cache* kcache, const
   int dev = 0;
   (void)hipGetDevice(&dev);
   if (int64_t(per_cu) * device_info(dev).cus < plan.nwg) return KVQ_ERR_UNSUPPORTED;
-  const hipError_t e = launch(kern, plan.nwg, kvq::kThreads, &a, plan.lds, l);
-  if (e != hipSuccess) {
-    (void)hipGetLastError();
-    return KVQ_ERR_LAUNCH;
+  // one launch per share of the groups, in order on the caller's stream
+  // (each finishes before the next starts and advances the epoch)
+  const int BG = kcache->batch * kcache->heads;
+  a.launches = plan.nsub;
+  for (int bg0 = 0; bg0 < BG; bg0 += plan.gpl) {
+    a.bg0 = bg0;
+    a.ngroups = std::min(plan.gpl, BG - bg0);
+    const hipError_t e = launch(kern, a.ngroups * plan.S, kvq::kThreads, &a, plan.lds, l);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return KVQ_ERR_LAUNCH;
+    }
   }
   return KVQ_OK;
 }
@@ -449,6 +470,7 @@ extern "C" int32_t kvq_stats(const kvq_launch* l, kvq_stats_t* out, float* kept_
     for (int32_t v : lv) out->live_tiles += v;
   }
   out->status = int32_t(h.status);
+  out->launches = int32_t(h.launches);
   out->splits = h.splits;
   out->batch = h.batch;
   out->q_heads = h.q_heads;

@@ -40,8 +40,10 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 
+// phase stamps are kept per workgroup of the whole call: a launch covers the
+// groups bg0 .. bg0 + ngroups - 1, so its workgroup i is number bg0 * S + i
 __device__ inline void stamp(const GqaArgs& a, int k) {
-  if (a.times && threadIdx.x == 0) a.times[int64_t(blockIdx.x) * 16 + k] = wall_clock64();
+  if (a.times && threadIdx.x == 0) a.times[(int64_t(a.bg0) * a.S + blockIdx.x) * 16 + k] = wall_clock64();
 }
 
 // 2^x with the hardware instruction (results below the normal range flush
@@ -684,9 +686,9 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   // tile index and loop bound derived from it stays scalar (no exec-masked
   // branches around uniform per-tile tests)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wg = blockIdx.x;
-  const int bg = wg / a.S;                  // b * Hkv + g
-  const int split = wg - bg * a.S;
+  const int bg = a.bg0 + int(blockIdx.x) / a.S;   // b * Hkv + g
+  const int split = int(blockIdx.x) - (bg - a.bg0) * a.S;
+  const int wg = bg * a.S + split;                 // workgroup number within the whole call
   const bool master = split == 0;                  // advances the epoch for its group
   const int b = bg / a.Hkv;
   const int g = bg - b * a.Hkv;
@@ -754,10 +756,11 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   __asm__ volatile("" ::: "memory");
 
   // ---------------------------------------------------------------- setup
-  if (wg == 0 && tid == 0) {
+  if (blockIdx.x == 0 && tid == 0) {
     a.hdr->batch = a.B; a.hdr->q_heads = a.Hq; a.hdr->kv_heads = a.Hkv; a.hdr->ctx = ctx;
     a.hdr->splits = a.S; a.hdr->positions_per_split = P; a.hdr->fmt = FMT; a.hdr->v_dim = 128;
-    a.hdr->nwg = int(gridDim.x);
+    a.hdr->nwg = a.B * a.Hkv * a.S;
+    a.hdr->launches = a.launches;
     a.hdr->k_row_bytes = T::CB + T::SB;
     a.hdr->v_row_bytes = T::CB + T::SB;
     a.hdr->live_off = a.live_off;
@@ -798,46 +801,54 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(qv[e]));
     }
+    // The 32 threads of a head are one half of a wave: the butterfly leaves
+    // the head's max |q| in each of them, so the prescale, the fp16 hi/lo
+    // rows and their bias sums are formed without a barrier. A thread's four
+    // dims lie in one scale block; the blocks of the biased formats (q4_0,
+    // q8_0) are dims 32bb .. 32bb + 31, the threads ln = 8bb .. 8bb + 7.
     if (j < 8) {
 #pragma unroll
       for (int o = 16; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 32));
-      if (j < G && ln == 0) qmax[j] = m;
-    }
-  }
-  __syncthreads();
-  {
-    const int j = tid >> 5, ln = tid & 31;
-    if (j < G) {
-      const float m = qmax[j];
-      const int ex = (m > 0.f) ? ilogbf(m) + 1 : 0;           // m * 2^-ex in [0.5, 1)
-      if (ln == 0) hs[j] = ldexpf(a.sigma_log2e, ex) * T::kRowMul;
+      float shi = 0.f, slo = 0.f;                             // this thread's part of the bias sums
+      if (j < G) {
+        const int ex = (m > 0.f) ? ilogbf(m) + 1 : 0;         // m * 2^-ex in [0.5, 1)
+        if (ln == 0) hs[j] = ldexpf(a.sigma_log2e, ex) * T::kRowMul;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int d = ln * 4 + e;
-        const float qs = ldexpf(qv[e], -ex);
-        const _Float16 hi = _Float16(qs);
-        const _Float16 lo = _Float16(qs - float(hi));
-        int bb, kk, slot;
-        T::locate(d, bb, kk, slot);
-        qop[((2 * j) * 16 + bb * 4 + kk) * 8 + slot] = hi;
-        qop[((2 * j + 1) * 16 + bb * 4 + kk) * 8 + slot] = lo;
+        for (int e = 0; e < 4; ++e) {
+          const int d = ln * 4 + e;
+          const float qs = ldexpf(qv[e], -ex);
+          const _Float16 hi = _Float16(qs);
+          const _Float16 lo = _Float16(qs - float(hi));
+          int bb, kk, slot;
+          T::locate(d, bb, kk, slot);
+          qop[((2 * j) * 16 + bb * 4 + kk) * 8 + slot] = hi;
+          qop[((2 * j + 1) * 16 + bb * 4 + kk) * 8 + slot] = lo;
+          shi += float(hi);
+          slo += float(lo);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int d = ln * 4 + e;
+          const int bb = d >> 5, kk = (d >> 3) & 3;
+          const int slot = d & 7;
+          qop[((2 * j) * 16 + bb * 4 + kk) * 8 + slot] = _Float16(0.f);
+          qop[((2 * j + 1) * 16 + bb * 4 + kk) * 8 + slot] = _Float16(0.f);
+        }
       }
-    } else if (j < 8) {
-      for (int e = 0; e < 4; ++e) {
-        const int d = ln * 4 + e;
-        const int bb = d >> 5, kk = (d >> 3) & 3;
-        const int slot = d & 7;
-        qop[((2 * j) * 16 + bb * 4 + kk) * 8 + slot] = _Float16(0.f);
-        qop[((2 * j + 1) * 16 + bb * 4 + kk) * 8 + slot] = _Float16(0.f);
+      if constexpr (T::kBias != 0.f) {
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1) {
+          shi += __shfl_xor(shi, o, 32);
+          slo += __shfl_xor(slo, o, 32);
+        }
+      }
+      if ((ln & 7) == 0) {                                    // bias correction per (block, row)
+        const int bb = ln >> 3;
+        cst[bb * 16 + 2 * j] = -T::kBias * shi;
+        cst[bb * 16 + 2 * j + 1] = -T::kBias * slo;
       }
     }
-  }
-  __syncthreads();
-  if (tid < 64) {                                // bias correction per (block, row)
-    const int bb = tid >> 4, m = tid & 15;
-    float s = 0.f;
-    for (int k = 0; k < 32; ++k) s += float(qop[(m * 16 + bb * 4 + (k >> 3)) * 8 + (k & 7)]);
-    cst[bb * 16 + m] = -T::kBias * s;
   }
   __syncthreads();
 
@@ -1510,7 +1521,7 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
       }
       if (uint32_t(aw) == 0u) pw = u32x4{0u, epoch, 0u, epoch};   // no partial: zeros
     }
-    if (counts && prev == uint32_t(a.B * a.Hkv) - 1) {
+    if (counts && prev == uint32_t(a.ngroups) - 1) {
       __hip_atomic_store(&a.hdr->groups_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&a.hdr->epoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }

@@ -25,7 +25,7 @@ struct WsHeader {
   uint32_t epoch;                       // tag of the last call (0 in a fresh workspace)
   uint32_t groups_done;                 // groups past their LSE exchange in the running call (returns to 0)
   uint32_t status;                      // sticky device fault bits
-  uint32_t pad0;
+  uint32_t launches;                    // kernel launches of the last call (the grouped plans may need several)
   long long live_off;                   // byte offset of the per-workgroup live-tile counts (int32 [nwg])
   unsigned long long reserved3;
   int32_t batch, q_heads, kv_heads, ctx;
@@ -103,6 +103,8 @@ struct GqaArgs {
   int32_t withhold;               // test aid: split 0 of group 0 does not publish its statistics
   int32_t* live;                  // [nwg] live 64-position chunks per workgroup
   long long live_off;             // its byte offset in the workspace (recorded in the header)
+  int32_t bg0, ngroups;           // this launch covers groups bg0 .. bg0 + ngroups - 1 (of B * Hkv)
+  int32_t launches;               // launches of the call
 };
 
 // Arguments of the two MLA kernels.

@@ -459,6 +459,7 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
     a.hdr->k_row_bytes = D + 4 * NGROUPS;               // a whole latent row
     a.hdr->v_row_bytes = DV + 4 * (DV / 128);           // its value part
     a.hdr->live_off = a.live_off;
+    a.hdr->launches = 2;                             // the scores kernel, then one output kernel
   }
 
   const TileSrc<NW> src(a.kc + row0 * D, reinterpret_cast<const float*>(a.ks) + row0 * NGROUPS, ctx, wave, lane);

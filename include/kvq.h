@@ -247,7 +247,15 @@ int32_t kvq_workspace_bytes(int32_t fmt, const kvq_cache* kcache, const kvq_laun
  *  out      device float32 [batch][q_heads][value dim]
  * Asynchronous on l->stream; returns after enqueueing. Errors: ARG, ALIGN,
  * RANGE, WORKSPACE, UNSUPPORTED (shape outside the built kernels), LAUNCH.
- * Device-side faults are reported by kvq_stats. */
+ * Device-side faults are reported by kvq_stats.
+ * Grouped formats: one launch holds at most one workgroup per compute unit
+ * and keeps a split's scores (q_heads/kv_heads * positions per split floats)
+ * in LDS. A call whose batch * kv_heads groups do not fit one launch under
+ * both limits is enqueued as several launches on l->stream, each over an
+ * equal share of the groups (in group order) with more splits per group;
+ * kvq_stats.launches reports how many. UNSUPPORTED only when one group alone
+ * does not fit (about 1.1 million positions at 8 query heads per kv head).
+ * If a launch fails to enqueue, earlier launches of the call may have run. */
 int32_t kvq_decode_attn(const void* q, const kvq_cache* kcache, const kvq_cache* vcache,
                         int32_t fmt, int32_t ctx_len, float threshold, float* out,
                         const kvq_launch* l);
@@ -288,6 +296,10 @@ typedef struct kvq_stats_t {
                               (the chunks whose value rows are read); fp8 latent: 32-position
                               tiles re-scored because their score maximum could reach the
                               threshold (a superset of the tiles holding kept rows) */
+  int32_t launches;        /* kernel launches of the call: grouped formats run in several when
+                              one launch cannot hold every group (see kvq_decode_attn); the
+                              fp8 latent path always uses two (scores, then output) */
+  int32_t reserved;
 } kvq_stats_t;
 
 /* Statistics of the last kvq_decode_attn on this workspace. Synchronizes

@@ -169,6 +169,32 @@ def test_lut3_full_size(name, threshold):
     compare(inp, tau, g, r, po)
 
 
+@pytest.mark.parametrize("threshold", [None, 0.0])
+def test_lut3_batch_over_one_launch(threshold):
+    """Batch 8 x 4 kv heads at ctx 40000: 8 splits of 5056 positions per
+    group would not fit their scores in LDS, so the call runs as two
+    launches of 16 groups with 16 splits each."""
+    say("case lut3 batch 8, 32/4 heads, ctx 40000 (two launches), threshold",
+        "of the workload" if threshold is None else threshold)
+    inp, tau = _case("lut3", threshold, ctx=40000)
+    g = run_gpu(inp, tau)
+    assert g["stats"]["launches"] == 2 and g["stats"]["splits"] == 16, g["stats"]
+    r, po = oracle_for(inp, tau)
+    compare(inp, tau, g, r, po)
+
+
+@pytest.mark.parametrize("threshold", [1e-6, 0.0])
+def test_more_groups_than_compute_units(threshold):
+    """72 sequences x 4 kv heads = 288 groups, more than one workgroup per
+    compute unit allows in one launch: two launches of 144 groups."""
+    say("case q4_0 batch 72, 32/4 heads, ctx 1000 (two launches), tau", threshold)
+    inp, tau = _case("long", threshold, batch=72, ctx=1000, hot=4)
+    g = run_gpu(inp, tau)
+    assert g["stats"]["launches"] == 2, g["stats"]
+    r, po = oracle_for(inp, tau)
+    compare(inp, tau, g, r, po)
+
+
 @pytest.mark.parametrize("name,heads,threshold", [("long", None, 1e-6), ("long", None, 0.0), ("mla", 32, 0.0),
                                                   ("mla", 128, 0.0), ("mla", 64, 1e-6)])
 def test_one_workspace_for_shorter_contexts(name, heads, threshold):

@@ -13,7 +13,9 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("fmt,batch,kv_heads,q_heads,dim,v_dim,cap", [
     ("q4_0", 1, 4, 32, 128, 0, 70001),      # the long shape, one split per CU
-    ("lut3", 8, 4, 32, 128, 0, 32768),      # the LUT3 batch at its largest supported context
+    ("lut3", 8, 4, 32, 128, 0, 32768),      # the LUT3 batch at its largest one-launch context
+    ("lut3", 8, 4, 32, 128, 0, 40000),      # ... and past it (two launches)
+    ("q4_0", 72, 4, 32, 128, 0, 5000),      # more groups than compute units (several launches)
     ("q8_0", 1, 1, 4, 128, 0, 9000),
     ("fp8_b128", 8, 1, 128, 576, 512, 70001),
     ("fp8_b128", 1, 1, 32, 576, 512, 30000),
@@ -28,8 +30,8 @@ def test_workspace_size_covers_every_shorter_context(fmt, batch, kv_heads, q_hea
     f = B.FMT[fmt]
     top = kvq.kvq_workspace_bytes(f, k, launch, cap)
     rng = np.random.default_rng(cap)
-    probes = sorted(set([1, 2, 63, 64, 65, 127, 128, 129, cap - 1, cap] + list(range(4032, 4224)) +
-                        rng.integers(1, cap + 1, 3000).tolist()))
+    probes = sorted(n for n in set([1, 2, 63, 64, 65, 127, 128, 129, cap - 1, cap] + list(range(4032, 4224)) +
+                                   rng.integers(1, cap + 1, 3000).tolist()) if n <= cap)
     worst = 0
     for n in probes:
         b = kvq.kvq_workspace_bytes(f, k, launch, int(n))
