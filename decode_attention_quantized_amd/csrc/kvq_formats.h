@@ -147,6 +147,66 @@ KVQ_HD inline void wht128(double* y) {
   for (int i = 0; i < 128; ++i) y[i] = y[i] * kWhtScale;
 }
 
+// Little-endian loads from byte planes.
+KVQ_HD inline uint16_t ld_u16(const uint8_t* p) { return uint16_t(p[0] | (p[1] << 8)); }
+KVQ_HD inline float ld_f32(const uint8_t* p) {
+  const uint32_t u = uint32_t(p[0]) | (uint32_t(p[1]) << 8) | (uint32_t(p[2]) << 16) | (uint32_t(p[3]) << 24);
+  float f;
+  __builtin_memcpy(&f, &u, 4);
+  return f;
+}
+
+// Element i of a dequantized row in float64 for the formats whose elements
+// stand alone (q8_0, q4_0: code times the block's fp16 scale; FP8-B128: the
+// e4m3 value times its group's fp32 scale). fmt: 0 = q8_0, 1 = q4_0, 3 = fp8.
+KVQ_HD inline double dequant_elem_f64(int fmt, const uint8_t* c, const uint8_t* s, int i) {
+  if (fmt == 0) return static_cast<int8_t>(c[i]) * f16_to_f64(ld_u16(s + 2 * (i / 32)));
+  if (fmt == 1) {
+    const uint8_t byte = c[16 * (i / 32) + (i % 32) / 2];
+    const int code = (i & 1) ? (byte >> 4) : (byte & 15);
+    return (code - 8) * f16_to_f64(ld_u16(s + 2 * (i / 32)));
+  }
+  return e4m3_to_f64(c[i]) * static_cast<double>(ld_f32(s + 4 * (i / 128)));
+}
+
+// A LUT3 row (128 elements) dequantized in float64: element i is the norm
+// scalar times the signed table magnitude of its 3-bit code, over sqrt(128);
+// the rotated variant then applies the (self-inverse) transform.
+KVQ_HD inline void dequant_lut3_f64(bool rotated, const uint8_t* c, const uint8_t* s, double* t) {
+  const double nu = f16_to_f64(ld_u16(s));
+  for (int i = 0; i < 128; ++i) {
+    unsigned code = 0;
+    for (int k = 0; k < 3; ++k) code |= ((c[(3 * i + k) / 8] >> ((3 * i + k) % 8)) & 1u) << k;
+    const double m = f16_to_f64(kLut3Bits[code & 3]);
+    t[i] = (nu * ((code >> 2) & 1 ? -m : m)) / sqrt(128.0);
+  }
+  if (rotated) wht128(t);
+}
+
+// Norm of a dequantized row: the square root of the float64 sum of squares
+// added in element order. fmt as in include/kvq.h (LUT3 rows are 128 wide).
+KVQ_HD inline double row_norm_f64(int fmt, const uint8_t* c, const uint8_t* s, int dim) {
+  double acc = 0.0;
+  if (fmt == 2 || fmt == 4) {
+    double t[128];
+    dequant_lut3_f64(fmt == 4, c, s, t);
+    for (int i = 0; i < 128; ++i) acc += t[i] * t[i];
+  } else {
+    for (int i = 0; i < dim; ++i) {
+      const double y = dequant_elem_f64(fmt, c, s, i);
+      acc += y * y;
+    }
+  }
+  return sqrt(acc);
+}
+
+// float64 -> float32 rounded toward +infinity (never below x; x >= 0 finite).
+KVQ_HD inline float f64_to_f32_up(double x) {
+  float f = static_cast<float>(x);
+  if (static_cast<double>(f) < x) f = nextafterf(f, INFINITY);
+  return f;
+}
+
 }  // namespace fmt
 }  // namespace kvq
 

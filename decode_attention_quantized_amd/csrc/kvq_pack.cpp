@@ -10,6 +10,7 @@
 // BlockWise1x128 scaling is from "FP8 MLA KV compression projection"
 // (kernelindex.com).
 
+#include <algorithm>
 #include <cfenv>
 #include <cmath>
 #include <cstdint>
@@ -207,6 +208,30 @@ extern "C" int32_t kvq_unpack(int32_t fmt, const uint8_t* codes, const uint8_t* 
         break;
     }
   }
+  return KVQ_OK;
+}
+
+extern "C" int32_t kvq_key_norms(int32_t fmt, const void* codes, const void* scales, int64_t n_seqs,
+                                 int32_t capacity, int32_t dim, float* out) {
+  int64_t cb = 0, sb = 0;
+  const int32_t rc = kvq_row_bytes(fmt, dim, &cb, &sb);
+  if (rc) return rc;
+  if (n_seqs < 0 || capacity < 1) return KVQ_ERR_ARG;
+  if (n_seqs == 0) return KVQ_OK;
+  if (!codes || !scales || !out) return KVQ_ERR_ARG;
+  const uint8_t* c = static_cast<const uint8_t*>(codes);
+  const uint8_t* s = static_cast<const uint8_t*>(scales);
+  const int64_t nbc = (int64_t(capacity) + 63) / 64;
+  for (int64_t q = 0; q < n_seqs; ++q)
+    for (int64_t k = 0; k < nbc; ++k) {
+      double m = 0.0;
+      for (int64_t r = 64 * k; r < std::min<int64_t>(64 * k + 64, capacity); ++r) {
+        const int64_t row = q * capacity + r;
+        const double n = kvq::fmt::row_norm_f64(fmt, c + row * cb, s + row * sb, dim);
+        if (n > m) m = n;
+      }
+      out[q * nbc + k] = kvq::fmt::f64_to_f32_up(m);
+    }
   return KVQ_OK;
 }
 
