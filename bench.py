@@ -436,6 +436,55 @@ def run_append(steps, warmup):
     return lines
 
 
+def run_kskip(steps, warmup):
+    """Key skipping (KVQ_SKIP_KEYS) against the exact rule on the same calls:
+    the long q4_0 shape (i.i.d. keys: nothing can be dropped, so this is the
+    flag's cost) and the aligned-hot q8_0 shape at ctx 32768 (planted keys
+    along the queries: most blocks are provably negligible). Both timed like
+    the headline call; one line per workload."""
+    import torch
+
+    import decode_attention_quantized_amd as kvq
+    import synth
+    from decode_attention_quantized_amd.runtime import DecodeAttention, PackedCache
+    lines = []
+    for name, w in (("long", synth.workload("long")),
+                    ("aligned_32k", synth.resized(synth.workload("tiny"), ctx=32768, hot=8))):
+        inp = synth.generate(w)
+        kc, ks = kvq.kvq_pack(w.fmt, inp.k)
+        vc, vs = kvq.kvq_pack(w.fmt, inp.v)
+        K0 = PackedCache.from_host(kc, ks, w.fmt, w.dim)
+        K0.norms = torch.from_numpy(kvq.kvq_key_norms(w.fmt, kc, ks, w.dim)).cuda()
+        V0 = PackedCache.from_host(vc, vs, w.fmt, w.dim)
+        set_bytes = 2 * K0.codes.numel() + 2 * K0.scales.numel()
+        R = max(2, math.ceil(ROTATION_BYTES / set_bytes))
+        caches = [(K0, V0)] + [(K0.clone(), V0.clone()) for _ in range(R - 1)]
+        q = torch.from_numpy(inp.q).cuda()
+        out = torch.empty((w.batch, w.q_heads, w.v_dim), dtype=torch.float32, device="cuda")
+        stream = torch.cuda.Stream()
+        res = {}
+        for mode, skip in (("exact", False), ("skip_keys", True)):
+            att = DecodeAttention(K0, V0, w.q_heads, ctx_len=w.ctx, softmax_scale=w.sigma, stream=stream,
+                                  skip_keys=skip)
+            res[mode] = time_mode(att, q, caches, w.ctx, w.threshold, steps, warmup, out, stream)
+            del att
+        cb, sb = kvq.kvq_row_bytes(w.fmt, w.dim)
+        st = res["skip_keys"]["stats"]
+        kb = (cb + sb) * (st["positions"] - st["key_rows_skipped"])
+        lines.append({"workload": "key_skipping", "case": name, "fmt": str(w.fmt), "batch": w.batch,
+                      "q_heads": w.q_heads, "kv_heads": w.kv_heads, "ctx": w.ctx, "threshold": w.threshold,
+                      "exact_kernel_us": round(res["exact"]["kernel_mean"] * 1e6, 3),
+                      "skip_keys_kernel_us": round(res["skip_keys"]["kernel_mean"] * 1e6, 3),
+                      "speedup": round(res["exact"]["kernel_mean"] / res["skip_keys"]["kernel_mean"], 3),
+                      "key_rows_skipped": st["key_rows_skipped"], "positions": st["positions"],
+                      "key_bytes_read": kb, "rows_fetched": st["rows_fetched"],
+                      "rows_fetched_exact": res["exact"]["stats"]["rows_fetched"], "rotation_sets": R})
+        torch.cuda.synchronize()
+        del caches, K0, V0, q, out, stream
+        torch.cuda.empty_cache()
+    return lines
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -447,7 +496,8 @@ def main():
                     help="which threshold(s) to time (a profiler run can restrict to one)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy 5 times (reference for HBM byte counters)")
-    ap.add_argument("--workload", choices=["long", "tiny", "sweep", "lut3", "lut3_wht", "mla", "stress", "append"],
+    ap.add_argument("--workload", choices=["long", "tiny", "sweep", "lut3", "lut3_wht", "mla", "stress", "append",
+                                           "kskip"],
                     default="long",
                     help="long (default) prints the metric line; the others print one line per "
                          "configuration (sweep: one per context length)")
@@ -485,6 +535,10 @@ def main():
 
     if args.workload == "append":
         for line in run_append(min(args.steps, 50), min(args.warmup, 5)):
+            print(json.dumps(line), flush=True)
+        return
+    if args.workload == "kskip":
+        for line in run_kskip(args.steps, args.warmup):
             print(json.dumps(line), flush=True)
         return
     if args.workload != "long":

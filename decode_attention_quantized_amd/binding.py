@@ -19,6 +19,7 @@ KVQ_Q_F32, KVQ_Q_BF16 = 0, 1
 KVQ_LAUNCH_COOPERATIVE = 1
 KVQ_SKIP_RUNNING = 2
 KVQ_TEST_WITHHOLD = 4
+KVQ_SKIP_KEYS = 8
 FMT = {"q8_0": KVQ_Q8_0, "q4_0": KVQ_Q4_0, "lut3": KVQ_LUT3, "fp8_b128": KVQ_FP8_B128, "lut3_wht": KVQ_LUT3_WHT}
 
 ERRORS = {0: "OK", -1: "ARG", -2: "ALIGN", -3: "RANGE", -4: "NONFINITE", -5: "WORKSPACE",
@@ -34,14 +35,15 @@ class KvqError(RuntimeError):
 
 class kvq_cache(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("batch", ctypes.c_int32),
-                ("heads", ctypes.c_int32), ("dim", ctypes.c_int32), ("capacity", ctypes.c_int32)]
+                ("heads", ctypes.c_int32), ("dim", ctypes.c_int32), ("capacity", ctypes.c_int32),
+                ("block_norms", ctypes.c_void_p)]
 
 
 class kvq_launch(ctypes.Structure):
     _fields_ = [("q_heads", ctypes.c_int32), ("q_dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
                 ("v_dim", ctypes.c_int32), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64),
                 ("stream", ctypes.c_void_p), ("mask_out", ctypes.c_void_p), ("splits", ctypes.c_int32),
-                ("flags", ctypes.c_int32), ("phase_times", ctypes.c_void_p)]
+                ("flags", ctypes.c_int32), ("phase_times", ctypes.c_void_p), ("key_skip_out", ctypes.c_void_p)]
 
 
 class kvq_stats_t(ctypes.Structure):
@@ -49,12 +51,12 @@ class kvq_stats_t(ctypes.Structure):
                 ("rows_fetched", ctypes.c_int64), ("k_bytes", ctypes.c_int64), ("v_bytes", ctypes.c_int64),
                 ("v_bytes_dense", ctypes.c_int64), ("status", ctypes.c_int32), ("splits", ctypes.c_int32),
                 ("batch", ctypes.c_int32), ("q_heads", ctypes.c_int32), ("live_tiles", ctypes.c_int64),
-                ("launches", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("launches", ctypes.c_int32), ("reserved", ctypes.c_int32), ("key_rows_skipped", ctypes.c_int64)]
 
 
 EXPORTS = ["kvq_row_bytes", "kvq_pack", "kvq_unpack", "kvq_lut3_levels", "kvq_append", "kvq_append_kv",
            "kvq_workspace_bytes", "kvq_decode_attn", "kvq_decode_attn_noalloc", "kvq_stats", "kvq_phase_count",
-           "kvq_strerror", "kvq_stream_read"]
+           "kvq_strerror", "kvq_stream_read", "kvq_key_norms", "kvq_key_norms_device"]
 
 _lib = None
 
@@ -84,6 +86,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_phase_count.argtypes = [ctypes.POINTER(kvq_launch), ctypes.POINTER(i32), ctypes.POINTER(i32)]
         L.kvq_strerror.argtypes = [i32]
         L.kvq_stream_read.argtypes = [vp, i64, i32, i32, vp, vp]
+        L.kvq_key_norms.argtypes = [i32, vp, vp, i64, i32, i32, vp]
+        L.kvq_key_norms_device.argtypes = [i32, vp, vp, i64, i32, i32, vp, i64, vp, vp, vp]
         L.kvq_strerror.restype = ctypes.c_char_p
         for name in EXPORTS:
             if name != "kvq_strerror":
@@ -177,20 +181,49 @@ def kvq_append_kv(fmt, k_src, v_src, dst_rows, k_codes, k_scales, v_codes, v_sca
                                None if status is None else status.data_ptr(), stream), "kvq_append_kv")
 
 
-def make_cache(codes, scales, dim: int) -> kvq_cache:
-    """kvq_cache for device tensors shaped [batch][heads][capacity][bytes]."""
+def make_cache(codes, scales, dim: int, block_norms=None) -> kvq_cache:
+    """kvq_cache for device tensors shaped [batch][heads][capacity][bytes]
+    (block_norms: optional device float32 [batch][heads][ceil(capacity/64)])."""
     B, H, cap = codes.shape[:3]
-    return kvq_cache(codes.data_ptr(), scales.data_ptr(), B, H, dim, cap)
+    return kvq_cache(codes.data_ptr(), scales.data_ptr(), B, H, dim, cap,
+                     None if block_norms is None else block_norms.data_ptr())
+
+
+def kvq_key_norms(fmt, codes: np.ndarray, scales: np.ndarray, dim: int) -> np.ndarray:
+    """Host block summaries of host planes [batch][heads][capacity][bytes]:
+    float32 [batch][heads][ceil(capacity/64)]."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    B, H, cap = codes.shape[:3]
+    out = np.zeros((B, H, (cap + 63) // 64), np.float32)
+    _check(lib().kvq_key_norms(_fmt(fmt), codes.ctypes.data, scales.ctypes.data, B * H, cap, dim, out.ctypes.data),
+           "kvq_key_norms")
+    return out
+
+
+def kvq_key_norms_device(fmt, codes, scales, dim: int, norms, blocks=None, status=None, stream=None):
+    """Device block summaries of device planes [batch][heads][capacity][bytes]
+    into the device float32 tensor ``norms`` [batch][heads][ceil(capacity/64)]:
+    every block, or the flat block ids of the device int64 tensor ``blocks``."""
+    B, H, cap = codes.shape[:3]
+    if norms.numel() != B * H * ((cap + 63) // 64):
+        raise KvqError(-1, "kvq_key_norms_device: norms must hold one value per block")
+    st = stream.cuda_stream if stream is not None else None
+    _check(lib().kvq_key_norms_device(_fmt(fmt), codes.data_ptr(), scales.data_ptr(), B * H, cap, dim,
+                                      None if blocks is None else blocks.data_ptr(),
+                                      0 if blocks is None else blocks.numel(), norms.data_ptr(),
+                                      None if status is None else status.data_ptr(), st), "kvq_key_norms_device")
 
 
 def make_launch(q_heads: int, *, q_dtype=KVQ_Q_F32, softmax_scale=0.0, v_dim=0, workspace=None,
-                stream=None, mask_out=None, splits=0, phase_times=None, flags=0) -> kvq_launch:
+                stream=None, mask_out=None, splits=0, phase_times=None, flags=0, key_skip_out=None) -> kvq_launch:
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = stream.cuda_stream if stream is not None else None
     mo = mask_out.data_ptr() if mask_out is not None else None
     pt = phase_times.data_ptr() if phase_times is not None else None
-    return kvq_launch(q_heads, q_dtype, float(softmax_scale), v_dim, ws_ptr, ws_bytes, st, mo, splits, flags, pt)
+    ko = key_skip_out.data_ptr() if key_skip_out is not None else None
+    return kvq_launch(q_heads, q_dtype, float(softmax_scale), v_dim, ws_ptr, ws_bytes, st, mo, splits, flags, pt, ko)
 
 
 def kvq_workspace_bytes(fmt, kcache: kvq_cache, launch: kvq_launch, ctx_len: int) -> int:

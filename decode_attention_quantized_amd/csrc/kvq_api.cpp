@@ -16,7 +16,7 @@
 
 namespace kvq {
 size_t gqa_lds_bytes(int fmt, int G, int P, int S);
-const void* gqa_kernel(int fmt, int G, bool run);
+const void* gqa_kernel(int fmt, int G, int mode);   // mode 0: exact rule, 1: single-pass rule, 2: key skipping
 size_t mla_lds_bytes(int H, int P, int S, int tpe);
 const void* mla_scores_kernel(int H);
 const void* mla_out_kernel();
@@ -345,12 +345,15 @@ extern "C" int32_t kvq_decode_attn(const void* q, const kvq_cache* kcache, const
                                    const kvq_launch* l) {
   if (!q || !kcache || !out || !l) return KVQ_ERR_ARG;
   if (!(threshold >= 0.0f) || !(threshold < 1.0f)) return KVQ_ERR_RANGE;   // also rejects NaN
-  if (l->flags & ~int32_t(KVQ_LAUNCH_COOPERATIVE | KVQ_SKIP_RUNNING | KVQ_TEST_WITHHOLD)) return KVQ_ERR_ARG;
+  if (l->flags & ~int32_t(KVQ_LAUNCH_COOPERATIVE | KVQ_SKIP_RUNNING | KVQ_TEST_WITHHOLD | KVQ_SKIP_KEYS))
+    return KVQ_ERR_ARG;
+  const bool kskip = (l->flags & KVQ_SKIP_KEYS) != 0;
+  if (kskip && (l->flags & KVQ_SKIP_RUNNING)) return KVQ_ERR_UNSUPPORTED;   // one skip rule per call
   Plan plan;
   int32_t rc = make_plan(fmt, kcache, l, ctx_len, &plan);
   if (rc) return rc;
   if (plan.mla) {
-    if (l->flags & KVQ_SKIP_RUNNING) return KVQ_ERR_UNSUPPORTED;   // latent kernels use the exact rule only
+    if (l->flags & (KVQ_SKIP_RUNNING | KVQ_SKIP_KEYS)) return KVQ_ERR_UNSUPPORTED;   // latent kernels: exact rule only
     return launch_mla(q, kcache, vcache, ctx_len, threshold, out, l, plan);
   }
   if (!vcache) return KVQ_ERR_UNSUPPORTED;                 // latent caches: not in this kernel family
@@ -362,6 +365,8 @@ extern "C" int32_t kvq_decode_attn(const void* q, const kvq_cache* kcache, const
       !aligned16(vcache->scales) || !aligned16(q) || !aligned16(out) ||
       (l->mask_out && !aligned16(l->mask_out)) || (l->workspace && !aligned16(l->workspace)))
     return KVQ_ERR_ALIGN;
+  if (kskip && !kcache->block_norms) return KVQ_ERR_ARG;
+  if (kskip && (reinterpret_cast<uintptr_t>(kcache->block_norms) & 3)) return KVQ_ERR_ALIGN;
   if (!l->workspace || l->workspace_bytes < plan.ws.total) return KVQ_ERR_WORKSPACE;
 
   unsigned char* ws = static_cast<unsigned char*>(l->workspace);
@@ -399,8 +404,15 @@ extern "C" int32_t kvq_decode_attn(const void* q, const kvq_cache* kcache, const
   a.times = reinterpret_cast<unsigned long long*>(l->phase_times);
   a.withhold = (l->flags & KVQ_TEST_WITHHOLD) != 0;
   a.spin_limit = a.withhold ? kvq::kTestSpinLimit : kvq::kSpinLimit;
+  a.kskip = kskip;
+  a.knorm = kcache->block_norms;
+  a.knorm_pitch = (kcache->capacity + 63) / 64;
+  a.pre_ml = reinterpret_cast<unsigned long long*>(ws + plan.ws.pre_ml);
+  a.kdrop = reinterpret_cast<int32_t*>(ws + plan.ws.kdrop);
+  a.kdrop_off = plan.ws.kdrop;
+  a.kskip_out = l->key_skip_out;
 
-  const void* kern = kvq::gqa_kernel(fmt, plan.G, (l->flags & KVQ_SKIP_RUNNING) != 0);
+  const void* kern = kvq::gqa_kernel(fmt, plan.G, kskip ? 2 : (l->flags & KVQ_SKIP_RUNNING) ? 1 : 0);
   if (!kern) return KVQ_ERR_UNSUPPORTED;
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kvq::kThreads, plan.lds) != hipSuccess)
@@ -468,6 +480,13 @@ extern "C" int32_t kvq_stats(const kvq_launch* l, kvq_stats_t* out, float* kept_
                   hipMemcpyDeviceToHost) != hipSuccess)
       return KVQ_ERR_LAUNCH;
     for (int32_t v : lv) out->live_tiles += v;
+  }
+  if (h.batch > 0 && h.nwg > 0 && h.kdrop_off > 0) {
+    std::vector<int32_t> kd(size_t(h.nwg));
+    if (hipMemcpy(kd.data(), static_cast<unsigned char*>(l->workspace) + h.kdrop_off, kd.size() * 4,
+                  hipMemcpyDeviceToHost) != hipSuccess)
+      return KVQ_ERR_LAUNCH;
+    for (int32_t v : kd) out->key_rows_skipped += v;
   }
   out->status = int32_t(h.status);
   out->launches = int32_t(h.launches);

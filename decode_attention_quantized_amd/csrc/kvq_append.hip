@@ -16,6 +16,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "kvq.h"
 #include "kvq_formats.h"
 
@@ -321,8 +323,61 @@ int32_t launch_append(int32_t fmt, const Job* jobs, int njobs, int64_t n_rows, i
   return KVQ_OK;
 }
 
+// Largest dequantized row norm of 64-row blocks (the summaries the decode
+// kernel's key skipping reads): one wave per block, lane r takes row 64k + r
+// of its sequence-head and computes the row's float64 norm with the host
+// packer's function (sum of squares in element order), the wave takes the
+// maximum and lane 0 stores it rounded up to float32. Blocks come from a
+// list of flat ids (sequence-head * blocks per capacity + block) or, with
+// no list, are all blocks.
+__global__ __launch_bounds__(64 * kWavesPerBlock) void key_norms_rows(int32_t fmt, const uint8_t* codes,
+                                                                      const uint8_t* scales, int64_t cb, int64_t sb,
+                                                                      int64_t n_seqs, int32_t capacity, int32_t dim,
+                                                                      const int64_t* blocks, int64_t n_blocks,
+                                                                      float* norms, int32_t* status) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t nbc = (int64_t(capacity) + 63) / 64;
+  for (int64_t i = int64_t(blockIdx.x) * kWavesPerBlock + wave; i < n_blocks; i += int64_t(gridDim.x) * kWavesPerBlock) {
+    const int64_t fb = blocks ? blocks[i] : i;
+    if (fb < 0 || fb >= n_seqs * nbc) {                  // uniform across the wave
+      if (lane == 0 && status) atomicOr(status, 8);
+      continue;
+    }
+    const int64_t q = fb / nbc, r = (fb - q * nbc) * 64 + lane;
+    double n = 0.0;
+    if (r < capacity) {
+      const int64_t row = q * capacity + r;
+      n = fmt::row_norm_f64(fmt, codes + row * cb, scales + row * sb, dim);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) n = fmax(n, __shfl_xor(n, o));
+    if (lane == 0) norms[fb] = fmt::f64_to_f32_up(n);
+  }
+}
+
 }  // namespace
 }  // namespace kvq
+
+extern "C" int32_t kvq_key_norms_device(int32_t fmt, const void* codes, const void* scales, int64_t n_seqs,
+                                        int32_t capacity, int32_t dim, const int64_t* blocks, int64_t n_blocks,
+                                        float* norms, int32_t* status, void* stream) {
+  int64_t cb = 0, sb = 0;
+  const int32_t rc = kvq_row_bytes(fmt, dim, &cb, &sb);
+  if (rc) return rc;
+  if (n_seqs < 0 || capacity < 1 || n_blocks < 0) return KVQ_ERR_ARG;
+  const int64_t total = n_seqs * ((int64_t(capacity) + 63) / 64);
+  if (!blocks) n_blocks = total;
+  if (n_blocks == 0) return KVQ_OK;
+  if (!codes || !scales || !norms) return KVQ_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(norms) & 3) || (reinterpret_cast<uintptr_t>(blocks) & 7)) return KVQ_ERR_ALIGN;
+  const int64_t grid = std::min<int64_t>((n_blocks + kvq::kWavesPerBlock - 1) / kvq::kWavesPerBlock, kvq::kMaxBlocks);
+  hipLaunchKernelGGL(kvq::key_norms_rows, dim3(unsigned(grid)), dim3(64 * kvq::kWavesPerBlock), 0,
+                     static_cast<hipStream_t>(stream), fmt, static_cast<const uint8_t*>(codes),
+                     static_cast<const uint8_t*>(scales), cb, sb, n_seqs, capacity, dim, blocks, n_blocks, norms,
+                     status);
+  if (hipGetLastError() != hipSuccess) return KVQ_ERR_LAUNCH;
+  return KVQ_OK;
+}
 
 extern "C" int32_t kvq_append(int32_t fmt, const float* src, int64_t n_rows, int32_t dim, const int64_t* dst_rows,
                               void* codes, void* scales, int64_t cache_rows, int32_t* status, void* stream) {

@@ -644,8 +644,17 @@ template <class T> struct LoadedOf<T, true> { using type = typename T::Raw16; };
 // workgroups, so the V pass runs right after the scores with weights relative
 // to the split's own max, and the group's LSE is gathered afterwards only to
 // scale the partial output (its wait overlaps the V pass).
-template <int FMT, int G, bool RUN>
+//
+// MODE 2 is key skipping (the default rule otherwise): the split first scores
+// its candidate blocks (largest key norm at least half the context's
+// largest), the group exchanges their statistics, which bound each head's
+// LSE from below, and the split then drops every other block whose bound
+// weight (64 positions or fewer, every score at most sigma * ||q_h|| * R)
+// is at most 1e-7 for all heads, and scores the rest.
+template <int FMT, int G, int MODE>
 __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
+  constexpr bool RUN = MODE == 1;                      // single-pass rule
+  constexpr bool KSKIP = MODE == 2;                    // key skipping
   using T = Traits<FMT>;
   constexpr bool kRot = FMT == KVQ_LUT3_WHT;           // rotate q in, partial outputs out
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
@@ -722,12 +731,24 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   const int nvalid = min(P, ctx - pos0);
   const __amdgpu_buffer_rsrc_t krc = rows_rsrc(a.kc + (row0 + pos0) * T::CB, nvalid * T::CB);
   const __amdgpu_buffer_rsrc_t krs = rows_rsrc(a.ks + (row0 + pos0) * T::SB, nvalid * T::SB);
-  const int kvc = (16 * wave + n16) * T::CB + T::kLaneOff * kg;
-  const int kvs = (16 * wave + n16) * T::SB;
-  auto load_tiles = [&](Loaded* raw, int kb) {
+  const int kvc = n16 * T::CB + T::kLaneOff * kg;
+  const int kvs = n16 * T::SB;
+  // Tile t of a K pass covers rows trow(t) .. trow(t) + 15 of the split: 16t,
+  // or, in the listed passes of key skipping, 16 (t mod 4) rows into the
+  // chunk klist[t / 4] (a listed tile past the pass's ntl tiles reads past
+  // the split's rows: zeros, no memory access).
+  const uint8_t* klist = nullptr;
+  int ntl = ntiles;
+  auto trow = [&](auto listed, int t) -> int {
+    if constexpr (decltype(listed)::value)
+      return t < ntl ? 64 * __builtin_amdgcn_readfirstlane(int(klist[t >> 2])) + 16 * (t & 3) : P;
+    else
+      return 16 * t;
+  };
+  auto load_tiles = [&](auto listed, Loaded* raw, int kb) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int m = (kb * U + u) * kWaves * 16;      // rows past the wave's first tile (uniform)
+      const int m = trow(listed, wave + (kb * U + u) * kWaves);     // uniform
       raw[u] = T::bload(krc, krs, kvc, kvs, m * T::CB, m * T::SB);
     }
   };
@@ -751,8 +772,17 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   const int qesz = a.q_bf16 ? 2 : 4;
   const __amdgpu_buffer_rsrc_t qrc = rows_rsrc(static_cast<const uint8_t*>(a.q), a.B * a.Hq * 128 * qesz);
   const uint4 qraw = bload16(qrc, ((b * a.Hq + g * G + min(jq, G - 1)) * 128 + lnq * 4) * qesz, 0);
+  // key skipping: this group's block summaries (the candidates' K tiles are
+  // requested once they are known)
+  float rmax = 0.f;
+  int nb_ctx = 0;
+  if constexpr (KSKIP) {
+    nb_ctx = (ctx + kChunk - 1) / kChunk;
+    const float* kn = a.knorm + int64_t(bg) * a.knorm_pitch;
+    for (int i = tid; i < nb_ctx; i += kThreads) rmax = fmaxf(rmax, kn[i]);
+  }
   __asm__ volatile("" ::: "memory");
-  load_tiles(rawA, 0);
+  if constexpr (!KSKIP) load_tiles(std::false_type{}, rawA, 0);
   __asm__ volatile("" ::: "memory");
 
   // ---------------------------------------------------------------- setup
@@ -764,6 +794,7 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     a.hdr->k_row_bytes = T::CB + T::SB;
     a.hdr->v_row_bytes = T::CB + T::SB;
     a.hdr->live_off = a.live_off;
+    a.hdr->kdrop_off = KSKIP ? a.kdrop_off : 0;
   }
   for (int c = tid; c < P / kChunk; c += kThreads) umask[c] = 0ull;
   if (tid == 0) wto[0] = wto[1] = 0;
@@ -780,6 +811,14 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
       } else {
         qv[0] = __uint_as_float(qraw.x); qv[1] = __uint_as_float(qraw.y);
         qv[2] = __uint_as_float(qraw.z); qv[3] = __uint_as_float(qraw.w);
+      }
+      if constexpr (KSKIP) {
+        // sigma * log2(e) * ||q_j|| of the query as given (the rotation of the
+        // LUT3_WHT path keeps the norm): the bound's factor per head
+        float ss = qv[0] * qv[0] + qv[1] * qv[1] + qv[2] * qv[2] + qv[3] * qv[3];
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 32);
+        if (ln == 0) qmax[j] = a.sigma_log2e * sqrtf(ss);
       }
       if constexpr (kRot) {
         // q' = H q / sqrt(128): dims 4ln + e; stages 1 and 2 inside the
@@ -850,6 +889,23 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
       }
     }
   }
+  // key skipping: per-chunk summaries of this split and the context's largest
+  // (LDS that the value pass's row lists use later: free until then)
+  float* rown = reinterpret_cast<float*>(rowlist);                // [nch] largest key norm per chunk
+  int* kcnt = reinterpret_cast<int*>(rown + P / kChunk);          // [4] list lengths, dropped positions
+  uint8_t* kl1 = reinterpret_cast<uint8_t*>(kcnt + 4);            // [nch] chunks of a listed K pass
+  uint8_t* kl2 = kl1 + P / kChunk;                                // [nch] chunks that are not candidates
+  uint8_t* kdr = kl2 + P / kChunk;                                // [nch] 1: chunk dropped
+  if constexpr (KSKIP) {
+    const float wmx = max_wave(rmax);
+    if (lane == 0) reinterpret_cast<float*>(wml)[wave] = wmx;
+    const float* kn = a.knorm + int64_t(bg) * a.knorm_pitch;
+    for (int c = tid; c < P / kChunk; c += kThreads) {
+      const int k = pos0 / kChunk + c;
+      rown[c] = k < nb_ctx ? kn[k] : 0.f;
+      kdr[c] = 0;
+    }
+  }
   __syncthreads();
 
   // MFMA operands of this lane
@@ -870,14 +926,14 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   // Scores go to LDS; each lane keeps a running (max, sum exp2) of its two
   // heads, updated once per batch of tiles without branches.
   float m0 = -INFINITY, l0 = 0.f, m1 = -INFINITY, l1 = 0.f;
-  auto score_batch = [&](const Loaded* raw, int t0) {
+  auto score_batch = [&](auto listed, const Loaded* raw, int t0) {
     float sa[U], sb[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) sa[u] = sb[u] = -INFINITY;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = t0 + u * kWaves;
-      if (t >= ntiles) break;                   // uniform across the wave
+      if (t >= ntl) break;                      // uniform across the wave
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
       const typename T::Raw ru = operands(raw[u]);
       if constexpr (T::kRowScale) {
@@ -897,7 +953,7 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
           acc[3] = fmaf(s, d[3], acc[3]);
         }
       }
-      const int lp = t * 16 + n16;
+      const int lp = trow(listed, t) + n16;
       const bool valid = (pos0 + lp) < ctx;
       const float s0 = valid ? (acc[0] + acc[1]) * hs0 : -INFINITY;
       const float s1 = valid ? (acc[2] + acc[3]) * hs1 : -INFINITY;
@@ -910,55 +966,60 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     batch_stats<U>(m1, l1, sb);
   };
   constexpr int STRIDE = kWaves * U;                  // tiles between a wave's batches
-  const int nbat = (ntiles + STRIDE - 1) / STRIDE;     // batches of the split (uniform)
-  if constexpr (kDouble) {
-    // the loads of the next batch are issued before the current batch is
-    // scored, unconditionally (past the split they read zeros without a
-    // memory access), so no load depends on a branch and two batches stay in
-    // flight; tiles past the split are skipped inside score_batch
-    for (int kb = 0; kb < nbat; kb += 2) {
-      load_tiles(rawB, kb + 1);
-      score_batch(rawA, wave + kb * STRIDE);
-      load_tiles(rawA, kb + 2);
-      score_batch(rawB, wave + (kb + 1) * STRIDE);
+  // One K pass over ntl tiles (all of the split's, or a listed pass's): the
+  // loads of the next batch are issued before the current batch is scored,
+  // unconditionally (past the split they read zeros without a memory
+  // access), so no load depends on a branch and two batches stay in flight;
+  // tiles past the pass are skipped inside score_batch.
+  auto k_pass = [&](auto listed, bool preloaded) {
+    const int nbat = (ntl + STRIDE - 1) / STRIDE;      // uniform
+    if (!preloaded) load_tiles(listed, rawA, 0);
+    if constexpr (kDouble) {
+      for (int kb = 0; kb < nbat; kb += 2) {
+        load_tiles(listed, rawB, kb + 1);
+        score_batch(listed, rawA, wave + kb * STRIDE);
+        load_tiles(listed, rawA, kb + 2);
+        score_batch(listed, rawB, wave + (kb + 1) * STRIDE);
+      }
+    } else {
+      for (int kb = 0; kb < nbat; ++kb) {
+        if (kb > 0) load_tiles(listed, rawA, kb);
+        score_batch(listed, rawA, wave + kb * STRIDE);
+      }
     }
-  } else {
-    for (int kb = 0; kb < nbat; ++kb) {
-      if (kb > 0) load_tiles(rawA, kb);
-      score_batch(rawA, wave + kb * STRIDE);
+  };
+  // split statistics of the tiles scored so far: merged over the 16 lanes of
+  // a lane group, then over the waves, and published to `base`
+  auto publish_stats = [&](u64* base, bool withhold) {
+    {
+      const float2 x0 = merge_row16(make_float2(m0, l0));
+      const float2 x1 = merge_row16(make_float2(m1, l1));
+      if (n16 == 0) {
+        wml[wave * 8 + j0] = x0;
+        wml[wave * 8 + j1] = x1;
+      }
     }
-  }
-  // split statistics: merge over the 16 lanes of a lane group, then over waves
-  {
-    const float2 x0 = merge_row16(make_float2(m0, l0));
-    const float2 x1 = merge_row16(make_float2(m1, l1));
-    if (n16 == 0) {
-      wml[wave * 8 + j0] = x0;
-      wml[wave * 8 + j1] = x1;
+    __syncthreads();
+    if (tid < 128) {                                 // row j of 16 lanes merges head j over the 16 waves
+      const int j = tid >> 4, w = tid & 15;
+      float2 acc = (j < G) ? wml[w * 8 + j] : make_float2(-INFINITY, 0.f);
+      acc = merge_row16(acc);
+      if (w == 0 && j < G && !withhold) {
+        u64* dst = base + ((int64_t(bg) * a.S + split) * G + j) * 2;
+        put_tagged_f(dst, epoch, acc.x);
+        put_tagged_f(dst + 1, epoch, acc.y);
+        if constexpr (RUN) lse[j] = acc.x;           // the split's max: reference of its weights
+      }
     }
-  }
-  __syncthreads();
-  stamp(a, 2);
-  if (tid < 128) {                                   // row j of 16 lanes merges head j over the 16 waves
-    const int j = tid >> 4, w = tid & 15;
-    float2 acc = (j < G) ? wml[w * 8 + j] : make_float2(-INFINITY, 0.f);
-    acc = merge_row16(acc);
-    // (test aid: split 0 of the first group withholds its statistics, so
-    // every workgroup of that group waits in vain)
-    if (w == 0 && j < G && !(a.withhold && bg == 0 && split == 0)) {
-      u64* dst = a.split_ml + ((int64_t(bg) * a.S + split) * G + j) * 2;
-      put_tagged_f(dst, epoch, acc.x);
-      put_tagged_f(dst + 1, epoch, acc.y);
-      if constexpr (RUN) lse[j] = acc.x;             // the split's max: reference of its weights
-    }
-  }
-  __syncthreads();                                   // wml is reused below
+    __syncthreads();                                 // wml is reused below
+  };
 
+  // ---------------------------------------------------------------- phase 2: LSE of the group
   // ---------------------------------------------------------------- phase 2: LSE of the group
   // Every workgroup gathers all split statistics of its group and merges
   // them itself (128 threads per head, fixed pattern, so every workgroup of
   // the group computes the same bits); no workgroup waits on another's LSE.
-  auto gather_lse = [&](float* dst) {
+  auto gather_lse = [&](const u64* src, float* dst) {
     // The group's S*G (max, sum) pairs are contiguous 16-byte pieces (split
     // sp, head j at piece sp*G + j). Thread t takes pieces t and t + kThreads
     // (S*G <= 2048: at most 256 splits of at most 8 heads), both of head
@@ -966,7 +1027,7 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     // waves' results are merged in wave order. The pattern is fixed, so every
     // workgroup of the group computes the same bits.
     const int nc = a.S * G;
-    const __amdgpu_buffer_rsrc_t r = coherent_rsrc(a.split_ml + int64_t(bg) * nc * 2, nc * 16);
+    const __amdgpu_buffer_rsrc_t r = coherent_rsrc(src + int64_t(bg) * nc * 2, nc * 16);
     u32x4 v[2];
     bool use[2];
     int off[2];
@@ -996,13 +1057,101 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     }
     __syncthreads();
   };
+
+  if constexpr (!KSKIP) {
+    k_pass(std::false_type{}, true);
+  } else {
+    // candidates: chunks inside the context whose largest key norm is at
+    // least half the context's largest; the others inside the context are
+    // tested after the exchange of the candidates' statistics
+    float R = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) R = fmaxf(R, reinterpret_cast<const float*>(wml)[w]);
+    const float half = 0.5f * R;
+    const int nchs = P / kChunk;
+    if (wave == 0) {                                 // lists in chunk order, 64 chunks per ballot
+      int n1 = 0, n2 = 0;
+      for (int c0 = 0; c0 < nchs; c0 += 64) {
+        const int c = c0 + lane;
+        const bool in = c < nchs && pos0 + c * kChunk < ctx;
+        const bool cand = in && rown[c] >= half;
+        const bool other = in && !cand;
+        const u64 b1 = __ballot(cand), b2 = __ballot(other);
+        const u64 below = (1ull << lane) - 1ull;
+        if (cand) kl1[n1 + __popcll(b1 & below)] = uint8_t(c);
+        if (other) kl2[n2 + __popcll(b2 & below)] = uint8_t(c);
+        n1 += __popcll(b1);
+        n2 += __popcll(b2);
+      }
+      if (lane == 0) { kcnt[0] = n1; kcnt[1] = n2; kcnt[2] = 0; kcnt[3] = 0; }
+    }
+    __syncthreads();
+    const int n1 = kcnt[0], n2 = kcnt[1];
+    klist = kl1;
+    ntl = 4 * n1;
+    k_pass(std::true_type{}, false);
+    publish_stats(a.pre_ml, false);
+    if (n2 > 0) {
+      // lower bounds of the heads' LSE from every split's candidates, then the
+      // drop test of this split's other chunks: every score of chunk c is at
+      // most sigma * log2(e) * ||q_j|| * R_c (log2 domain), so its weight
+      // under head j is at most |c| * 2^(that - L_j)
+      gather_lse(a.pre_ml, lse);
+      const float leps = log2f(1e-7f);
+      for (int i = tid; i < n2; i += kThreads) {
+        const int c = kl2[i];
+        const int size = min(kChunk, ctx - pos0 - c * kChunk);
+        const float lim = leps - log2f(float(size));
+        bool drop = true;
+#pragma unroll
+        for (int j = 0; j < G; ++j) drop = drop && qmax[j] * rown[c] <= lse[j] + lim;
+        kdr[c] = drop ? 1 : 0;
+      }
+      __syncthreads();
+      if (wave == 0) {                               // the chunks that stay, in order: pass 2's list
+        int n3 = 0, nd = 0;
+        for (int i0 = 0; i0 < n2; i0 += 64) {
+          const int i = i0 + lane;
+          const int c = i < n2 ? kl2[i] : 0;
+          const bool stay = i < n2 && !kdr[c];
+          const bool gone = i < n2 && kdr[c];
+          const u64 bs = __ballot(stay);
+          if (stay) kl1[n3 + __popcll(bs & ((1ull << lane) - 1ull))] = uint8_t(c);
+          n3 += __popcll(bs);
+          int sz = gone ? min(kChunk, ctx - pos0 - c * kChunk) : 0;
+#pragma unroll
+          for (int o = 32; o >= 1; o >>= 1) sz += __shfl_xor(sz, o);
+          nd += sz;
+        }
+        if (lane == 0) { kcnt[2] = n3; kcnt[3] = nd; }
+      }
+      __syncthreads();
+      ntl = 4 * kcnt[2];
+      k_pass(std::true_type{}, false);
+    }
+    // chunks never scored (dropped, or past the context) hold -inf scores
+    for (int i = tid; i < nchs * G * kChunk; i += kThreads) {
+      const int c = i / (G * kChunk);
+      if (kdr[c] || pos0 + c * kChunk >= ctx) sc[i] = -INFINITY;
+    }
+    if (a.kskip_out)
+      for (int c = tid; c < nchs; c += kThreads) {
+        const int k = pos0 / kChunk + c;
+        if (k < nb_ctx) a.kskip_out[int64_t(bg) * nb_ctx + k] = kdr[c];
+      }
+    if (tid == 0) a.kdrop[wg] = kcnt[3];
+  }
+  // (test aid: split 0 of the first group withholds its statistics, so
+  // every workgroup of that group waits in vain)
+  publish_stats(a.split_ml, a.withhold && bg == 0 && split == 0);
+  stamp(a, 2);
   const int nch = P / kChunk;                        // 64-position blocks of the split
   // single-pass rule: running LSE per (head, block) [G][nch] after block
   // summaries [G][nch], both in the K staging strip (free until the V pass)
   float2* csum = reinterpret_cast<float2*>(stg);
   float* rl = reinterpret_cast<float*>(csum + G * nch);
   if constexpr (!RUN) {
-    gather_lse(lse);
+    gather_lse(a.split_ml, lse);
   } else {
     // block summaries: four adjacent threads per (head, block), 16 positions
     // each, combined with two exchanges (kThreads is a multiple of 64, so the
@@ -1368,7 +1517,7 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   if constexpr (RUN) {
     // every workgroup takes part (the exchange also proves to the epoch
     // counter below that the whole group has read the epoch)
-    gather_lse(fac);
+    gather_lse(a.split_ml, fac);
     if (tid < G) fac[tid] = exp2f(lse[tid] - fac[tid]);
     __syncthreads();
   }
@@ -1592,11 +1741,12 @@ size_t gqa_lds_bytes(int fmt, int G, int P, int S) {
          size_t(kWaves) * 16 * pitch + 64;
 }
 
-const void* gqa_kernel(int fmt, int G, bool run) {
+const void* gqa_kernel(int fmt, int G, int mode) {
 #define KVQ_SEL(F, GG)                                                                      \
   if (fmt == F && G == GG)                                                                  \
-    return run ? reinterpret_cast<const void*>(&gqa_fused<F, GG, true>)                     \
-               : reinterpret_cast<const void*>(&gqa_fused<F, GG, false>);
+    return mode == 1 ? reinterpret_cast<const void*>(&gqa_fused<F, GG, 1>)                  \
+         : mode == 2 ? reinterpret_cast<const void*>(&gqa_fused<F, GG, 2>)                  \
+                     : reinterpret_cast<const void*>(&gqa_fused<F, GG, 0>);
   KVQ_SEL(KVQ_Q4_0, 1) KVQ_SEL(KVQ_Q4_0, 2) KVQ_SEL(KVQ_Q4_0, 4) KVQ_SEL(KVQ_Q4_0, 8)
   KVQ_SEL(KVQ_Q8_0, 1) KVQ_SEL(KVQ_Q8_0, 2) KVQ_SEL(KVQ_Q8_0, 4) KVQ_SEL(KVQ_Q8_0, 8)
   KVQ_SEL(KVQ_LUT3, 1) KVQ_SEL(KVQ_LUT3, 2) KVQ_SEL(KVQ_LUT3, 4) KVQ_SEL(KVQ_LUT3, 8)

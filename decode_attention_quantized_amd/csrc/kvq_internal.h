@@ -27,7 +27,7 @@ struct WsHeader {
   uint32_t status;                      // sticky device fault bits
   uint32_t launches;                    // kernel launches of the last call (the grouped plans may need several)
   long long live_off;                   // byte offset of the per-workgroup live-tile counts (int32 [nwg])
-  unsigned long long reserved3;
+  long long kdrop_off;                  // byte offset of the per-workgroup dropped key positions (int32 [nwg]; 0: none)
   int32_t batch, q_heads, kv_heads, ctx;
   int32_t splits, positions_per_split, fmt, v_dim;
   int32_t nwg, k_row_bytes;
@@ -50,6 +50,8 @@ struct WsLayout {
   int64_t pmass;       // tagged [B*Hkv][S][G]: per-split kept mass
   int64_t partial;     // tagged [B*Hkv][S][G][Dv]: per-split partial outputs
   int64_t live;        // int32 [B*Hkv][S]: 64-position chunks of the split holding a kept row
+  int64_t pre_ml;      // tagged [B*Hkv][S][G][2]: key skipping, (max, sum) over the split's candidate blocks
+  int64_t kdrop;       // int32 [B*Hkv][S]: key skipping, key positions the split left out
   int64_t total;
 };
 
@@ -69,6 +71,8 @@ inline WsLayout ws_layout(int B, int Hkv, int Hq, int S, int Dv) {
   w.pmass = off;     off = align256(off + BG * S * G * 8);
   w.partial = off;   off = align256(off + BG * S * G * int64_t(Dv) * 8);
   w.live = off;      off = align256(off + BG * S * 4);
+  w.pre_ml = off;    off = align256(off + BG * S * G * 16);
+  w.kdrop = off;     off = align256(off + BG * S * 4);
   w.total = off;
   return w;
 }
@@ -105,6 +109,16 @@ struct GqaArgs {
   long long live_off;             // its byte offset in the workspace (recorded in the header)
   int32_t bg0, ngroups;           // this launch covers groups bg0 .. bg0 + ngroups - 1 (of B * Hkv)
   int32_t launches;               // launches of the call
+  // key skipping (kskip != 0): block summaries [B*Hkv][knorm_pitch] (largest key
+  // norm per 64 rows), the candidates' statistics, dropped positions per
+  // workgroup and the optional dropped-block map [B*Hkv][ceil(ctx/64)]
+  int32_t kskip;
+  int32_t knorm_pitch;
+  const float* knorm;
+  unsigned long long* pre_ml;     // tagged
+  int32_t* kdrop;
+  long long kdrop_off;
+  uint8_t* kskip_out;
 };
 
 // Arguments of the two MLA kernels.

@@ -15,10 +15,11 @@ from . import binding as B
 class PackedCache:
     """Code and scale planes [batch][heads][capacity][bytes] on a GPU."""
 
-    def __init__(self, codes: torch.Tensor, scales: torch.Tensor, fmt, dim: int):
+    def __init__(self, codes: torch.Tensor, scales: torch.Tensor, fmt, dim: int, norms: torch.Tensor | None = None):
         assert codes.dtype == torch.uint8 and scales.dtype == torch.uint8
         assert codes.is_cuda and scales.is_cuda and codes.is_contiguous() and scales.is_contiguous()
         self.codes, self.scales, self.fmt, self.dim = codes, scales, B._fmt(fmt), int(dim)
+        self.norms = norms          # optional float32 [batch][heads][ceil(capacity/64)] key-block summaries
 
     @classmethod
     def from_host(cls, codes: np.ndarray, scales: np.ndarray, fmt, dim: int, device="cuda"):
@@ -31,10 +32,19 @@ class PackedCache:
         return tuple(self.codes.shape[:3])
 
     def struct(self) -> B.kvq_cache:
-        return B.make_cache(self.codes, self.scales, self.dim)
+        return B.make_cache(self.codes, self.scales, self.dim, self.norms)
 
     def clone(self) -> "PackedCache":
-        return PackedCache(self.codes.clone(), self.scales.clone(), self.fmt, self.dim)
+        return PackedCache(self.codes.clone(), self.scales.clone(), self.fmt, self.dim,
+                           None if self.norms is None else self.norms.clone())
+
+    def compute_norms(self, stream=None) -> torch.Tensor:
+        """(Re)compute every key-block summary on the GPU (kvq_key_norms_device)."""
+        Bn, H, cap = self.shape
+        if self.norms is None:
+            self.norms = torch.zeros((Bn, H, (cap + 63) // 64), dtype=torch.float32, device=self.codes.device)
+        B.kvq_key_norms_device(self.fmt, self.codes, self.scales, self.dim, self.norms, stream=stream)
+        return self.norms
 
     @classmethod
     def empty(cls, fmt, batch: int, heads: int, capacity: int, dim: int, device="cuda"):
@@ -74,7 +84,8 @@ class DecodeAttention:
 
     def __init__(self, k: PackedCache, v: PackedCache | None, q_heads: int, *, ctx_len: int,
                  q_dtype=B.KVQ_Q_F32, softmax_scale: float = 0.0, v_dim: int = 0, splits: int = 0,
-                 stream=None, cooperative: bool = False, running: bool = False, test_withhold: bool = False):
+                 stream=None, cooperative: bool = False, running: bool = False, test_withhold: bool = False,
+                 skip_keys: bool = False):
         self.k, self.v = k, v
         self.q_heads = q_heads
         self.fmt = k.fmt
@@ -84,7 +95,8 @@ class DecodeAttention:
                                  v_dim=v_dim if v is None else 0, splits=splits,
                                  flags=(B.KVQ_LAUNCH_COOPERATIVE if cooperative else 0)
                                  | (B.KVQ_SKIP_RUNNING if running else 0)
-                                 | (B.KVQ_TEST_WITHHOLD if test_withhold else 0))
+                                 | (B.KVQ_TEST_WITHHOLD if test_withhold else 0)
+                                 | (B.KVQ_SKIP_KEYS if skip_keys else 0))
         probe = B.make_launch(q_heads, **self.launch_proto)
         nbytes = B.kvq_workspace_bytes(self.fmt, k.struct(), probe, ctx_len)
         # zero-filled on the launch stream, so the fill is ordered before the
@@ -94,19 +106,21 @@ class DecodeAttention:
         self._ks = k.struct()
         self._vs = v.struct() if v is not None else None
 
-    def launch(self, mask_out=None, phase_times=None) -> B.kvq_launch:
+    def launch(self, mask_out=None, phase_times=None, key_skip_out=None) -> B.kvq_launch:
         return B.make_launch(self.q_heads, workspace=self.workspace, stream=self.stream, mask_out=mask_out,
-                             phase_times=phase_times, **self.launch_proto)
+                             phase_times=phase_times, key_skip_out=key_skip_out, **self.launch_proto)
 
     def __call__(self, q: torch.Tensor, ctx_len: int, threshold: float, out: torch.Tensor | None = None,
                  mask_out: torch.Tensor | None = None, k: PackedCache | None = None,
-                 v: PackedCache | None = None, phase_times: torch.Tensor | None = None) -> torch.Tensor:
+                 v: PackedCache | None = None, phase_times: torch.Tensor | None = None,
+                 key_skip_out: torch.Tensor | None = None) -> torch.Tensor:
         bsz = self.k.shape[0]
         if out is None:
             out = torch.empty((bsz, self.q_heads, self.v_dim), dtype=torch.float32, device=q.device)
         ks = self._ks if k is None else k.struct()
         vs = self._vs if v is None else v.struct()
-        B.kvq_decode_attn(q, ks, vs, self.fmt, ctx_len, threshold, out, self.launch(mask_out, phase_times))
+        B.kvq_decode_attn(q, ks, vs, self.fmt, ctx_len, threshold, out,
+                          self.launch(mask_out, phase_times, key_skip_out))
         return out
 
     def stats(self):

@@ -159,6 +159,31 @@ int32_t kvq_append_kv(int32_t fmt, const float* k_src, const float* v_src, int64
                       const int64_t* dst_rows, void* k_codes, void* k_scales, void* v_codes, void* v_scales,
                       int64_t cache_rows, int32_t* status, void* stream);
 
+/* Key-block summaries for KVQ_SKIP_KEYS. For each of n_seqs consecutive
+ * (sequence, head) row ranges of `capacity` rows of a packed cache and each
+ * block k of 64 rows (the last one shorter when capacity % 64 != 0):
+ *   out[s][k] = max over the block's rows of ||dequant(row)||,
+ * each norm the square root of the float64 sum of the squared float64
+ * dequantized elements added in element order (for KVQ_LUT3_WHT after the
+ * inverse rotation, as kvq_unpack), the maximum rounded up to float32, so a
+ * summary never understates a norm. Rows never written (zero planes) count
+ * as norm 0. kvq_key_norms works on host planes (codes, scales: n_seqs *
+ * capacity rows of kvq_row_bytes; out: host float[n_seqs][ceil(capacity/64)]).
+ * kvq_key_norms_device computes the same bits on the GPU from device planes
+ * into device `norms`, for the flat block ids in the device list `blocks`
+ * (s * ceil(capacity/64) + k; n_blocks of them) or, with blocks NULL, for
+ * every block: after a decode step's kvq_append_kv, pass the blocks that
+ * received rows. A listed id out of range is skipped and ORs 8 into the
+ * optional device int32 `status`. Asynchronous on `stream`.
+ * Errors: ARG (null pointers, negative counts, capacity < 1), UNSUPPORTED
+ * (fmt/dim as kvq_row_bytes), ALIGN (norms not 4-byte, blocks not 8-byte
+ * aligned), LAUNCH. */
+int32_t kvq_key_norms(int32_t fmt, const void* codes, const void* scales, int64_t n_seqs, int32_t capacity,
+                      int32_t dim, float* out);
+int32_t kvq_key_norms_device(int32_t fmt, const void* codes, const void* scales, int64_t n_seqs,
+                             int32_t capacity, int32_t dim, const int64_t* blocks, int64_t n_blocks,
+                             float* norms, int32_t* status, void* stream);
+
 /* ------------------------------------------------------------------ decode */
 
 /* A packed cache in device memory. Row r of (batch b, head h) is at
@@ -172,6 +197,9 @@ typedef struct kvq_cache {
   int32_t heads;
   int32_t dim;
   int32_t capacity;
+  const float* block_norms;   /* optional device [batch][heads][ceil(capacity/64)]: the largest key
+                                 norm of each block of 64 rows (kvq_key_norms, kvq_key_norms_device);
+                                 read only by KVQ_SKIP_KEYS, NULL otherwise */
 } kvq_cache;
 
 typedef struct kvq_launch {
@@ -189,6 +217,8 @@ typedef struct kvq_launch {
   uint64_t* phase_times;  /* optional device [workgroups][16] buffer (profiling aid; NULL to skip):
                              each workgroup stores the 100 MHz device wall clock at its phase
                              boundaries (see kvq_phase_count) */
+  uint8_t* key_skip_out;  /* optional device [batch][kv_heads][ceil(ctx_len/64)] (KVQ_SKIP_KEYS):
+                             1 where the block's keys were left out, else 0; NULL to skip */
 } kvq_launch;
 
 /* kvq_launch.flags (bits). The workgroups of one call exchange data while they
@@ -218,8 +248,29 @@ typedef struct kvq_launch {
  * sets the sticky status bit (kvq_stats then returns KVQ_ERR_DEVICE), and
  * every output element and kept mass that depended on a wait that gave up is
  * written as NaN (here: all outputs of the first group; the other groups are
- * exact). After such a call the workspace must be zero-filled again. */
-enum { KVQ_LAUNCH_COOPERATIVE = 1, KVQ_SKIP_RUNNING = 2, KVQ_TEST_WITHHOLD = 4 };
+ * exact). After such a call the workspace must be zero-filled again.
+ *
+ * KVQ_SKIP_KEYS leaves out key blocks whose weights a bound proves negligible
+ * ([SV] FAQ "Почему нельзя пропускать и K-деквантизацию?": a first pass has
+ * to filter key positions). It reads kcache->block_norms (required) and, for
+ * each (sequence, kv head), with blocks k of 64 positions and R_k their
+ * largest key norm:
+ *   1. candidate blocks: R_k >= R_max / 2 (R_max over the context's blocks);
+ *      they are scored first, and L_h, the log-sum-exp of head h's scores
+ *      over them, is a lower bound of the head's full log-sum-exp;
+ *   2. any other block is dropped, its keys never read, when for every head
+ *      h of the group |B_k| * exp(sigma * ||q_h|| * R_k - L_h) <= 1e-7, |B_k|
+ *      its positions inside the context (sigma * ||q_h|| * R_k bounds every
+ *      score of the block, so its whole weight is at most 1e-7);
+ *   3. the softmax, the keep rule and the output are then taken over the
+ *      positions of the blocks not dropped; the normalized weights there are
+ *      the exact ones times at most 1 / (1 - W), W <= 1e-7 per dropped block.
+ * The blocks that are neither candidates nor dropped are scored after an
+ * extra exchange of the candidates' statistics. Grouped formats only, not
+ * with KVQ_SKIP_RUNNING (UNSUPPORTED); ARG if kcache->block_norms is NULL.
+ * kvq_stats.key_rows_skipped counts the positions left out;
+ * kvq_launch.key_skip_out optionally receives the dropped blocks. */
+enum { KVQ_LAUNCH_COOPERATIVE = 1, KVQ_SKIP_RUNNING = 2, KVQ_TEST_WITHHOLD = 4, KVQ_SKIP_KEYS = 8 };
 
 /* Device workspace bytes kvq_decode_attn needs for these shapes on the
  * current device (bytes: host out-pointer), for every context length from 1
@@ -300,6 +351,7 @@ typedef struct kvq_stats_t {
                               one launch cannot hold every group (see kvq_decode_attn); the
                               fp8 latent path always uses two (scores, then output) */
   int32_t reserved;
+  int64_t key_rows_skipped;  /* KVQ_SKIP_KEYS: key positions (inside the context) left out */
 } kvq_stats_t;
 
 /* Statistics of the last kvq_decode_attn on this workspace. Synchronizes

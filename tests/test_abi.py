@@ -59,7 +59,7 @@ def test_decode_argument_validation_without_gpu():
     assert _call(fmt=7) == -1
     bad = B.kvq_launch(3, 0, 0.0, 0, 0x50000, 1 << 30, None, None, 0, 0, None)   # 3 % 1 ok, use heads=2
     assert _call(k=_cache(heads=2), v=_cache(heads=2), launch=bad) == -1        # q_heads % kv heads
-    badflags = B.kvq_launch(4, 0, 0.0, 0, 0x50000, 1 << 30, None, None, 0, 8, None)
+    badflags = B.kvq_launch(4, 0, 0.0, 0, 0x50000, 1 << 30, None, None, 0, 16, None)
     assert _call(launch=badflags) == -1
     assert _call(k=_cache(dim=64), v=_cache(dim=64)) == -7       # UNSUPPORTED head dim
     g16 = B.kvq_launch(16, 0, 0.0, 0, 0x50000, 1 << 30, None, None, 0, 0, None)
