@@ -324,7 +324,7 @@ def run_config(w, steps, warmup, splits=0, modes=("sparse", "dense"), single_pas
     k_bytes = (w.batch * w.ctx if latent else w.batch * w.kv_heads * w.ctx) * row
     line = {"workload": w.name, "fmt": str(w.fmt), "batch": w.batch,
             "q_heads": w.q_heads, "kv_heads": w.kv_heads, "dim": w.dim, "ctx": w.ctx,
-            "rotation_sets": R, "splits": res["sparse"]["stats"]["splits"]}
+            "rotation_sets": R, "splits": next(iter(res.values()))["stats"]["splits"]}
     for m, r in res.items():
         st = r["stats"]
         ab = k_bytes + st["rows_fetched"] * vrow + qo
@@ -439,9 +439,9 @@ def run_append(steps, warmup):
 def run_kskip(steps, warmup):
     """Key skipping (KVQ_SKIP_KEYS) against the exact rule on the same calls:
     the long q4_0 shape (i.i.d. keys: nothing can be dropped, so this is the
-    flag's cost) and the aligned-hot q8_0 shape at ctx 32768 (planted keys
-    along the queries: most blocks are provably negligible). Both timed like
-    the headline call; one line per workload."""
+    flag's cost) and the aligned-hot q8_0 shape at ctx 32768, batch 1 and 8
+    (planted keys along the queries: most blocks are provably negligible).
+    All timed like the headline call; one line per workload."""
     import torch
 
     import decode_attention_quantized_amd as kvq
@@ -449,7 +449,8 @@ def run_kskip(steps, warmup):
     from decode_attention_quantized_amd.runtime import DecodeAttention, PackedCache
     lines = []
     for name, w in (("long", synth.workload("long")),
-                    ("aligned_32k", synth.resized(synth.workload("tiny"), ctx=32768, hot=8))):
+                    ("aligned_32k", synth.resized(synth.workload("tiny"), ctx=32768, hot=8)),
+                    ("aligned_b8_32k", synth.resized(synth.workload("tiny"), batch=8, ctx=32768, hot=8))):
         inp = synth.generate(w)
         kc, ks = kvq.kvq_pack(w.fmt, inp.k)
         vc, vs = kvq.kvq_pack(w.fmt, inp.v)

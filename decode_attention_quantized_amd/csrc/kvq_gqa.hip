@@ -678,12 +678,10 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   float* wmass = reinterpret_cast<float*>(wrows + kWaves);        // [kWaves][G]
   float2* wml = reinterpret_cast<float2*>(wmass + kWaves * G);    // [kWaves][8] per-wave (max, sum)
   int* wproc = reinterpret_cast<int*>(wml + kWaves * 8);          // [kWaves] value rows each wave summed
-  int* wto = wproc + kWaves;                                      // [4]: [0] a wait of this workgroup gave up,
-                                                                  // [1] a head of the group keeps a row here
-  unsigned long long* umask = reinterpret_cast<unsigned long long*>(wproc + kWaves + 4);  // [P/64] union keep bits
-  // per-wave lists of the kept rows a wave fetches: [kWaves][32 * ceil(P/64 / (kWaves/2))]
-  uint16_t* rowlist = reinterpret_cast<uint16_t*>(umask + (P / kChunk));
-  const int list_cap = 32 * ((P / kChunk + kWaves / 2 - 1) / (kWaves / 2));
+  int* wto = wproc + kWaves;                                      // [4]: [0] a wait of this workgroup gave up
+  // per-wave lists of the kept rows a wave fetches: [kWaves][64 * ceil(P/64 / kWaves)]
+  uint16_t* rowlist = reinterpret_cast<uint16_t*>(wto + 4);
+  const int list_cap = 64 * ((P / kChunk + kWaves - 1) / kWaves);
   // per-wave K staging strip [kWaves][16 rows][PITCH] (16-byte aligned; the
   // offset is rounded, not the pointer, so accesses stay LDS instructions)
   const int stg_off = (int(reinterpret_cast<unsigned char*>(rowlist + kWaves * list_cap) - smem) + 15) & ~15;
@@ -796,8 +794,7 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     a.hdr->live_off = a.live_off;
     a.hdr->kdrop_off = KSKIP ? a.kdrop_off : 0;
   }
-  for (int c = tid; c < P / kChunk; c += kThreads) umask[c] = 0ull;
-  if (tid == 0) wto[0] = wto[1] = 0;
+  if (tid == 0) wto[0] = 0;
   if (kLut3 && tid < 64) lut3_tab[tid] = lut3_pair_entry(tid);
   // q of this group: per-head max |q| -> power-of-two prescale, then fp16 hi/lo rows
   float qv[4];
@@ -1181,20 +1178,21 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
   stamp(a, 3);
 
   // ---------------------------------------------------------------- phase 3: sparse V pass
-  // Waves 2c' and 2c'+1 share the 64-position chunks c = c' (mod kWaves/2).
-  // (a) Each decides the keep bits of half of the group's heads and ORs the
-  //     union (a value row is fetched iff some head keeps it) into umask[c].
-  //     A head keeps a position iff its normalized weight 2^(s - LSE) reaches
-  //     the threshold, decided on the score as s >= LSE + log2(threshold)
-  //     (the two differ only for weights within float32 rounding of the
-  //     threshold). The scores stay in place: the value pass forms the
-  //     weights of the rows it fetches (the same decision, then 2^(s - LSE)).
-  // (b) After one barrier each takes the kept rows of its chunks of even
-  //     (first wave of the pair) or odd (second) rank and fetches only those.
-  constexpr int HALF = G > 1 ? G / 2 : 1;
-  const int pair = wave >> 1, side = wave & 1;
-  const int jb = G > 1 ? side * HALF : 0;
-  const bool do_p = G > 1 || side == 0;
+  // Wave w takes the 64-position chunks c = w (mod kWaves). With fewer
+  // chunks than waves, chunk c goes to the waves w = c (mod nchunks), which
+  // share its kept rows by rank (wave w takes ranks w / nchunks modulo their
+  // count); each of them decides the chunk.
+  // (a) It decides the keep bits of every head of the group for its chunks:
+  //     a head keeps a position iff its normalized weight 2^(s - LSE)
+  //     reaches the threshold, decided on the score as s >= LSE +
+  //     log2(threshold) (the two differ only for weights within float32
+  //     rounding of the threshold). A value row is fetched iff some head
+  //     keeps it: the union of the heads' ballots goes straight to the
+  //     wave's own row list. The scores stay in place: the value pass forms
+  //     the weights of the rows it fetches (the same decision, then
+  //     2^(s - LSE)).
+  // (b) The wave then fetches only those rows. No other wave reads its list,
+  //     so no barrier separates the decision from the value pass.
   // the hardware exp flushes results below 2^-126: exact for weights that a
   // normal threshold keeps, and for threshold 0 (such weights add < 2^-126);
   // a subnormal threshold needs the full-range exp2f
@@ -1204,49 +1202,56 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
 #pragma unroll
   for (int j = 0; j < G; ++j) { o0[j] = 0.f; o1[j] = 0.f; mass[j] = 0.f; }
   int kept_cnt = 0;
-  float lsej[HALF], thr[HALF];
-#pragma unroll
-  for (int jj = 0; jj < HALF; ++jj) {
-    lsej[jj] = lse[jb + jj];
-    thr[jj] = lsej[jj] + ltau;
-  }
   const int nchunks = P / kChunk;
-  if (do_p) {
-    // a score past the context is -inf, below every threshold (threshold 0
-    // compares with the lowest finite value)
-    float th[HALF];
+  uint16_t* mylist = rowlist + wave * list_cap;
+  int nmine = 0, nlive = 0;                          // rows in the wave's list, chunks holding one
+  // (not under the single-pass rule, whose decision writes the weights over
+  // the scores: a second wave could read them back as scores)
+  const bool few = !RUN && nchunks < kWaves;         // uniform
+  const int cfirst = few ? wave % nchunks : wave;
+  const int sub = few ? wave / nchunks : 0;          // this wave's share of a shared chunk's rows
+  const int nsub = few ? (kWaves - 1 - cfirst) / nchunks + 1 : 1;
+  {
+    // a score past the context (or of a dropped key block) is -inf, below
+    // every threshold (threshold 0 compares with the lowest finite value)
+    float lsej[G], th[G];
 #pragma unroll
-    for (int jj = 0; jj < HALF; ++jj) th[jj] = fmaxf(thr[jj], -3.4028235e38f);
-    // four of the wave's chunks per step: their scores are read together,
-    // so the LDS latency is paid once per four chunks
-    constexpr int CB4 = 4, CSTEP = kWaves / 2;
-    for (int c0 = pair; c0 < nchunks; c0 += CB4 * CSTEP) {
-      float sv4[CB4][HALF];
+    for (int j = 0; j < G; ++j) {
+      lsej[j] = lse[j];
+      th[j] = fmaxf(lsej[j] + ltau, -3.4028235e38f);
+    }
+    // two of the wave's chunks per step: their scores are read together,
+    // so the LDS latency is paid once per two chunks
+    constexpr int CB = 2;
+    for (int c0 = cfirst; c0 < nchunks; c0 += CB * kWaves) {
+      float sv2[CB][G];
 #pragma unroll
-      for (int q = 0; q < CB4; ++q) {
-        const int c = min(c0 + q * CSTEP, nchunks - 1);
-        const float* base = sc + c * (G * kChunk) + jb * kChunk + lane;
+      for (int q = 0; q < CB; ++q) {
+        const int c = min(c0 + q * kWaves, nchunks - 1);
+        const float* base = sc + c * (G * kChunk) + lane;
 #pragma unroll
-        for (int jj = 0; jj < HALF; ++jj) sv4[q][jj] = base[jj * kChunk];
+        for (int j = 0; j < G; ++j) sv2[q][j] = base[j * kChunk];
       }
 #pragma unroll
-      for (int q = 0; q < CB4; ++q) {
-        const int c = c0 + q * CSTEP;
+      for (int q = 0; q < CB; ++q) {
+        const int c = c0 + q * kWaves;
         if (c >= nchunks) break;                      // uniform
-        float* base = sc + c * (G * kChunk) + jb * kChunk + lane;
-        const float (&sv)[HALF] = sv4[q];
-        unsigned long long bal[HALF], uni = 0ull;
+        float* base = sc + c * (G * kChunk) + lane;
+        const float (&sv)[G] = sv2[q];
+        unsigned long long bal[G], uni = 0ull;
 #pragma unroll
-        for (int jj = 0; jj < HALF; ++jj) {
+        for (int j = 0; j < G; ++j) {
           // single-pass rule: the reference is the running LSE of the block
-          const float t = RUN ? fmaxf(rl[(jb + jj) * nch + c] + ltau, -3.4028235e38f) : th[jj];
-          bal[jj] = __ballot(sv[jj] >= t);
-          uni |= bal[jj];
-          kept_cnt += __popcll(bal[jj]);
+          const float t = RUN ? fmaxf(rl[j * nch + c] + ltau, -3.4028235e38f) : th[j];
+          bal[j] = __ballot(sv[j] >= t);
+          uni |= bal[j];
+          if (sub == 0) kept_cnt += __popcll(bal[j]);
         }
-        if (lane == 0 && uni) {
-          atomicOr(&umask[c], uni);
-          wto[1] = 1;
+        if (uni) {                                    // uniform
+          const int rank = __popcll(uni & ((1ull << lane) - 1ull));
+          if (((uni >> lane) & 1ull) && rank % nsub == sub) mylist[nmine + rank / nsub] = uint16_t(c * kChunk + lane);
+          nmine += (__popcll(uni) - sub + nsub - 1) / nsub;
+          if (sub == 0) ++nlive;
         }
         if constexpr (RUN) {
           // single-pass rule: the running LSE of the blocks lives in the K
@@ -1254,50 +1259,28 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
           // (relative to the split's max, 0 where a head skips) replace the
           // scores here
 #pragma unroll
-          for (int jj = 0; jj < HALF; ++jj) {
-            const bool keep = (bal[jj] >> lane) & 1ull;
-            const float x = sv[jj] - lsej[jj];
-            base[jj * kChunk] = keep ? (hw_exp ? ex2(x) : exp2f(x)) : 0.f;
+          for (int j = 0; j < G; ++j) {
+            const bool keep = (bal[j] >> lane) & 1ull;
+            const float x = sv[j] - lsej[j];
+            base[j * kChunk] = keep ? (hw_exp ? ex2(x) : exp2f(x)) : 0.f;
           }
         }
-        if (a.mask_out && lane < 2) {
+        if (a.mask_out && sub == 0 && lane < 2) {
           const int word = (pos0 + c * kChunk) / 32 + lane;
           if (word < a.mask_words)
 #pragma unroll
-            for (int jj = 0; jj < HALF; ++jj)
-              a.mask_out[(int64_t(b) * a.Hq + g * G + jb + jj) * a.mask_words + word] = uint32_t(bal[jj] >> (32 * lane));
+            for (int j = 0; j < G; ++j)
+              a.mask_out[(int64_t(b) * a.Hq + g * G + j) * a.mask_words + word] = uint32_t(bal[j] >> (32 * lane));
         }
       }
     }
   }
-  stamp(a, 7);
-  __syncthreads();
-  // Whether this split will publish a partial output, published at once:
-  // the merge reads it with the partials and skips the partial of a split
-  // that keeps nothing (which never writes one). A split whose wait gave up
-  // publishes its NaN partial; under the single-pass rule every split
-  // publishes (its factor to the group's LSE is only known later).
+  // single-pass rule: the running LSE lives in the K staging strips, which
+  // the value pass below overwrites; every wave must be done reading it
+  if constexpr (RUN) __syncthreads();
+  const int rows_cnt = nmine | (nlive << 16);        // rows | live chunks << 16
   const int64_t pbase = int64_t(bg) * a.S + split;
-  const bool publishes = RUN || wto[0] != 0 || wto[1] != 0;
-  if (tid == 0) put_tagged(a.act + pbase, epoch, publishes ? 1u : 0u);
-  uint16_t* mylist = rowlist + wave * list_cap;
-  int nmine = 0, rows_cnt = 0;                       // rows_cnt: rows | live chunks << 16
-  for (int c0 = pair; c0 < nchunks; c0 += 4 * (kWaves / 2)) {
-    unsigned long long um4[4];                        // four chunks' union words read together
-#pragma unroll
-    for (int q = 0; q < 4; ++q) um4[q] = umask[min(c0 + q * (kWaves / 2), nchunks - 1)];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int c = c0 + q * (kWaves / 2);
-      if (c >= nchunks) break;                        // uniform
-      const unsigned long long um = um4[q];
-      const int n = __popcll(um);
-      if (side == 0) rows_cnt += n + (n ? 1 << 16 : 0);
-      const int rank = __popcll(um & ((1ull << lane) - 1ull));
-      if (((um >> lane) & 1ull) && (rank & 1) == side) mylist[nmine + (rank >> 1)] = uint16_t(c * kChunk + lane);
-      nmine += (n + 1 - side) >> 1;
-    }
-  }
+  stamp(a, 7);
   stamp(a, 8);
   using VM = VMfma<FMT>;
   // weight of head j at split position i: 2^(s - LSE) if the head keeps the
@@ -1513,6 +1496,13 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
     if (wproc[w] > 0) act |= 1u << w;
   }
   nact = __popc(act);
+  // Whether this split publishes a partial output: the merge reads this word
+  // with the partials and skips the partial of a split that keeps nothing
+  // (which never writes one). A split whose wait gave up publishes its NaN
+  // partial; under the single-pass rule every split publishes (its factor to
+  // the group's LSE is only known later).
+  const bool publishes = RUN || wto[0] != 0 || nact > 0;
+  if (tid == 0) put_tagged(a.act + pbase, epoch, publishes ? 1u : 0u);
   float* fac = qmax;                                  // single-pass rule: per-head factor to the group LSE
   if constexpr (RUN) {
     // every workgroup takes part (the exchange also proves to the epoch
@@ -1732,12 +1722,12 @@ __global__ __launch_bounds__(kThreads) void gqa_fused(GqaArgs a) {
 // LDS bytes the kernel needs for P positions per split and group size G.
 size_t gqa_lds_bytes(int fmt, int G, int P, int S) {
   const size_t sc = size_t(gqa_sc_floats(G, P, S));
-  const size_t list_cap = 32 * ((P / kChunk + kWaves / 2 - 1) / (kWaves / 2));
+  const size_t list_cap = 64 * ((P / kChunk + kWaves - 1) / kWaves);
   const size_t pitch = fmt == KVQ_Q4_0 ? Traits<KVQ_Q4_0>::PITCH
                      : fmt == KVQ_Q8_0 ? Traits<KVQ_Q8_0>::PITCH
                                        : Traits<KVQ_LUT3>::PITCH;     // LUT3 and LUT3_WHT
   return sc * 4 + 16 * 128 * 2 + 64 * 4 + 3 * 8 * 4 + 2 * kWaves * 4 + size_t(kWaves) * G * 4 +
-         size_t(kWaves) * 8 * 8 + (kWaves + 4) * 4 + size_t(P / kChunk) * 8 + size_t(kWaves) * list_cap * 2 + 16 +
+         size_t(kWaves) * 8 * 8 + (kWaves + 4) * 4 + size_t(kWaves) * list_cap * 2 + 16 +
          size_t(kWaves) * 16 * pitch + 64;
 }
 
