@@ -375,6 +375,36 @@ def lut3_object(steps, warmup):
     return line
 
 
+def sweep_object(steps, warmup):
+    """The long shape over context lengths 4K..64K (16 log2(n/1024) hot
+    positions per kv head), sparse against dense: where the skip starts to
+    pay, as the pages' speed-up-versus-context figures. Kernel time per call
+    from the graph replay, like the headline."""
+    import synth
+    rows = []
+    for n in synth.SWEEP:
+        r = run_config(synth.workload(f"sweep_{n}"), steps, warmup, single_pass=False)
+        rows.append({"ctx": n, "sparse_us": r["sparse"]["kernel_us_mean"], "dense_us": r["dense"]["kernel_us_mean"],
+                     "speedup_sparse_vs_dense": r["speedup_sparse_vs_dense"],
+                     "sparse_tokens_per_s": r["sparse"]["tokens_per_s"],
+                     "frac_hbm_sparse": r["sparse"]["frac_hbm"], "rows_fetched": r["sparse"]["rows_fetched"]})
+    return {"workload": "long shape (q4_0, batch 1, 32/4 heads) at each context", "lengths": rows}
+
+
+def mla_object(steps, warmup):
+    """The fp8 latent (MLA-shaped) configuration: batch 8, 128 heads over one
+    576-wide latent, ctx 65536, bf16 queries; both kernels per call."""
+    import synth
+    r = run_config(synth.workload("mla"), steps, warmup, single_pass=False)
+    sp = r["sparse"]
+    r["roofline"] = {"bound": "hbm", "achieved": sp["achieved_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": sp["frac_hbm"], "traffic": None, "kernel": "kvq::mla_scores<8> + kvq::mla_out",
+                     "algorithmic_bytes_per_launch": sp["algorithmic_bytes"], "kernel_us_mean": sp["kernel_us_mean"],
+                     "mfma_frac_bf16": sp["frac_mfma_bf16"],
+                     "timing": "HIP events around one graph replay of the timed steps (both kernels of a call)"}
+    return r
+
+
 def run_append(steps, warmup):
     """The device append packer (kvq_append): one decode step's new K and V rows
     (one row per (sequence, kv head) each, as the long-context and latent
@@ -508,6 +538,8 @@ def main():
     ap.add_argument("--traffic-workload", choices=["long", "lut3"], default="long")
     ap.add_argument("--no-lut3", action="store_true",
                     help="leave the LUT3 (batch 8, ctx 32768) object out of the default line")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="leave the context sweep and the latent (MLA) objects out of the default line")
     args = ap.parse_args()
     if args.write_traffic:
         print(json.dumps(write_traffic(args.write_traffic, args.traffic_workload)), flush=True)
@@ -677,6 +709,9 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_lut3 and args.profile_mode == "both":
         line["lut3_32k"] = lut3_object(args.steps, args.warmup)
+    if not args.no_other_configs and args.profile_mode == "both":
+        line["sweep"] = sweep_object(min(args.steps, 50), min(args.warmup, 5))
+        line["mla_64k"] = mla_object(min(args.steps, 50), min(args.warmup, 5))
     if not args.no_cpu_baseline:
         cb_, ref, (okc, oks) = cpu_baseline(inp)
         line["cpu_baseline"] = cb_
