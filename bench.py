@@ -41,8 +41,14 @@ KERNEL_SRC = os.path.join(ROOT, "decode_attention_quantized_amd", "csrc", "kvq_g
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the grouped kernel's code: the source with its comments and
+    blank space removed (line comments only: the file has no block comments
+    and no // inside strings), so edits of comments keep the stamp valid."""
+    with open(KERNEL_SRC) as f:
+        src = f.read()
+    code = "\n".join(" ".join(line.split("//", 1)[0].split()) for line in src.splitlines())
+    code = "\n".join(line for line in code.splitlines() if line)
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def traffic_file(workload: str) -> str:

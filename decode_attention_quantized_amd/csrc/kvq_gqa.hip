@@ -1,8 +1,9 @@
 // Fused sparse-V decode attention for grouped-query caches (q8_0, q4_0, LUT3)
-// on gfx950. One launch per call; all workgroups are resident at once (at
-// most one per compute unit) and the workgroups of one (sequence, kv head)
-// group exchange data through workspace words tagged with the call's epoch,
-// so the scores of a whole context never leave the chip:
+// on gfx950. One launch per call (or one per share of the groups when they
+// do not all fit one launch); all workgroups of a launch are resident at once
+// (at most one per compute unit) and the workgroups of one (sequence, kv
+// head) group exchange data through workspace words tagged with the call's
+// epoch, so the scores of a whole context never leave the chip:
 //
 //  1. K pass. Each workgroup owns P consecutive positions of one (sequence,
 //     kv head). Waves stream 16-position tiles of packed K rows, dequantize
@@ -637,7 +638,7 @@ template <class T> struct LoadedOf<T, true> { using type = typename T::Raw16; };
 // each group also counts its group towards publishing the next epoch (once
 // past the LSE exchange every workgroup of the group has read the epoch).
 //
-// RUN selects the single-pass skip rule: a position is kept when its weight
+// MODE 1 (RUN) selects the single-pass skip rule: a position is kept when its weight
 // under the softmax of its split's positions up to the end of its 64-position
 // block reaches the threshold (the weight an in-loop flash-attention kernel
 // sees with its running max and sum). That decision needs nothing from other
@@ -645,7 +646,7 @@ template <class T> struct LoadedOf<T, true> { using type = typename T::Raw16; };
 // to the split's own max, and the group's LSE is gathered afterwards only to
 // scale the partial output (its wait overlaps the V pass).
 //
-// MODE 2 is key skipping (the default rule otherwise): the split first scores
+// MODE 2 (KSKIP) is key skipping (the default rule otherwise): the split first scores
 // its candidate blocks (largest key norm at least half the context's
 // largest), the group exchanges their statistics, which bound each head's
 // LSE from below, and the split then drops every other block whose bound
