@@ -109,6 +109,20 @@ def test_ragged_context_and_device_summaries():
     _check(inp, w.threshold, g, r, drop, margin, planes, summ, ctx_len=1000)
 
 
+def test_several_launches():
+    """300 sequences of the tiny shape (one kv head each): 300 groups, more
+    than one launch holds, so the call runs as two launches; key skipping
+    per group is unchanged."""
+    say("case key skipping over two launches: tiny shape, batch 300")
+    w = synth.resized(synth.workload("tiny"), batch=300)
+    inp = synth.generate(w)
+    r, drop, margin, planes, summ = _oracle(inp, w.threshold)
+    assert drop.any()
+    g = _run(inp, w.threshold)
+    assert g["stats"]["launches"] == 2, g["stats"]
+    _check(inp, w.threshold, g, r, drop, margin, planes, summ)
+
+
 def test_nothing_to_drop_on_the_long_shape():
     """i.i.d. keys with boosted hot positions: no block can be proven
     negligible, so the result is the exact rule's."""

@@ -60,6 +60,18 @@ def test_noalloc_matches_workspace_call_twice(fmt):
             assert err <= MAX_ABS and rel <= MAX_REL_L2
 
 
+def test_noalloc_with_several_launches():
+    """A call whose 288 groups need two launches runs on the fixed array
+    too (each launch advances the epoch in it), then a one-launch call."""
+    for kw in (dict(batch=72, ctx=1000, hot=4), dict(batch=1, ctx=2000, hot=4)):
+        say("case no-alloc entry point:", kw)
+        inp, K, V, q = _inputs("long", **kw)
+        ref, out = _both(inp, K, V, q, 1e-6)
+        assert np.array_equal(out, ref), "no-alloc output differs from the workspace call"
+        r, _ = oracle_for(inp, 1e-6)
+        assert float(np.abs(out - r.out64).max()) <= MAX_ABS
+
+
 def test_noalloc_refuses_latent_plans():
     import torch
 
