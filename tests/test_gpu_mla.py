@@ -132,3 +132,56 @@ def test_mla_full_size(threshold):
     else:
         assert st["rows_fetched"] == 8 * 65536, st
         assert np.allclose(g["stats"]["kept_mass"], 1.0, atol=1e-5)
+
+
+def _identical_rows(ctx, heads=128, seed=12):
+    inp, _ = _case(0.0, batch=1, q_heads=heads, ctx=ctx, hot=0, seed=seed)
+    inp.k[:] = inp.k[:, :, :1, :]                   # every position holds the same latent row
+    return inp
+
+
+@pytest.mark.parametrize("ctx", [4097, 32768])
+def test_mla_identical_rows_all_skipped(ctx):
+    """Every weight is 1/n; a threshold 1% above it skips every position:
+    no tile is re-scored, the output is exactly zero, no row is read."""
+    say("case mla identical rows, all skipped: ctx", ctx)
+    inp = _identical_rows(ctx)
+    tau = float(np.float32(1.01 / ctx))
+    g = run_gpu(inp, tau, q_bf16=True)
+    r, po = oracle_for(inp, tau)
+    assert r.kept_pairs == 0 and r.rows_fetched == 0
+    compare(inp, tau, g, r, po)
+    assert np.all(g["out"] == 0.0), "output must be exactly zero when every position is skipped"
+    assert g["stats"]["rows_fetched"] == 0 and g["stats"]["kept_pairs"] == 0, g["stats"]
+    assert g["stats"]["live_tiles"] == 0, g["stats"]
+    assert not g["mask"].any()
+
+
+@pytest.mark.parametrize("ctx", [4097, 32768])
+def test_mla_identical_rows_all_kept(ctx):
+    """A threshold 1% below 1/n keeps every position: out = mean of the
+    dequantized value parts of the rows."""
+    say("case mla identical rows, all kept: ctx", ctx)
+    inp = _identical_rows(ctx)
+    tau = float(np.float32(0.99 / ctx))
+    g = run_gpu(inp, tau, q_bf16=True)
+    r, po = oracle_for(inp, tau)
+    H = inp.w.q_heads
+    assert r.kept_pairs == H * ctx
+    compare(inp, tau, g, r, po)
+    assert g["mask"].all()
+    assert g["stats"]["rows_fetched"] == ctx and g["stats"]["kept_pairs"] == H * ctx, g["stats"]
+
+
+@pytest.mark.parametrize("threshold", [1e-40, 1e-39])
+def test_mla_threshold_below_smallest_normal(threshold):
+    """Latent rows of standard deviation 16 spread the scaled logits over
+    more than a hundred nats, so the threshold falls among subnormal float32
+    weights; the keep test and the weights stay exact there."""
+    say("case mla subnormal threshold", threshold)
+    inp, tau = _case(threshold, batch=1, q_heads=32, ctx=8192, hot=0, key_std=16.0, seed=13)
+    g = run_gpu(inp, tau, q_bf16=True)
+    r, po = oracle_for(inp, tau)
+    assert 0 < r.kept_pairs < inp.w.q_heads * inp.w.ctx, r.kept_pairs
+    assert (r.p[r.mask] < 1.17549435e-38).any(), "some kept weights must be subnormal"
+    compare(inp, tau, g, r, po)
