@@ -32,19 +32,25 @@ METRIC = "decode-attn tokens/s + KV GB/s (% HBM roofline) at 32K ctx, sparse-V o
 HBM_PEAK_GBS = 8000.0
 ROTATION_BYTES = 640 << 20
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
-KERNEL_NAMES = {"long": "kvq::gqa_fused<q4_0, G=8>", "lut3": "kvq::gqa_fused<lut3, G=8>"}
+KERNEL_NAMES = {"long": "kvq::gqa_fused<q4_0, G=8>", "lut3": "kvq::gqa_fused<lut3, G=8>",
+                "mla": "kvq::mla_scores<8> + kvq::mla_out (kvq::mla_out_dense at threshold 0)"}
 WORKLOAD_TEXT = {
     "long": "long-ctx q4_0: batch 1, 32/4 heads, dim 128, ctx 32768",
     "lut3": "LUT3: batch 8, 32/4 heads, dim 128, ctx 32768, 8..64 hot per kv head",
+    "mla": "fp8 latent (MLA shape): batch 8, 128 heads over one 576-wide latent, ctx 65536, 96 hot per sequence",
 }
-KERNEL_SRC = os.path.join(ROOT, "decode_attention_quantized_amd", "csrc", "kvq_gqa.hip")
+CSRC = os.path.join(ROOT, "decode_attention_quantized_amd", "csrc")
+KERNEL_SRCS = {"long": "kvq_gqa.hip", "lut3": "kvq_gqa.hip", "mla": "kvq_mla.hip"}
+# kernels of one call whose dispatches are summed per call (name substrings)
+TRAFFIC_KERNELS = {"long": ("gqa_fused",), "lut3": ("gqa_fused",), "mla": ("mla_scores", "mla_out")}
 
 
-def kernel_hash() -> str:
-    """Hash of the grouped kernel's code: the source with its comments and
-    blank space removed (line comments only: the file has no block comments
-    and no // inside strings), so edits of comments keep the stamp valid."""
-    with open(KERNEL_SRC) as f:
+def kernel_hash(workload: str = "long") -> str:
+    """Hash of the workload's kernel source code: the source with its comments
+    and blank space removed (line comments only: the files have no block
+    comments and no // inside strings), so edits of comments keep the stamp
+    valid."""
+    with open(os.path.join(CSRC, KERNEL_SRCS[workload])) as f:
         src = f.read()
     code = "\n".join(" ".join(line.split("//", 1)[0].split()) for line in src.splitlines())
     code = "\n".join(line for line in code.splitlines() if line)
@@ -52,7 +58,8 @@ def kernel_hash() -> str:
 
 
 def traffic_file(workload: str) -> str:
-    return os.path.join(TRAFFIC_DIR, f"traffic_gqa_fused_{workload}.json")
+    name = "traffic_mla_latent.json" if workload == "mla" else f"traffic_gqa_fused_{workload}.json"
+    return os.path.join(TRAFFIC_DIR, name)
 
 
 def load_traffic(mode: str, workload: str = "long"):
@@ -63,7 +70,7 @@ def load_traffic(mode: str, workload: str = "long"):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_sha256_16") != kernel_hash():
+    if t.get("kernel_sha256_16") != kernel_hash(workload):
         return None
     m = t.get(mode)
     return None if m is None else m.get("bytes_per_launch")
@@ -73,7 +80,8 @@ def write_traffic(base: str, workload: str = "long") -> dict:
     """Turn six rocprofv3 --pmc runs under `base` (fs/ws: FETCH_SIZE and
     WRITE_SIZE at threshold 1e-6, fd/wd: the same at threshold 0, cf/cw: the
     plain device copy of --copy-calibration) into calibrated HBM bytes per
-    launch of the grouped kernel, stamped with the kernel source hash."""
+    call (the latent workload: its two kernels summed), stamped with the
+    kernel source hash."""
     import csv
     import glob
 
@@ -95,13 +103,18 @@ def write_traffic(base: str, workload: str = "long") -> dict:
     ff, wf = n / 1024 / cf, n / 1024 / cw
     t = {"kernel": KERNEL_NAMES[workload],
          "workload": WORKLOAD_TEXT[workload],
-         "kernel_sha256_16": kernel_hash(),
+         "kernel_sha256_16": kernel_hash(workload),
          "calibration": {"copy_bytes_each_way": n, "copy_FETCH_SIZE_KiB": cf, "copy_WRITE_SIZE_KiB": cw,
                          "fetch_factor": ff, "write_factor": wf}}
     for mode, fs, ws in (("sparse", "fs", "ws"), ("dense", "fd", "wd")):
-        nd, fk = per_dispatch(fs, "gqa_fused")
-        _, wk = per_dispatch(ws, "gqa_fused")
-        t[mode] = {"FETCH_SIZE_KiB": fk, "WRITE_SIZE_KiB": wk, "dispatches": nd,
+        fk = wk = 0.0
+        nds = []
+        for kname in TRAFFIC_KERNELS[workload]:
+            nd, f1 = per_dispatch(fs, kname)
+            _, w1 = per_dispatch(ws, kname)
+            fk, wk = fk + f1, wk + w1
+            nds.append(nd)
+        t[mode] = {"FETCH_SIZE_KiB": fk, "WRITE_SIZE_KiB": wk, "dispatches": nds[0] if len(nds) == 1 else nds,
                    "bytes_per_launch": int(round((fk * ff + wk * wf) * 1024))}
     with open(traffic_file(workload), "w") as f:
         json.dump(t, f, indent=1)
@@ -404,10 +417,12 @@ def mla_object(steps, warmup):
     r = run_config(synth.workload("mla"), steps, warmup, single_pass=False)
     sp = r["sparse"]
     r["roofline"] = {"bound": "hbm", "achieved": sp["achieved_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": sp["frac_hbm"], "traffic": None, "kernel": "kvq::mla_scores<8> + kvq::mla_out",
+                     "frac": sp["frac_hbm"], "traffic": load_traffic("sparse", "mla"),
+                     "kernel": "kvq::mla_scores<8> + kvq::mla_out",
                      "algorithmic_bytes_per_launch": sp["algorithmic_bytes"], "kernel_us_mean": sp["kernel_us_mean"],
                      "mfma_frac_bf16": sp["frac_mfma_bf16"],
                      "timing": "HIP events around one graph replay of the timed steps (both kernels of a call)"}
+    r["dense"]["traffic"] = load_traffic("dense", "mla")
     return r
 
 
@@ -541,7 +556,7 @@ def main():
     ap.add_argument("--write-traffic", metavar="DIR",
                     help="no GPU work: summarize rocprofv3 counter runs under DIR (fs ws fd wd cf cw) "
                          "into the committed traffic file of --traffic-workload")
-    ap.add_argument("--traffic-workload", choices=["long", "lut3"], default="long")
+    ap.add_argument("--traffic-workload", choices=["long", "lut3", "mla"], default="long")
     ap.add_argument("--no-lut3", action="store_true",
                     help="leave the LUT3 (batch 8, ctx 32768) object out of the default line")
     ap.add_argument("--no-other-configs", action="store_true",
