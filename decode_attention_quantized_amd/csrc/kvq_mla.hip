@@ -300,38 +300,39 @@ __device__ inline void hand_over(const float (&send)[8], float4* __restrict__ xw
   xw[64] = make_float4(send[4], send[5], send[6], send[7]);
 }
 
-// Maximum over the 32 columns of a wave half of each of the 8 rows in v,
-// ending with row e = col & 7 in every lane (the four lanes of a row hold
-// equal bits). Each of the first three steps halves the rows a lane carries:
-// bit 0, 1, 2 of col picks the half it keeps, and it sends the other half to
-// the partner lane that keeps it (col ^ 1, col ^ 2, then col -+ 4 in the
-// 16-lane row, which flips bit 2 and keeps bits 0 and 1); two more steps
-// combine lanes that carry the same row (col -+ 8, then the other 16 lanes).
-__device__ __attribute__((always_inline)) inline float max32_row(const float (&v)[8], int col) {
-  const bool c0 = col & 1, c1 = (col >> 1) & 1, c2 = (col >> 2) & 1;
-  float w[4], y[2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) w[i] = fmaxf(c0 ? v[2 * i + 1] : v[2 * i], dpp<0xB1>(c0 ? v[2 * i] : v[2 * i + 1]));
-#pragma unroll
-  for (int j = 0; j < 2; ++j) y[j] = fmaxf(c1 ? w[2 * j + 1] : w[2 * j], dpp<0x4E>(c1 ? w[2 * j] : w[2 * j + 1]));
-  float z = fmaxf(c2 ? y[1] : y[0], dpp<0x124>(c2 ? y[0] : y[1]));   // row_ror:4
-  z = fmaxf(z, dpp<0x128>(z));                                           // row_ror:8
+// Maximum over the 32 columns of a wave half of each group of four rows of v
+// (rows 4i .. 4i + 3, i = col & 1 in the result). The group's rows are
+// merged in the lane; the lane pair col, col ^ 1 halves the two groups (each
+// keeps the group of its parity and sends the other); the lanes that carry
+// the same group (equal parity) are then combined: col ^ 2, the quads 4 and
+// 8 lanes away in the 16-lane row, and the other 16 lanes.
+__device__ __attribute__((always_inline)) inline float max32_group(const float (&v)[8], int col) {
+  const float g0 = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+  const float g1 = fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7]));
+  const bool c0 = col & 1;
+  float z = fmaxf(c0 ? g1 : g0, dpp<0xB1>(c0 ? g0 : g1));   // quad_perm [1,0,3,2]
+  z = fmaxf(z, dpp<0x4E>(z));                                 // quad_perm [2,3,0,1]
+  z = fmaxf(z, dpp<0x124>(z));                                // row_ror:4
+  z = fmaxf(z, dpp<0x128>(z));                                // row_ror:8
   const float2 r = rows16(z);
   return fmaxf(r.x, r.y);
 }
 
 // Split statistics of the finished tiles 2u and 2u + 1 (8 head rows of this
-// lane x its column each): each tile's maximum per head, reduced over the 32
-// columns, goes to the tile-maximum table (one entry per 32-position tile
-// when it fits in LDS, else one per pair: fine = false), lane col writing row
-// e = col mod 8 of its half (lanes with equal e hold equal values); every lane
+// lane x its column each): each tile's maximum over the 32 columns and a
+// group of four heads goes to the tile-maximum table entry of every head of
+// the group (an upper bound of the head's own maximum, so the live-tile test
+// stays conservative; one entry per 32-position tile when it fits in LDS,
+// else one per pair: fine = false), lane col writing head 8 (col & 1) +
+// ((col >> 1) & 3) of its rows (lanes that write one entry hold equal
+// values); every lane
 // keeps a running maximum m of its own scores and adds exp2(s - m) of its two
 // scores to its sum l (rescaled when m grows); the lanes are merged once, at
 // the end of the pass. No branch: the table index and value are selected.
 __device__ __attribute__((always_inline)) inline void tile_stats(int u, const float (&s0)[8], const float (&s1)[8],
                                                                  float* __restrict__ tslot, bool fine, int col,
                                                                  float (&m)[8], float (&l)[8]) {
-  const float t0 = max32_row(s0, col), t1 = max32_row(s1, col);
+  const float t0 = max32_group(s0, col), t1 = max32_group(s1, col);
   const float tb = fmaxf(t0, t1);
   tslot[fine ? 2 * u : u] = fine ? t0 : tb;
   tslot[fine ? 2 * u + 1 : u] = fine ? t1 : tb;
@@ -486,8 +487,8 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
   float m[8], l[8], sprev[8], own[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) { m[e] = -INFINITY; l[e] = 0.f; sprev[e] = -INFINITY; own[e] = 0.f; }
-  const int esel = col & 7;                          // the tile-maximum row this lane writes
-  float* tslot = tmax + (hrow + 8 * (esel >> 2) + (esel & 3)) * NLT;
+  // the tile-maximum entry this lane writes: head 8 (col & 1) + ((col >> 1) & 3) of its rows
+  float* tslot = tmax + (hrow + 8 * (col & 1) + ((col >> 1) & 3)) * NLT;
   auto xr_of = [&](int t) { return xbuf + ((t & 1) * NW + partner) * 128 + lane; };
   auto xw_of = [&](int t) { return xbuf + ((t & 1) * NW + wave) * 128 + lane; };
   auto wr_of = [&](int t) { return t + 3 < T ? ring + ((t + 3) % NBUF) * BUF_BYTES : nullptr; };
