@@ -537,6 +537,81 @@ def run_kskip(steps, warmup):
     return lines
 
 
+GQA_STAMPS = {0: "start", 1: "set-up done", 2: "K pass done, statistics published", 3: "group LSE known",
+              7: "keep decision done (wave 0)", 8: "value pass entered (wave 0)", 9: "value pass done (wave 0)",
+              4: "partial outputs published (all waves)", 5: "merge inputs settled", 6: "outputs written"}
+MLA_STAMPS = {0: "start", 1: "q operands ready", 2: "score pass done", 3: "sequence LSE known",
+              4: "kept rows published"}
+
+
+def run_phases(names, warm=20, calls=6):
+    """Phase stamps of single calls (caches rotated as in the timed runs):
+    per stamp, the p0/p10/p50/p90/max over workgroups of the time since the
+    earliest workgroup start (us), each the median over `calls` calls. The
+    stamps (the 100 MHz device clock, read by thread 0 of each workgroup)
+    add about 0.3 us each, so a stamped call runs a few us longer than an
+    unstamped one; the timeline's shape is what they show."""
+    import numpy as np
+    import torch
+    import decode_attention_quantized_amd as kvq
+    import synth
+    from decode_attention_quantized_amd.runtime import DecodeAttention, PackedCache
+    lines = []
+    for name in names:
+        w = synth.workload(name)
+        inp = synth.generate(w)
+        latent = inp.v is None
+        kc, ks = kvq.kvq_pack(w.fmt, inp.k)
+        K0 = PackedCache.from_host(kc, ks, w.fmt, w.dim)
+        V0 = None
+        set_bytes = kc.nbytes + ks.nbytes
+        if not latent:
+            vc, vs = kvq.kvq_pack(w.fmt, inp.v)
+            V0 = PackedCache.from_host(vc, vs, w.fmt, w.dim)
+            set_bytes *= 2
+        R = max(2, math.ceil(ROTATION_BYTES / set_bytes))
+        caches = [(K0, V0)] + [(K0.clone(), None if latent else V0.clone()) for _ in range(R - 1)]
+        q = torch.from_numpy(inp.q).cuda()
+        if w.q_bf16:
+            q = q.to(torch.bfloat16)
+        att = DecodeAttention(K0, V0, w.q_heads, ctx_len=w.ctx, softmax_scale=w.sigma,
+                              q_dtype=kvq.KVQ_Q_BF16 if w.q_bf16 else kvq.KVQ_Q_F32,
+                              v_dim=w.v_dim if latent else 0)
+        out = torch.empty((w.batch, w.q_heads, w.v_dim), dtype=torch.float32, device="cuda")
+        for i in range(warm):
+            k, v = caches[i % R]
+            att(q, w.ctx, w.threshold, out=out, k=k, v=v)
+        prof = []
+        for i in range(calls):
+            k, v = caches[(warm + i) % R]
+            prof.append(att.phase_profile(q, w.ctx, w.threshold, k=k, v=v) / 100.0)
+        check_stats(att.stats(), f"{name} phase stamps")
+        names_of = MLA_STAMPS if latent else GQA_STAMPS
+        pct = (0, 10, 50, 90, 100)
+        stamps = {}
+        for s in sorted(names_of, key=lambda s: float(np.median([np.median(p[:, s]) for p in prof]))):
+            rows = np.array([[np.percentile(p[:, s], c) for c in pct] for p in prof])
+            stamps[names_of[s]] = [round(float(x), 2) for x in np.median(rows, axis=0)]
+        # the exchange of split statistics, per group (the splits of one
+        # (sequence, kv head), or of one sequence for the latent shape):
+        # earliest "LSE known" minus latest "statistics published" (the
+        # latent kernel's stamp 2 precedes its publication by a few reductions)
+        nwg = prof[0].shape[0]
+        ngroups = w.batch * (1 if latent else w.kv_heads)
+        S = nwg // ngroups
+        gaps = np.array([[p[g * S:(g + 1) * S, 3].min() - p[g * S:(g + 1) * S, 2].max() for g in range(ngroups)]
+                         for p in prof])
+        exch = [round(float(np.median([np.percentile(x, c) for x in gaps])), 2) for c in (0, 50, 100)]
+        lines.append({"workload": name, "threshold": w.threshold, "workgroups": int(nwg),
+                      "calls": calls, "unit": "us since the earliest workgroup start",
+                      "columns": ["p0", "p10", "p50", "p90", "max"], "stamps": stamps,
+                      "exchange_after_last_publication_us": {"groups": ngroups, "splits": S,
+                                                             "p0_p50_max": exch}})
+        del att, caches
+        torch.cuda.synchronize()
+    return lines
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -561,6 +636,9 @@ def main():
                     help="leave the LUT3 (batch 8, ctx 32768) object out of the default line")
     ap.add_argument("--no-other-configs", action="store_true",
                     help="leave the context sweep and the latent (MLA) objects out of the default line")
+    ap.add_argument("--phases", metavar="WORKLOADS",
+                    help="comma-separated workloads (e.g. long,lut3,tiny,mla): print the phase timeline of "
+                         "single stamped calls instead of timing")
     args = ap.parse_args()
     if args.write_traffic:
         print(json.dumps(write_traffic(args.write_traffic, args.traffic_workload)), flush=True)
@@ -587,6 +665,10 @@ def main():
     import synth
     from decode_attention_quantized_amd.runtime import DecodeAttention, PackedCache
 
+    if args.phases:
+        for line in run_phases(args.phases.split(",")):
+            print(json.dumps(line), flush=True)
+        return
     if args.workload == "append":
         for line in run_append(min(args.steps, 50), min(args.warmup, 5)):
             print(json.dumps(line), flush=True)
