@@ -235,6 +235,7 @@ int32_t launch_mla(const void* q, const kvq_cache* kcache, const kvq_cache* vcac
   a.ocnt = reinterpret_cast<uint32_t*>(ws + plan.mws.ocnt);
   a.done = reinterpret_cast<unsigned long long*>(ws + plan.mws.done);
   a.lseo = reinterpret_cast<float*>(ws + plan.mws.lseo);
+  a.lsep = reinterpret_cast<unsigned long long*>(ws + plan.mws.lsep);
   a.live = reinterpret_cast<int32_t*>(ws + plan.mws.live);
   a.live_off = plan.mws.live;
   a.mask_out = l->mask_out;

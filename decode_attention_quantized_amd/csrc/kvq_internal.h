@@ -143,6 +143,7 @@ struct MlaArgs {
   int32_t tpe;                    // 32-position tiles per tile-maximum entry of the scores kernel (1 or 2)
   int32_t scores_out;             // 1: kp holds every row's log2-domain scores (threshold 0, mla_out_dense)
   float* lseo;                    // [B][H] log2-domain LSE per head (written when scores_out)
+  unsigned long long* lsep;       // tagged [B][H]: log2-domain LSE per head, published by the scores kernel
   uint32_t* mask_out;             // optional keep bits [B][H][mask_words]
   int32_t mask_words;             // ceil(ctx / 32)
   int32_t B, Hq, ctx, cap;
@@ -157,7 +158,7 @@ struct MlaArgs {
 };
 
 struct MlaLayout {
-  int64_t kept_mass, bgstat, split_ml, kcount, kpairs, kpos, kp, opart, mpart, ocnt, done, lseo, live, total;
+  int64_t kept_mass, bgstat, split_ml, kcount, kpairs, kpos, kp, opart, mpart, ocnt, done, lseo, lsep, live, total;
 };
 
 // The first two regions match ws_layout() so kvq_stats reads both families
@@ -175,6 +176,7 @@ inline MlaLayout mla_ws_layout(int B, int H, int S, int64_t SP, int R) {
   w.ocnt = off;      off = align256(off + int64_t(B) * (H / 32) * 4 * 4);
   w.done = off;      off = align256(off + int64_t(B) * (H >= 64 ? H / 64 : 1) * kMaxRanges * 8);
   w.lseo = off;      off = align256(off + int64_t(B) * H * 4);
+  w.lsep = off;      off = align256(off + int64_t(B) * H * 8);
   w.split_ml = off;  off = align256(off + int64_t(B) * S * H * 16);
   w.kcount = off;    off = align256(off + int64_t(B) * S * 4);
   w.kpairs = off;    off = align256(off + int64_t(B) * S * 4);

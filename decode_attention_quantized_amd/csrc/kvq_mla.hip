@@ -553,63 +553,78 @@ __global__ __launch_bounds__(64 * NW) void mla_scores(MlaArgs a) {
   }
 
   // ---------------------------------------------------------------- phase 2: LSE
-  // Every workgroup merges the split statistics of all heads of its sequence
-  // itself (one exchange, no second round trip): thread (q, h) merges head
-  // h's splits q, q + 4, ... in order, reading each (max, sum) pair of tagged
-  // words with one coherent 16-byte load (consecutive threads on consecutive
-  // heads, so a wave reads whole lines) and re-reading the stale ones of a
-  // batch together; the four partial results of a head are merged in a fixed
-  // order, so every workgroup of the sequence computes the same bits.
+  // Two hand-offs of epoch-tagged words. Stage 1: workgroup `split` merges
+  // the split statistics of its share of the heads (hp = ceil(H / S) heads
+  // from split * hp), one wave per head: lane l merges splits l, l + 64, ...
+  // in order, then a fixed butterfly over the lanes; the head's log-sum-exp
+  // is published. Stage 2: every workgroup reads the published log-sum-exps
+  // of all heads, so all of them use the same bits. A workgroup reads
+  // S * hp + H words instead of the S * H pairs of every split (64 KB per
+  // workgroup, 16 MB per call at 32 splits and 128 heads).
   bool sbad;                                          // a wait of this workgroup gave up
   {
-    const int h = tid % H, q = tid / H;               // NT = 4 * H
-    float2 acc = make_float2(-INFINITY, 0.f);
     bool gave_up = false;
-    constexpr int SB = 8;                             // splits per batch of loads
+    const int hp = (H + a.S - 1) / a.S;
+    const int h0 = split * hp;
+    const int nh = max(0, min(hp, H - h0));
+    constexpr int SB = 4;                             // pairs per lane in flight
     const __amdgpu_buffer_rsrc_t r =
         __builtin_amdgcn_make_buffer_rsrc(a.split_ml + int64_t(b) * a.S * H * 2, 0, a.S * H * 16, 0x00020000);
-    for (int s0 = q; s0 < a.S; s0 += 4 * SB) {
-      u32x4 v[SB];
-      int off[SB];
-      bool use[SB];
+    for (int hh = wave; hh < nh; hh += NW) {          // uniform across the wave
+      const int h = h0 + hh;
+      float2 acc = make_float2(-INFINITY, 0.f);
+      bool gone = false;
+      for (int s0 = 0; s0 < a.S; s0 += 64 * SB) {
+        u32x4 v[SB];
+        int off[SB];
+        bool use[SB];
 #pragma unroll
-      for (int u = 0; u < SB; ++u) {
-        const int sp = s0 + 4 * u;
-        use[u] = sp < a.S;
-        off[u] = ((use[u] ? sp : 0) * H + h) * 16;
-        v[u] = use[u] ? __builtin_amdgcn_raw_buffer_load_b128(r, off[u], 0, kCoherentLoad) : u32x4{0u, epoch, 0u, epoch};
-      }
-      for (uint32_t spins = 0;; ++spins) {
-        bool stale = false;
-#pragma unroll
-        for (int u = 0; u < SB; ++u) stale |= use[u] && (v[u][1] != epoch || v[u][3] != epoch);
-        if (!stale) break;
-        if (spins > a.spin_limit) {
-          __hip_atomic_fetch_or(&a.hdr->status, kStatusWaitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          gave_up = true;
-          break;
+        for (int u = 0; u < SB; ++u) {
+          const int sp = s0 + lane + 64 * u;
+          use[u] = sp < a.S;
+          off[u] = ((use[u] ? sp : 0) * H + h) * 16;
+          v[u] = use[u] ? __builtin_amdgcn_raw_buffer_load_b128(r, off[u], 0, kCoherentLoad) : u32x4{0u, epoch, 0u, epoch};
         }
-        __builtin_amdgcn_s_sleep(1);
+        for (uint32_t spins = 0;; ++spins) {
+          bool stale = false;
+#pragma unroll
+          for (int u = 0; u < SB; ++u) stale |= use[u] && (v[u][1] != epoch || v[u][3] != epoch);
+          if (!stale || gone) break;
+          if (spins > a.spin_limit) {
+            __hip_atomic_fetch_or(&a.hdr->status, kStatusWaitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            gone = true;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+          for (int u = 0; u < SB; ++u)
+            if (use[u] && (v[u][1] != epoch || v[u][3] != epoch))
+              v[u] = __builtin_amdgcn_raw_buffer_load_b128(r, off[u], 0, kCoherentLoad);
+        }
 #pragma unroll
         for (int u = 0; u < SB; ++u)
-          if (use[u] && (v[u][1] != epoch || v[u][3] != epoch))
-            v[u] = __builtin_amdgcn_raw_buffer_load_b128(r, off[u], 0, kCoherentLoad);
+          if (use[u]) acc = lse_merge(acc, make_float2(__uint_as_float(v[u][0]), __uint_as_float(v[u][2])));
       }
 #pragma unroll
-      for (int u = 0; u < SB; ++u) {
-        if (!use[u]) break;
-        acc = lse_merge(acc, make_float2(__uint_as_float(v[u][0]), __uint_as_float(v[u][2])));
-      }
+      for (int o = 1; o < 64; o <<= 1) acc = lse_merge(acc, make_float2(__shfl_xor(acc.x, o), __shfl_xor(acc.y, o)));
+      gone = __ballot(gone) != 0ull;
+      if (lane == 0) put_tagged_f(a.lsep + int64_t(b) * H + h, epoch, poison_if(gone, acc.x + log2f(acc.y)));
+      gave_up = gave_up || gone;
     }
-    float2* part = reinterpret_cast<float2*>(xbuf);   // [4][H]; the hand-over slots are idle here
-    part[q * H + h] = acc;
+    if (tid < H) {
+      const u64* p = a.lsep + int64_t(b) * H + tid;
+      bool late = false;
+      const float x = settle_f(peek(p), p, epoch, a.hdr, a.spin_limit, late);
+      // a head whose publisher gave up carries NaN (tested on the bits: the
+      // kernel is compiled without NaN semantics)
+      const uint32_t xb = __float_as_uint(x);
+      gave_up = gave_up || late || ((xb & 0x7F800000u) == 0x7F800000u && (xb & 0x007FFFFFu) != 0u);
+      lse[tid] = x;
+    }
     sbad = __syncthreads_or(gave_up) != 0;
-    if (q == 0) {
-      const float2 r01 = lse_merge(part[h], part[H + h]);
-      const float2 r23 = lse_merge(part[2 * H + h], part[3 * H + h]);
-      const float2 rr = lse_merge(r01, r23);
-      lse[h] = poison_if(sbad, rr.x + log2f(rr.y));
-      if (a.scores_out && split == 0) a.lseo[int64_t(b) * H + h] = lse[h];
+    if (tid < H) {
+      lse[tid] = poison_if(sbad, lse[tid]);
+      if (a.scores_out && split == 0) a.lseo[int64_t(b) * H + tid] = lse[tid];
     }
     __syncthreads();
   }
